@@ -1,0 +1,359 @@
+"""Pins for the fp64 oracle: each test checks it against something other than
+itself -- hand-derived instances of the pages' fold rule, closed forms,
+invariants, special cases that reduce to library routines (scipy, torch), and
+planted-key probes with exact answers.  CPU only."""
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from mla_token_decode_amd import inputs as gen
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SM = gen.SM_SCALE
+
+
+# ----------------------------------------------------------- independent decoding
+
+def decode_q(q_bits):
+    """bf16 bits -> float64 through torch's bfloat16 dtype (not the oracle's decoder)."""
+    t = torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def decode_kv(inp):
+    if inp.kv_fp8:
+        t = torch.from_numpy(np.ascontiguousarray(inp.kv)).view(torch.float8_e4m3fn)
+        return t.to(torch.float64).numpy() * float(inp.kv_scale)
+    return decode_q(inp.kv)
+
+
+def run_oracle(inp, mode=oracle.MODE_DIRECT, splits=None, granule=64):
+    return oracle.mla_decode(inp.q_bits, inp.kv, inp.q_len, inp.kv_len, inp.H,
+                             kv_is_fp8=inp.kv_fp8, kv_scale=inp.kv_scale, sm_scale=inp.sm_scale,
+                             mode=mode, splits=splits, granule=granule)
+
+
+def scipy_reference(inp):
+    """Dense attention with an explicit causal mask matrix: logits by numpy
+    matmul, LSE by scipy.special.logsumexp, weights by scipy.special.softmax."""
+    Q = decode_q(inp.q_bits)
+    KV = decode_kv(inp)
+    H = inp.H
+    outs, lses = [], []
+    qo = ko = 0
+    for b in range(inp.batch):
+        qb, nb = int(inp.q_len[b]), int(inp.kv_len[b])
+        K = KV[ko:ko + nb]
+        V = K[:, :512]
+        for i in range(qb):
+            s = (Q[qo + i] @ K.T) * SM                    # [H, nb]
+            mask = np.arange(nb)[None, :] > (nb - qb + i)
+            s = np.where(mask, -np.inf, s)
+            lses.append(scipy.special.logsumexp(s, axis=1))
+            outs.append(scipy.special.softmax(s, axis=1) @ V)
+        qo += qb
+        ko += nb
+    return np.stack(outs), np.stack(lses)
+
+
+# ------------------------------------------------------------------- fold rule
+
+def test_fold_rule_golden_instances():
+    path = os.path.join(HERE, "golden", "fold_rule_instances.txt")
+    n = 0
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            H, q, F, R, T = map(int, line.split())
+            assert oracle.fold_factor(H, q) == F, (H, q)
+            if F:
+                assert H * F == R and q // F == T
+            n += 1
+    assert n >= 20
+
+
+def test_fold_rule_properties_exhaustive():
+    for H in range(1, 131):
+        for q in range(1, 33):
+            F = oracle.fold_factor(H, q)
+            divs = [d for d in range(1, q + 1) if q % d == 0 and H * d <= 128]
+            assert F == (max(divs) if divs else 0)
+            if F:
+                assert q % F == 0 and H * F <= 128
+
+
+# -------------------------------------------------------------------- decoders
+
+def test_e4m3_fixed_points():
+    assert oracle.e4m3_to_double(0x7E) == 448.0
+    assert oracle.e4m3_to_double(0xFE) == -448.0
+    assert oracle.e4m3_to_double(0x38) == 1.0
+    assert oracle.e4m3_to_double(0x08) == 2.0 ** -6
+    assert oracle.e4m3_to_double(0x01) == 2.0 ** -9
+    assert oracle.e4m3_to_double(0x07) == 7 * 2.0 ** -9
+    assert oracle.e4m3_to_double(0x00) == 0.0
+    assert math.isnan(oracle.e4m3_to_double(0x7F))
+    assert math.isnan(oracle.e4m3_to_double(0xFF))
+
+
+def test_e4m3_all_codes_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = np.array([oracle.e4m3_to_double(c) for c in codes])
+    both_nan = np.isnan(ref) & np.isnan(mine)
+    assert np.all(both_nan | (ref == mine))
+    assert both_nan.sum() == 2
+
+
+def test_bf16_decode_vs_torch():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 65536, size=4000).astype(np.uint16)
+    exp_field = (bits >> 7) & 0xFF
+    bits = bits[exp_field != 0xFF]  # drop inf/nan patterns
+    ref = decode_q(bits)
+    mine = np.array([oracle.bf16_to_double(b) for b in bits])
+    assert np.array_equal(ref, mine)
+
+
+def test_generator_codecs_vs_torch():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(20000) * 3).astype(np.float32)
+    x[:4] = [0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8]     # ties to even
+    mine = gen.bf16_bits_from_f32(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+    codes = gen.e4m3_codes_from_f32(np.array([500.0, -1000.0, 448.0, 2 ** -10, 3 * 2 ** -10], np.float32))
+    assert list(codes) == [0x7E, 0xFE, 0x7E, 0x00, 0x02]
+
+
+# ----------------------------------------------------------------- split layout
+
+@pytest.mark.parametrize("n,S,G", [(4096, 16, 64), (131072, 256, 64), (125000, 32, 64),
+                                   (1, 1, 64), (65, 2, 64), (100, 7, 1), (1000, 3, 16),
+                                   (1048576, 300, 64), (64, 5, 64)])
+def test_split_layout_properties(n, S, G):
+    L, S_eff = oracle.split_layout(n, S, G)
+    assert L % G == 0 and L >= G
+    assert S_eff == -(-n // L)
+    assert (S_eff - 1) * L < n <= S_eff * L
+    assert S_eff <= S
+    # equal chunks as long as possible: L is the smallest granule multiple >= ceil(n/S)
+    assert L - G < -(-n // S) <= L
+
+
+# ------------------------------------------------------------ closed forms
+
+def test_single_key_closed_form():
+    inp = gen.random_inputs(3, [1], [1], False, seed=11)
+    o, lse = run_oracle(inp)
+    Q, K = decode_q(inp.q_bits), decode_kv(inp)
+    assert np.array_equal(o[0], np.repeat(K[:1, :512], 3, axis=0))
+    np.testing.assert_allclose(lse[0], (Q[0] @ K[0]) * SM, rtol=1e-14, atol=1e-16)
+
+
+def test_two_key_closed_form():
+    inp = gen.random_inputs(4, [1], [2], False, seed=12)
+    o, lse = run_oracle(inp)
+    Q, K = decode_q(inp.q_bits), decode_kv(inp)
+    s = (Q[0] @ K.T) * SM                                            # [H, 2]
+    w0 = scipy.special.expit(s[:, 0] - s[:, 1])
+    w1 = scipy.special.expit(s[:, 1] - s[:, 0])
+    ref = w0[:, None] * K[0, :512] + w1[:, None] * K[1, :512]
+    np.testing.assert_allclose(o[0], ref, rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(lse[0], np.logaddexp(s[:, 0], s[:, 1]), rtol=1e-14)
+
+
+def test_identical_keys_mean_and_log_count():
+    # q=4 tail tokens over n=9 keys: visible counts 6, 7, 8, 9.
+    inp = gen.identical_key_inputs(5, [4], [9], seed=13)
+    o, lse = run_oracle(inp)
+    Q, K = decode_q(inp.q_bits), decode_kv(inp)
+    for i in range(4):
+        np.testing.assert_allclose(o[i], np.repeat(K[:1, :512], 5, axis=0), rtol=1e-14, atol=1e-17)
+        s = (Q[i] @ K[0]) * SM
+        np.testing.assert_allclose(lse[i], s + math.log(6 + i), rtol=1e-13)
+
+
+# ---------------------------------------------------------- library brute force
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_brute_force_scipy(seed, fp8):
+    rng = np.random.default_rng([seed, 99])
+    B = int(rng.integers(1, 4))
+    H = int(rng.integers(1, 5))
+    q_len = [int(rng.integers(1, 5)) for _ in range(B)]
+    kv_len = [int(q + rng.integers(0, 60)) for q in q_len]
+    inp = gen.random_inputs(H, q_len, kv_len, fp8, seed=100 + seed)
+    # a larger spread of logits than the workloads, so the softmax is not flat
+    inp.q_bits = gen.bf16_bits_from_f32(gen.f32_from_bf16_bits(inp.q_bits) * np.float32(40.0))
+    o, lse = run_oracle(inp)
+    ro, rl = scipy_reference(inp)
+    np.testing.assert_allclose(o, ro, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(lse, rl, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- invariants
+
+def _exact_inputs(H, q_len, kv_len, seed):
+    """Small-integer / 8 values: sums of them and shifts by 1/2 stay exact in bf16."""
+    rng = np.random.default_rng([seed, 5])
+    sq, sn = int(np.sum(q_len)), int(np.sum(kv_len))
+    q = rng.integers(-8, 9, size=(sq, H, 576)).astype(np.float32) / 8
+    kv = rng.integers(-8, 9, size=(sn, 576)).astype(np.float32) / 8
+    return gen.Inputs(H, np.asarray(q_len, np.int32), np.asarray(kv_len, np.int32),
+                      gen.bf16_bits_from_f32(q), gen.bf16_bits_from_f32(kv), False, 1.0)
+
+
+def test_rope_shift_invariance():
+    inp = _exact_inputs(3, [3], [20], seed=1)
+    o, lse = run_oracle(inp)
+    kvf = gen.f32_from_bf16_bits(inp.kv).copy()
+    u = np.zeros(576, np.float32)
+    u[512 + 5] = 0.5
+    u[512 + 40] = -0.5
+    kvf += u
+    shifted = gen.Inputs(inp.H, inp.q_len, inp.kv_len, inp.q_bits, gen.bf16_bits_from_f32(kvf), False, 1.0)
+    o2, lse2 = run_oracle(shifted)
+    Q = decode_q(inp.q_bits)
+    np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(lse2, lse + (Q @ u.astype(np.float64)) * SM, rtol=1e-12, atol=1e-13)
+
+
+def test_prefix_permutation_invariance():
+    inp = _exact_inputs(2, [3], [30], seed=2)
+    o, lse = run_oracle(inp)
+    perm = np.random.default_rng(3).permutation(27)   # keys 0..26 are seen by every tail row
+    kv2 = inp.kv.copy()
+    kv2[:27] = inp.kv[perm]
+    o2, lse2 = run_oracle(gen.Inputs(inp.H, inp.q_len, inp.kv_len, inp.q_bits, kv2, False, 1.0))
+    np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-14)
+
+
+def test_causal_truncation_bitwise():
+    inp = gen.random_inputs(4, [5], [40], False, seed=21)
+    o, lse = run_oracle(inp)
+    for i in range(5):
+        n = 40 - 5 + i + 1
+        sub = gen.Inputs(4, np.array([1], np.int32), np.array([n], np.int32),
+                         inp.q_bits[i:i + 1], inp.kv[:n], False, 1.0)
+        o1, l1 = run_oracle(sub)
+        assert np.array_equal(o1[0], o[i]) and np.array_equal(l1[0], lse[i])
+
+
+@pytest.mark.parametrize("H,q_len,kv_len", [
+    (12, [8], [50]), (96, [8], [20]), (24, [8], [33]), (40, [6], [64]),
+    (7, [20], [25]), (96, [1, 2, 3, 4], [10, 11, 12, 13]), (5, [3, 1, 7], [9, 4, 7])])
+def test_folded_equals_direct_bitwise(H, q_len, kv_len):
+    inp = gen.random_inputs(H, q_len, kv_len, False, seed=31)
+    o, lse = run_oracle(inp)
+    of, lf = run_oracle(inp, mode=oracle.MODE_FOLDED)
+    assert not np.isnan(of).any()
+    assert np.array_equal(o, of) and np.array_equal(lse, lf)
+
+
+@pytest.mark.parametrize("splits,granule", [(1, 64), (2, 64), (3, 16), (7, 1), (40, 1), (5, 8)])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_split_merge_equals_unsplit(splits, granule, fp8):
+    # q=6 with chunks as short as one key: early tail tokens see empty chunks.
+    inp = gen.random_inputs(3, [6, 2], [45, 70], fp8, seed=41)
+    inp.q_bits = gen.bf16_bits_from_f32(gen.f32_from_bf16_bits(inp.q_bits) * np.float32(30.0))
+    o, lse = run_oracle(inp)
+    os_, ls = run_oracle(inp, mode=oracle.MODE_SPLIT, splits=[splits, splits], granule=granule)
+    np.testing.assert_allclose(os_, o, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(ls, lse, rtol=1e-13, atol=1e-14)
+
+
+def test_partial_chunks_merge_to_full():
+    inp = gen.random_inputs(2, [3], [50], False, seed=51)
+    o, lse = run_oracle(inp)
+    parts = [oracle.mla_partial(inp.q_bits, inp.kv, inp.q_len, inp.kv_len, 2, 0, 2, 1, lo, lo + 16,
+                               sm_scale=inp.sm_scale)
+             for lo in range(0, 64, 16)]
+    lses = np.array([p[1] for p in parts])
+    m = lses.max()
+    w = np.exp(lses - m)
+    ref_o = sum(wi * p[0] for wi, p in zip(w, parts)) / w.sum()
+    np.testing.assert_allclose(ref_o, o[2, 1], rtol=1e-12, atol=1e-16)
+    np.testing.assert_allclose(m + np.log(w.sum()), lse[2, 1], rtol=1e-13)
+
+
+# ------------------------------------------------------------- planted probes
+
+def _planted_expectation(inp, markers):
+    """Closed form for the planted probe.  A query row has one non-zero column
+    (rope column 512 + d), so its logit is Q[512+d] * K[p, 512+d] * sm for a
+    marker p and exactly 0 for every other key; non-marker values are 0."""
+    H = inp.H
+    KV = decode_kv(inp)
+    Q = decode_q(inp.q_bits)
+    outs, lses = [], []
+    ko = 0
+    qo = 0
+    for b in range(inp.batch):
+        qb, nb = int(inp.q_len[b]), int(inp.kv_len[b])
+        for i in range(qb):
+            vis = nb - qb + i + 1
+            for h in range(H):
+                d = (i * H + h) % 64
+                a = float(Q[qo + i, h, 512 + d])
+                seen = [p for (p, _) in markers[b] if p < vis]
+                s = np.array([a * KV[ko + p, 512 + d] * SM for p in seen] + [0.0])
+                top = s.max()
+                w = np.exp(s[:-1] - top)
+                rest = (vis - len(seen)) * math.exp(-top)
+                num = sum(wi * KV[ko + p, :512] for wi, p in zip(w, seen)) if seen else np.zeros(512)
+                den = w.sum() + rest
+                outs.append(num / den)
+                lses.append(top + math.log(den))
+        qo += qb
+        ko += nb
+    sq = int(inp.q_len.sum())
+    return np.array(outs).reshape(sq, H, 512), np.array(lses).reshape(sq, H)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_planted_probe_closed_form(fp8):
+    H, q_len, kv_len = 12, [8, 3], [200, 90]
+    markers = [[(0, 0), (63, 1), (64, 13), (200 - 8 + 0, 0), (200 - 8 + 1, 12), (199, 95 % 64),
+                (150, 5)],
+               [(0, 2), (89, 6), (88, 5), (87, 4), (40, 3)]]
+    inp = gen.planted_inputs(H, q_len, kv_len, markers, fp8=fp8)
+    o, lse = run_oracle(inp)
+    ro, rl = _planted_expectation(inp, markers)
+    np.testing.assert_allclose(o, ro, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, rl, rtol=1e-12, atol=1e-12)
+    # the probe discriminates: token 0 head 0 (direction 0) sees the tail
+    # marker at 192 and outputs mostly its value code; token 1 head 0
+    # (direction 12) sees the marker at 193 instead.
+    v192 = decode_kv(inp)[192, :512]
+    v193 = decode_kv(inp)[193, :512]
+    assert np.abs(o[0, 0] - v192 / 2 - decode_kv(inp)[0, :512] / 2).max() < 1e-6
+    assert np.abs(o[1, 0] - v193).max() < 1e-6
+
+
+def test_rows_api_matches_full():
+    inp = gen.random_inputs(6, [4, 2], [70, 30], True, seed=61)
+    o, lse = run_oracle(inp)
+    rows = np.array([0, 5, 7, 13, 23, 30, 35])
+    o2, l2 = oracle.mla_decode_rows(inp.q_bits, inp.kv, inp.q_len, inp.kv_len, 6, rows,
+                                    kv_is_fp8=True, kv_scale=inp.kv_scale)
+    flat_o, flat_l = o.reshape(-1, 512), lse.reshape(-1)
+    assert np.array_equal(o2, flat_o[rows]) and np.array_equal(l2, flat_l[rows])
+
+
+def test_rejects_invalid():
+    inp = gen.random_inputs(2, [3], [5], False, seed=1)
+    with pytest.raises(ValueError):
+        oracle.mla_decode(inp.q_bits, inp.kv, [3], [2], 2)  # kv_len < q_len (sizes also wrong)
+    big = gen.random_inputs(129, [1], [2], False, seed=1)
+    with pytest.raises(ValueError):
+        run_oracle(big)
