@@ -1,0 +1,160 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) MLA speculative-verify decode
+ * library (libmla_decode.so).
+ *
+ * The operation.  Each of `batch` sequences brings q_len[b] verify tokens
+ * (the last q_len[b] of its kv_len[b] cached positions).  All `num_heads`
+ * query heads of a token attend over ONE shared latent KV head (MQA): a
+ * 576-wide row per position, 512 latent columns followed by 64 rope columns.
+ * Scores use all 576 columns; the value is the first 512 columns of the same
+ * row.  Token i of a sequence sees keys 0 .. kv_len - q_len + i (causal only
+ * among the tail tokens).  Outputs: O (bf16) and the natural-log
+ * log-sum-exp of the scaled scores (fp32) per (token, head).
+ * Sources: "[Kimi-K3] Allow DSPARK verify on cutedsl_mla (fold_sq)" (sglang
+ * PR #33650) -- verify width q = block_size + 1 (opening paragraphs), one KV
+ * head for all H query heads and the per-rank H values (section "Which
+ * decode backend?"), the 576-wide query/key (section "GPU timeline"), the
+ * fold rule and the single KV pass per tile (section "Decision rule",
+ * paragraph "Why"), the split-KV reduction (section "GPU timeline").
+ *
+ * How it runs.  mla_decode_plan folds F = the largest divisor of q_len[b]
+ * with H * F <= 128 tokens into one tile of H * F rows (fold rule above), so
+ * each KV byte of a chunk is streamed from HBM once per tile; it cuts each
+ * sequence into split-KV chunks and sizes the caller's workspace.
+ * mla_decode_run enqueues the main decode kernel, which writes final O/LSE
+ * for unsplit tiles and per-chunk partials for split ones; mla_decode_reduce
+ * enqueues the log-sum-exp merge of those partials (a separate kernel, as in
+ * "bench(cake_mla_varq_dcp_decode): ..." (flashinfer PR #5588), table "What
+ * was measured", row "split rows").
+ *
+ * Error convention.  Every call returns an mla_status and never throws or
+ * aborts.  Unsupported shapes and options are rejected explicitly; there is
+ * no silent fallback to another path (the pages' first PR exists because a
+ * silent fallback to a slower backend went unnoticed: opening paragraphs of
+ * sglang PR #33650; the flashinfer Cake route likewise rejects unsupported
+ * options explicitly, section "Unsupported (rejected explicitly)" of the
+ * text embedded in flashinfer PR #5588).  After a non-OK status,
+ * mla_last_error() returns a message for the calling thread.
+ *
+ * Ownership.  The caller owns every device buffer and the stream.  The
+ * library allocates no device memory.  A plan is host memory owned by the
+ * library until mla_plan_destroy; it must outlive work enqueued with it only
+ * until mla_decode_run / mla_decode_reduce return (kernel arguments are
+ * copied at launch).
+ *
+ * Threading.  Plans are immutable after creation and may be used from
+ * several threads.  Calls that share one workspace on overlapping streams
+ * race; give each in-flight call its own workspace.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = 1, /* bad shape, null/misaligned pointer, bad scale */
+  MLA_ERR_UNSUPPORTED = 2,      /* no valid fold (H > 128), unknown dtype, not gfx950 */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MLA_ERR_DEVICE = 4            /* a HIP call failed; mla_last_error() has its message */
+} mla_status;
+
+typedef enum {
+  MLA_KV_BF16 = 0,     /* KV rows are bf16 */
+  MLA_KV_FP8_E4M3 = 1  /* KV rows are OCP FP8 E4M3FN codes; value = code * kv_scale */
+} mla_kv_dtype;
+
+/* Width constants of the latent layout. */
+#define MLA_DQK 576          /* query/key width: 512 latent + 64 rope */
+#define MLA_DV 512           /* value width: first 512 columns of the KV row */
+#define MLA_MAX_TILE_ROWS 128 /* H * F must not exceed this */
+#define MLA_KV_GRANULE 64    /* split-KV chunk lengths are multiples of this */
+
+typedef struct mla_plan mla_plan; /* opaque, host-owned */
+
+/* Plan options; zero-initialise for automatic choices.
+ *  force_fold   > 0: cap the fold factor -- F_b = the largest divisor of q_len[b]
+ *                    that is <= force_fold and satisfies H * F <= 128
+ *                    (force_fold = 1 gives the unfolded control: one token per tile).
+ *  force_splits > 0: request this many split-KV chunks for every sequence
+ *                    (the effective count and chunk length follow the split rule
+ *                    documented at mla_plan_query).
+ *  num_cus      > 0: compute-unit count the cost model plans for; 0 queries the
+ *                    current HIP device. */
+typedef struct {
+  int32_t force_fold;
+  int32_t force_splits;
+  int32_t num_cus;
+} mla_plan_options;
+
+/* Build a plan.
+ *  batch >= 1; num_heads = H in [1, 128]; q_len, kv_len: HOST arrays [batch]
+ *  with 1 <= q_len[b] <= kv_len[b].  opts may be NULL.
+ *  On MLA_OK, *plan_out owns a new plan and *workspace_bytes_out (may be
+ *  NULL) is the device workspace mla_decode_run needs (0 when no sequence is
+ *  split).  Pure host computation; touches the GPU only when num_cus == 0.
+ *  Errors: INVALID_ARGUMENT (shapes, null pointers), UNSUPPORTED (H > 128,
+ *  unknown dtype), DEVICE (CU query failed). */
+mla_status mla_decode_plan(int32_t batch, int32_t num_heads, const int32_t* q_len,
+                           const int32_t* kv_len, mla_kv_dtype kv_dtype,
+                           const mla_plan_options* opts, mla_plan** plan_out,
+                           size_t* workspace_bytes_out);
+
+/* Enqueue the main decode kernel(s) on `stream` (a hipStream_t; NULL = the
+ * default stream) and return.
+ *  q:   device bf16 [sum q_len, H, 576], token-major then head, row-major.
+ *  kv:  device [sum kv_len, 576] bf16 or e4m3 codes (plan's dtype); sequence b's
+ *       rows start at sum_{c<b} kv_len[c].
+ *  sm_scale: softmax scale applied to the dot products (> 0, finite).
+ *  kv_scale: fp8: per-tensor dequantisation scale (> 0, finite); bf16: must be 1.
+ *  o:   device bf16 [sum q_len, H, 512].   lse: device fp32 [sum q_len, H],
+ *       natural-log log-sum-exp of the scaled scores.
+ *  workspace: device scratch of at least the planned bytes (may be NULL when
+ *       the plan needs 0).  Its contents on entry do not matter.
+ *  All device pointers must be 16-byte aligned.  For split tiles, O/LSE are
+ *  written by mla_decode_reduce, which must follow on the same stream.
+ *  Errors: INVALID_ARGUMENT, WORKSPACE_TOO_SMALL, UNSUPPORTED (device is not
+ *  gfx950), DEVICE (launch failure). */
+mla_status mla_decode_run(const mla_plan* plan, const void* q, const void* kv, float sm_scale,
+                          float kv_scale, void* o, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Enqueue the split-KV merge on `stream`: for every split tile row, in
+ * ascending chunk order, M = max_s lse_s, lse = M + ln sum_s exp(lse_s - M),
+ * O = sum_s exp(lse_s - lse) * O_s; chunks a row cannot see (lse_s = -inf)
+ * get weight 0.  A no-op (returns MLA_OK, launches nothing) when no sequence
+ * is split.  Same pointer rules as mla_decode_run. */
+mla_status mla_decode_reduce(const mla_plan* plan, const void* workspace, void* o, float* lse,
+                             void* stream);
+
+/* Free a plan (NULL is allowed). */
+void mla_plan_destroy(mla_plan* plan);
+
+/* Message for the last non-OK status on the calling thread ("" if none). */
+const char* mla_last_error(void);
+
+/* Per-sequence plan facts, for tests and tools.
+ *  fold = F_b, tiles = q_len[b] / F_b, splits = S_eff, chunk_len = L_b.
+ *  Split rule: with S requested chunks and granule G = MLA_KV_GRANULE,
+ *    L = G * ceil(ceil(kv_len / S) / G),  S_eff = ceil(kv_len / L),
+ *    chunk s covers keys [s * L, min((s + 1) * L, kv_len)).
+ *  Any output pointer may be NULL. */
+mla_status mla_plan_query(const mla_plan* plan, int32_t seq, int32_t* fold, int32_t* tiles,
+                          int32_t* splits, int32_t* chunk_len);
+
+/* Whole-plan facts: main-kernel work units (one workgroup each), tiles that
+ * are split (rows merged by the reduce), main-kernel launches (one per slice
+ * of up to 64 sequences), and the workspace bytes. Any pointer may be NULL. */
+mla_status mla_plan_info(const mla_plan* plan, int32_t* num_units, int32_t* num_split_tiles,
+                         int32_t* num_launches, size_t* workspace_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,194 @@
+"""Thin ctypes binding of libmla_decode.so (include/mla_decode.h).
+
+Argument marshalling only: every step of the decode runs in the library's HIP
+kernels.  Torch tensors are accepted for device buffers (their data pointers
+are passed through) and the current torch stream is used by default.  A
+missing library raises; nothing falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_decode.so")
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARGUMENT = 1
+MLA_ERR_UNSUPPORTED = 2
+MLA_ERR_WORKSPACE_TOO_SMALL = 3
+MLA_ERR_DEVICE = 4
+MLA_KV_BF16 = 0
+MLA_KV_FP8_E4M3 = 1
+DQK = 576
+DV = 512
+KV_GRANULE = 64
+
+EXPORTED = ["mla_decode_plan", "mla_decode_run", "mla_decode_reduce", "mla_plan_destroy",
+            "mla_last_error", "mla_plan_query", "mla_plan_info"]
+
+_lock = threading.Lock()
+_lib = None
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"mla status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [("force_fold", ctypes.c_int32), ("force_splits", ctypes.c_int32),
+                ("num_cus", ctypes.c_int32)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree library (raises FileNotFoundError if it was not built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError(
+                f"{LIB_PATH} is missing: build it with `python -m mla_token_decode_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        L.mla_decode_plan.argtypes = [ctypes.c_int32, ctypes.c_int32, i32p, i32p, ctypes.c_int,
+                                      ctypes.POINTER(_Options), ctypes.POINTER(ctypes.c_void_p),
+                                      ctypes.POINTER(ctypes.c_size_t)]
+        L.mla_decode_plan.restype = ctypes.c_int
+        L.mla_decode_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+                                     ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p]
+        L.mla_decode_run.restype = ctypes.c_int
+        L.mla_decode_reduce.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+        L.mla_decode_reduce.restype = ctypes.c_int
+        L.mla_plan_destroy.argtypes = [ctypes.c_void_p]
+        L.mla_plan_destroy.restype = None
+        L.mla_last_error.argtypes = []
+        L.mla_last_error.restype = ctypes.c_char_p
+        L.mla_plan_query.argtypes = [ctypes.c_void_p, ctypes.c_int32, i32p, i32p, i32p, i32p]
+        L.mla_plan_query.restype = ctypes.c_int
+        L.mla_plan_info.argtypes = [ctypes.c_void_p, i32p, i32p, i32p, ctypes.POINTER(ctypes.c_size_t)]
+        L.mla_plan_info.restype = ctypes.c_int
+        _lib = L
+        return L
+
+
+def _check(status: int):
+    if status != MLA_OK:
+        msg = lib().mla_last_error()
+        raise MlaError(status, msg.decode() if msg else "")
+
+
+def _ptr(x):
+    """Device pointer of a torch tensor (or an int / None passed through)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class Plan:
+    """Owns an mla_plan (host memory); free with close() or by garbage collection."""
+
+    def __init__(self, num_heads, q_len, kv_len, kv_fp8=False, *, force_fold=0, force_splits=0,
+                 num_cus=0):
+        L = lib()
+        q_len = [int(v) for v in q_len]
+        kv_len = [int(v) for v in kv_len]
+        n = len(q_len)
+        if len(kv_len) != n:
+            raise ValueError("q_len and kv_len must have the same length")
+        qa = (ctypes.c_int32 * max(n, 1))(*q_len)
+        ka = (ctypes.c_int32 * max(n, 1))(*kv_len)
+        opts = _Options(int(force_fold), int(force_splits), int(num_cus))
+        handle = ctypes.c_void_p()
+        ws = ctypes.c_size_t(0)
+        self._h = None
+        _check(L.mla_decode_plan(n, int(num_heads), qa, ka,
+                                 MLA_KV_FP8_E4M3 if kv_fp8 else MLA_KV_BF16, ctypes.byref(opts),
+                                 ctypes.byref(handle), ctypes.byref(ws)))
+        self._h = handle
+        self.num_heads = int(num_heads)
+        self.q_len = q_len
+        self.kv_len = kv_len
+        self.kv_fp8 = bool(kv_fp8)
+        self.workspace_bytes = int(ws.value)
+        nu, ns, nl = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(L.mla_plan_info(self._h, ctypes.byref(nu), ctypes.byref(ns), ctypes.byref(nl), None))
+        self.num_units, self.num_split_tiles, self.num_launches = nu.value, ns.value, nl.value
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("plan is closed")
+        return self._h
+
+    def query(self, seq: int):
+        """(fold F, tiles T, splits S_eff, chunk length L) of one sequence."""
+        f, t, s, c = (ctypes.c_int32() for _ in range(4))
+        _check(lib().mla_plan_query(self.handle, int(seq), ctypes.byref(f), ctypes.byref(t),
+                                    ctypes.byref(s), ctypes.byref(c)))
+        return f.value, t.value, s.value, c.value
+
+    def close(self):
+        if self._h is not None:
+            lib().mla_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def mla_decode_plan(num_heads, q_len, kv_len, kv_fp8=False, **opts) -> Plan:
+    return Plan(num_heads, q_len, kv_len, kv_fp8, **opts)
+
+
+def mla_decode_run(plan: Plan, q, kv, sm_scale: float, kv_scale: float, o, lse, workspace=None,
+                   workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else (
+            workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0)
+    _check(lib().mla_decode_run(plan.handle, _ptr(q), _ptr(kv), float(sm_scale), float(kv_scale),
+                                _ptr(o), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+                                _stream(stream)))
+
+
+def mla_decode_reduce(plan: Plan, workspace, o, lse, stream=None):
+    _check(lib().mla_decode_reduce(plan.handle, _ptr(workspace), _ptr(o), _ptr(lse),
+                                   _stream(stream)))
+
+
+def alloc_outputs(plan: Plan, device="cuda"):
+    """O (bf16 [sum q, H, 512]), LSE (fp32 [sum q, H]) and the workspace, via torch."""
+    import torch
+    sq = sum(plan.q_len)
+    o = torch.empty((sq, plan.num_heads, DV), dtype=torch.bfloat16, device=device)
+    lse = torch.empty((sq, plan.num_heads), dtype=torch.float32, device=device)
+    ws = torch.empty((max(plan.workspace_bytes, 16),), dtype=torch.uint8, device=device)
+    return o, lse, ws
+
+
+def decode(plan: Plan, q, kv, sm_scale: float, kv_scale: float = 1.0, out=None, stream=None):
+    """Run + reduce on the given (or freshly allocated) outputs; returns (O, LSE)."""
+    o, lse, ws = out if out is not None else alloc_outputs(plan, q.device)
+    mla_decode_run(plan, q, kv, sm_scale, kv_scale, o, lse, ws, ws.numel(), stream)
+    mla_decode_reduce(plan, ws, o, lse, stream)
+    return o, lse

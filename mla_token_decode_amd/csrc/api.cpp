@@ -1,0 +1,246 @@
+// C ABI of libmla_decode.so: argument validation, device checks and kernel
+// launches.  See include/mla_decode.h for the contract of each call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <new>
+
+#include "plan.hpp"
+
+namespace mla {
+const char* last_error();
+hipError_t launch_main(const MainArgs& a, bool fp8, int nrt, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+int g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+int g_dev_cus[kMaxDevices];
+
+// Checks that the current device is a gfx950 and returns its CU count.
+mla_status current_device(int* cus) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    set_error("hipGetDevice failed: %s", hipGetErrorString(e));
+    return MLA_ERR_DEVICE;
+  }
+  if (dev >= kMaxDevices) {
+    set_error("device index %d out of range", dev);
+    return MLA_ERR_DEVICE;
+  }
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) {
+      set_error("hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+      return MLA_ERR_DEVICE;
+    }
+    g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_cus[dev] = prop.multiProcessorCount;
+  }
+  if (g_dev_state[dev] != 1) {
+    set_error("device %d is not gfx950; this library only carries gfx950 code", dev);
+    return MLA_ERR_UNSUPPORTED;
+  }
+  if (cus) *cus = g_dev_cus[dev];
+  return MLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" {
+
+mla_status mla_decode_plan(int32_t batch, int32_t num_heads, const int32_t* q_len,
+                           const int32_t* kv_len, mla_kv_dtype kv_dtype,
+                           const mla_plan_options* opts, mla_plan** plan_out,
+                           size_t* workspace_bytes_out) {
+  if (!plan_out) {
+    set_error("plan_out must be non-null");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  *plan_out = nullptr;
+  mla_plan_options o{};
+  if (opts) o = *opts;
+  if (o.num_cus == 0) {
+    int cus = 0;
+    mla_status st = current_device(&cus);
+    if (st != MLA_OK) return st;
+    o.num_cus = cus;
+  }
+  mla_plan* p = new (std::nothrow) mla_plan();
+  if (!p) {
+    set_error("out of host memory");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  mla_status st = build_plan(batch, num_heads, q_len, kv_len, kv_dtype, &o, p);
+  if (st != MLA_OK) {
+    delete p;
+    return st;
+  }
+  *plan_out = p;
+  if (workspace_bytes_out) *workspace_bytes_out = p->workspace_bytes;
+  return MLA_OK;
+}
+
+void mla_plan_destroy(mla_plan* plan) { delete plan; }
+
+const char* mla_last_error(void) { return mla::last_error(); }
+
+mla_status mla_plan_query(const mla_plan* plan, int32_t seq, int32_t* fold, int32_t* tiles,
+                          int32_t* splits, int32_t* chunk_len) {
+  if (!plan) {
+    set_error("plan must be non-null");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (seq < 0 || seq >= plan->batch) {
+    set_error("sequence index %d out of range [0, %d)", seq, plan->batch);
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  const SeqDesc& d = plan->seqs[seq];
+  if (fold) *fold = d.F;
+  if (tiles) *tiles = d.T;
+  if (splits) *splits = d.S;
+  if (chunk_len) *chunk_len = d.L;
+  return MLA_OK;
+}
+
+mla_status mla_plan_info(const mla_plan* plan, int32_t* num_units, int32_t* num_split_tiles,
+                         int32_t* num_launches, size_t* workspace_bytes) {
+  if (!plan) {
+    set_error("plan must be non-null");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (num_units) *num_units = plan->num_units;
+  if (num_split_tiles) *num_split_tiles = plan->num_split_tiles;
+  if (num_launches) *num_launches = static_cast<int32_t>(plan->launches.size());
+  if (workspace_bytes) *workspace_bytes = plan->workspace_bytes;
+  return MLA_OK;
+}
+
+mla_status mla_decode_run(const mla_plan* plan, const void* q, const void* kv, float sm_scale,
+                          float kv_scale, void* o, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!plan) {
+    set_error("plan must be non-null");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (!q || !kv || !o || !lse) {
+    set_error("q, kv, o and lse must be non-null device pointers");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(o) || !aligned16(lse)) {
+    set_error("q, kv, o and lse must be 16-byte aligned");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) {
+    set_error("sm_scale must be finite and > 0 (got %g)", static_cast<double>(sm_scale));
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  const bool fp8 = plan->dtype == MLA_KV_FP8_E4M3;
+  if (fp8 && (!(kv_scale > 0.0f) || !std::isfinite(kv_scale))) {
+    set_error("fp8 kv_scale must be finite and > 0 (got %g)", static_cast<double>(kv_scale));
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (!fp8 && kv_scale != 1.0f) {
+    set_error("bf16 KV takes kv_scale == 1 (got %g)", static_cast<double>(kv_scale));
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (workspace_bytes < plan->workspace_bytes) {
+    set_error("workspace of %zu bytes is smaller than the planned %zu", workspace_bytes,
+              plan->workspace_bytes);
+    return MLA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if (plan->workspace_bytes > 0 && (!workspace || !aligned16(workspace))) {
+    set_error("this plan needs a 16-byte aligned workspace of %zu bytes", plan->workspace_bytes);
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  mla_status st = current_device(nullptr);
+  if (st != MLA_OK) return st;
+
+  MainArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint8_t*>(kv);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.part_lse = plan->workspace_bytes ? static_cast<float*>(workspace) : nullptr;
+  a.part_o = plan->workspace_bytes
+                 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->part_o_offset)
+                 : nullptr;
+  const double log2e = 1.4426950408889634;
+  a.scale_log2 = static_cast<float>(static_cast<double>(sm_scale) * (fp8 ? kv_scale : 1.0) * log2e);
+  a.o_scale = fp8 ? kv_scale : 1.0f;
+  a.H = plan->H;
+  for (const Launch& ln : plan->launches) {
+    a.num_seqs = ln.seq_end - ln.seq_begin;
+    a.num_units = ln.num_units;
+    a.units_per_xcd = (ln.num_units + kNumXcd - 1) / kNumXcd;
+    for (int b = ln.seq_begin; b < ln.seq_end; ++b) a.seqs[b - ln.seq_begin] = plan->seqs[b];
+    hipError_t e = launch_main(a, fp8, ln.nrt, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+      set_error("main kernel launch failed: %s", hipGetErrorString(e));
+      return MLA_ERR_DEVICE;
+    }
+  }
+  return MLA_OK;
+}
+
+mla_status mla_decode_reduce(const mla_plan* plan, const void* workspace, void* o, float* lse,
+                             void* stream) {
+  if (!plan) {
+    set_error("plan must be non-null");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (plan->total_part_rows == 0) return MLA_OK;
+  if (!workspace || !o || !lse) {
+    set_error("workspace, o and lse must be non-null device pointers");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (!aligned16(workspace) || !aligned16(o) || !aligned16(lse)) {
+    set_error("workspace, o and lse must be 16-byte aligned");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  mla_status st = current_device(nullptr);
+  if (st != MLA_OK) return st;
+  ReduceArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.part_lse = static_cast<const float*>(workspace);
+  a.part_o = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + plan->part_o_offset);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.H = plan->H;
+  for (const Launch& ln : plan->launches) {
+    if (ln.num_split_rows == 0) continue;
+    int ns = 0, rows = 0;
+    for (int b = ln.seq_begin; b < ln.seq_end; ++b) {
+      const SeqDesc& d = plan->seqs[b];
+      if (d.S <= 1) continue;
+      a.seqs[ns] = d;
+      a.row0[ns] = rows;
+      rows += d.T * d.R;
+      ++ns;
+    }
+    a.num_seqs = ns;
+    a.num_rows = rows;
+    hipError_t e = launch_reduce(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+      set_error("reduce kernel launch failed: %s", hipGetErrorString(e));
+      return MLA_ERR_DEVICE;
+    }
+  }
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Internal plan structures shared by the host plan and the kernel launchers.
+// Not part of the public ABI (include/mla_decode.h is).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "mla_decode.h"
+
+namespace mla {
+
+constexpr int kDqk = MLA_DQK;            // 576 = 512 latent + 64 rope
+constexpr int kDv = MLA_DV;              // 512
+constexpr int kMaxRows = MLA_MAX_TILE_ROWS;  // 128
+constexpr int kGranule = MLA_KV_GRANULE;     // 64 keys
+constexpr int kMaxSeqPerLaunch = 60;     // sequence descriptors travel in kernel arguments
+constexpr int kMaxUnitRows = 64;         // rows one workgroup processes (2 groups x 2 MFMA tiles)
+constexpr int kNumXcd = 8;               // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// One sequence as the kernels see it.  All counts fit int32 for any cache that
+// fits in one GPU's HBM (row counts, not bytes); byte offsets are formed in
+// 64-bit inside the kernels.
+struct SeqDesc {
+  int32_t q_row0;     // first Q/O/LSE row of the sequence: (sum of earlier q_len) * H
+  int32_t kv_row0;    // first KV row of the sequence
+  int32_t part_row0;  // first partial row in the workspace (-1 when the sequence is unsplit)
+  int32_t n;          // kv_len
+  int32_t qlen;       // q_len
+  int32_t F;          // fold factor
+  int32_t T;          // tiles = qlen / F
+  int32_t R;          // rows per tile = H * F
+  int32_t S;          // effective split count
+  int32_t L;          // chunk length (keys, multiple of kGranule)
+  int32_t NRB;        // row blocks per tile (tiles of more than 96 rows are cut)
+  int32_t RBS;        // rows per row block (multiple of 16 unless NRB == 1)
+  int32_t unit0;      // first work unit of the sequence within its launch
+};
+
+struct MainArgs {
+  const uint16_t* q;
+  const uint8_t* kv;
+  uint16_t* o;
+  float* lse;
+  float* part_lse;     // [total partial rows]
+  float* part_o;       // [total partial rows][512]
+  float scale_log2;    // sm_scale * kv_scale * log2(e)
+  float o_scale;       // kv_scale (fp8) or 1 (bf16)
+  int32_t H;
+  int32_t num_seqs;
+  int32_t num_units;
+  int32_t units_per_xcd;
+  SeqDesc seqs[kMaxSeqPerLaunch];
+};
+
+struct ReduceArgs {
+  const float* part_lse;
+  const float* part_o;
+  uint16_t* o;
+  float* lse;
+  int32_t H;
+  int32_t num_seqs;
+  int32_t num_rows;    // split rows covered by this launch
+  int32_t pad_;
+  SeqDesc seqs[kMaxSeqPerLaunch];
+  int32_t row0[kMaxSeqPerLaunch];  // first reduce row of each sequence in this launch
+};
+
+struct Launch {
+  int seq_begin, seq_end;  // [begin, end) global sequence indices
+  int num_units;
+  int nrt;                 // 16-row MFMA tiles per row group (1..3), from the widest unit
+  int num_split_rows;      // rows the reduce merges for this slice
+};
+
+}  // namespace mla
+
+struct mla_plan {
+  int32_t batch = 0;
+  int32_t H = 0;
+  mla_kv_dtype dtype = MLA_KV_BF16;
+  int32_t num_cus = 0;
+  std::vector<mla::SeqDesc> seqs;  // global: unit0 is relative to the sequence's launch
+  std::vector<mla::Launch> launches;
+  int64_t total_part_rows = 0;
+  int32_t num_units = 0;
+  int32_t num_split_tiles = 0;
+  size_t workspace_bytes = 0;
+  size_t part_o_offset = 0;  // byte offset of partial O inside the workspace
+};
+
+namespace mla {
+// Implemented in plan.cpp.
+mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int32_t* kv_len,
+                      mla_kv_dtype dtype, const mla_plan_options* opts, mla_plan* plan);
+void set_error(const char* fmt, ...);
+int fold_factor(int H, int q, int cap);
+void split_layout(int64_t n, int S, int G, int32_t* L, int32_t* S_eff);
+}  // namespace mla

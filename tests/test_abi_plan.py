@@ -1,0 +1,135 @@
+"""C-ABI library: loads, exports every symbol include/mla_decode.h declares,
+and its host plan agrees with the oracle's independent fold / split code.
+CPU only: no compute call touches a GPU here (num_cus is passed explicitly)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from mla_token_decode_amd import binding as mb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = mb.lib()
+    names = declared_functions()
+    assert set(names) == set(mb.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def plan(H, q_len, kv_len, fp8=False, **kw):
+    kw.setdefault("num_cus", 256)
+    return mb.Plan(H, q_len, kv_len, fp8, **kw)
+
+
+@pytest.mark.parametrize("H", [1, 6, 7, 12, 24, 40, 48, 64, 96, 128])
+def test_fold_matches_oracle(H):
+    for q in range(1, 17):
+        p = plan(H, [q], [max(q, 100)])
+        F, T, S, L = p.query(0)
+        assert F == oracle.fold_factor(H, q), (H, q)
+        assert T == q // F
+
+
+def test_force_fold_caps_fold():
+    p = plan(12, [8, 6, 4], [50, 50, 50], force_fold=1)
+    assert [p.query(b)[0] for b in range(3)] == [1, 1, 1]
+    p = plan(12, [8, 6, 4], [50, 50, 50], force_fold=3)
+    assert [p.query(b)[0] for b in range(3)] == [2, 3, 2]
+
+
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 100, 127, 128, 129, 4096, 125000, 131072, 1048576])
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 16, 100, 257])
+def test_forced_split_layout_bit_exact(n, S):
+    q = 1
+    p = plan(12, [q], [n], force_splits=S)
+    _, _, S_eff, L = p.query(0)
+    assert (L, S_eff) == oracle.split_layout(n, S, mb.KV_GRANULE)
+
+
+def test_auto_plan_shapes_of_the_workloads():
+    # bf16 H=12 q=8 ctx 131072: one 96-row tile, split so every CU has work
+    p = plan(12, [8], [131072])
+    F, T, S, L = p.query(0)
+    assert (F, T) == (8, 1) and S > 1 and L % 64 == 0
+    assert p.workspace_bytes > 0
+    # H=96 q=8: F=1, eight tiles
+    p = plan(96, [8], [125000])
+    assert p.query(0)[:2] == (1, 8)
+    # ragged
+    ql = [1, 2, 3, 4] * 8
+    p = plan(96, ql, [32768] * 32)
+    for b in range(32):
+        assert p.query(b)[:2] == (1, ql[b])
+    # short context: a single chunk needs no workspace when forced
+    p = plan(12, [2], [4096], force_splits=1)
+    assert p.query(0)[2] == 1 and p.workspace_bytes == 0
+
+
+def test_workspace_size_formula():
+    H, ql, kl = 12, [8, 3, 1], [5000, 700, 64]
+    p = plan(H, ql, kl, force_splits=4)
+    rows = 0
+    for b in range(3):
+        F, T, S, L = p.query(b)
+        if S > 1:
+            rows += T * S * H * F
+    lse_bytes = -(-rows * 4 // 256) * 256
+    assert p.workspace_bytes == lse_bytes + rows * 512 * 4
+
+
+def test_many_sequences_use_several_launches():
+    p = plan(8, [1] * 150, [300] * 150)
+    assert p.num_launches == 3
+
+
+@pytest.mark.parametrize("args,status", [
+    ((12, [0], [10]), mb.MLA_ERR_INVALID_ARGUMENT),
+    ((12, [5], [4]), mb.MLA_ERR_INVALID_ARGUMENT),
+    ((0, [1], [4]), mb.MLA_ERR_INVALID_ARGUMENT),
+    ((129, [1], [4]), mb.MLA_ERR_UNSUPPORTED),
+    ((12, [], []), mb.MLA_ERR_INVALID_ARGUMENT),
+])
+def test_plan_rejects(args, status):
+    with pytest.raises(mb.MlaError) as e:
+        plan(*args)
+    assert e.value.status == status
+    assert e.value.message
+
+
+def test_run_rejects_bad_arguments_before_touching_a_device():
+    p = plan(12, [2], [100], force_splits=2)
+    good = 1 << 20
+    cases = [
+        dict(q=None), dict(q=good + 8), dict(sm_scale=0.0), dict(sm_scale=float("nan")),
+        dict(kv_scale=2.0), dict(workspace_bytes=p.workspace_bytes - 1),
+    ]
+    for c in cases:
+        kw = dict(q=good, kv=good, sm_scale=0.04, kv_scale=1.0, o=good, lse=good, workspace=good,
+                  workspace_bytes=p.workspace_bytes, stream=0)
+        kw.update(c)
+        with pytest.raises(mb.MlaError) as e:
+            mb.mla_decode_run(p, **kw)
+        assert e.value.status in (mb.MLA_ERR_INVALID_ARGUMENT, mb.MLA_ERR_WORKSPACE_TOO_SMALL)
+    pf = plan(12, [2], [100], fp8=True)
+    with pytest.raises(mb.MlaError):
+        mb.mla_decode_run(pf, good, good, 0.04, 0.0, good, good, good, pf.workspace_bytes, 0)
+
+
+def test_query_out_of_range():
+    p = plan(4, [1, 1], [3, 3])
+    with pytest.raises(mb.MlaError):
+        p.query(2)

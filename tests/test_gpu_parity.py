@@ -1,0 +1,160 @@
+"""GPU parity: the HIP path (called through the C ABI) against the fp64 oracle.
+
+Small shapes are compared element by element; the full-size workloads are
+compared on sampled rows the oracle computes one by one.  Extra gates beyond
+the graded tolerances: planted-key probes (exact answers), peaked queries (|O|
+far above the tolerance), folded == unfolded, split invariance, bitwise replay
+determinism, NaN-poisoned workspace."""
+import numpy as np
+import pytest
+
+from mla_token_decode_amd import inputs as gen
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+SMALL_CASES = [
+    # (H, q_len, kv_len, fp8)
+    (12, [2], [4096], False),
+    (12, [8], [700], False),
+    (12, [8], [700], True),
+    (96, [8], [300], False),
+    (96, [3], [257], True),
+    (24, [8], [129], False),
+    (1, [1], [1], False),
+    (6, [16], [16], False),
+    (7, [20], [90], False),
+    (40, [6], [200], True),
+    (64, [2], [65], False),
+    (128, [1], [130], False),
+    (128, [2], [64], False),
+    (12, [1, 2, 3, 4, 8], [33, 64, 65, 500, 8], False),
+    (96, [1, 2, 3, 4], [100, 40, 9, 4], True),
+]
+
+
+@pytest.mark.parametrize("H,q_len,kv_len,fp8", SMALL_CASES)
+@pytest.mark.parametrize("peaked", [False, True])
+def test_small_shapes_vs_oracle(H, q_len, kv_len, fp8, peaked):
+    gu.log(f"case H={H} q={q_len} n={kv_len} fp8={fp8} peaked={peaked}")
+    inp = gen.random_inputs(H, q_len, kv_len, fp8, seed=hash((H, len(q_len), kv_len[0])) % 1000)
+    if peaked:
+        inp = gen.peaked_inputs(inp, beta=10.0, seed=3)
+    ro, rl = gu.oracle_full(inp)
+    for splits in (0, 1, 3):
+        o, lse, plan = gu.run_gpu(inp, force_splits=splits)
+        gu.compare(o, lse, ro, rl, fp8, f"splits={splits} units={plan.num_units}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_planted_probe(fp8):
+    H, q_len, kv_len = 12, [8, 3], [600, 200]
+    markers = [[(0, 0), (63, 1), (64, 13), (600 - 8, 0), (600 - 7, 12), (599, 31), (150, 5),
+                (191, 24), (192, 36), (255, 48), (256, 60)],
+               [(0, 2), (199, 6), (198, 5), (197, 4), (63, 3), (64, 15), (127, 27)]]
+    inp = gen.planted_inputs(H, q_len, kv_len, markers, fp8=fp8)
+    ro, rl = gu.oracle_full(inp)
+    for splits in (1, 2, 5, 9):
+        o, lse, _ = gu.run_gpu(inp, force_splits=splits)
+        gu.log(f"planted fp8={fp8} splits={splits}")
+        # bf16 output rounding is the only expected error on these exact inputs
+        err = np.abs(o - ro) - 2.0 ** -8 * np.abs(ro)
+        assert err.max() <= 1e-6, f"max excess {err.max()}"
+        assert np.abs(lse - rl).max() <= 1e-3
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_folded_equals_unfolded(fp8):
+    inp = gen.peaked_inputs(gen.random_inputs(12, [8, 4], [1000, 333], fp8, seed=5), beta=10.0)
+    for splits in (1, 4):
+        o1, l1, p1 = gu.run_gpu(inp, force_splits=splits)
+        o2, l2, p2 = gu.run_gpu(inp, force_splits=splits, force_fold=1)
+        assert p1.query(0)[0] == 8 and p2.query(0)[0] == 1
+        same = np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        gu.log(f"folded vs unfolded splits={splits}: bitwise={same} "
+               f"max|dO|={np.abs(o1 - o2).max():.3e} max|dLSE|={np.abs(l1 - l2).max():.3e}")
+        assert same
+
+
+def test_split_counts_agree():
+    inp = gen.peaked_inputs(gen.random_inputs(12, [8], [5000], False, seed=7), beta=10.0)
+    ro, rl = gu.oracle_full(inp)
+    for splits in (1, 2, 7, 40, 79):
+        o, lse, _ = gu.run_gpu(inp, force_splits=splits)
+        gu.compare(o, lse, ro, rl, False, f"splits={splits}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_replay_is_bitwise_deterministic(fp8):
+    inp = gen.random_inputs(96, [8], [3000], fp8, seed=9)
+    dev = gu.to_device(inp)
+    o1, l1, _ = gu.run_gpu(inp, dev)
+    o2, l2, _ = gu.run_gpu(inp, dev)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_poisoned_workspace_is_never_read_unwritten():
+    inp = gen.random_inputs(12, [8, 2], [3000, 77], False, seed=13)
+    ro, rl = gu.oracle_full(inp)
+    o, lse, _ = gu.run_gpu(inp, poison_workspace=True, force_splits=6)
+    gu.compare(o, lse, ro, rl, False, "poisoned workspace")
+
+
+def test_outputs_outside_the_rows_are_untouched():
+    import torch
+    from mla_token_decode_amd import binding as mb
+    inp = gen.random_inputs(12, [4], [900], False, seed=17)
+    plan = mb.Plan(12, inp.q_len, inp.kv_len, False, force_splits=3)
+    q, kv = gu.to_device(inp)
+    rows = 4 * 12
+    guard = 4096
+    o_big = torch.full((rows * 512 + 2 * guard,), -7.0, dtype=torch.bfloat16, device="cuda")
+    l_big = torch.full((rows + 2 * guard,), -7.0, dtype=torch.float32, device="cuda")
+    o = o_big[guard:guard + rows * 512]
+    lse = l_big[guard:guard + rows]
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    mb.mla_decode_run(plan, q, kv, inp.sm_scale, 1.0, o, lse, ws, ws.numel())
+    mb.mla_decode_reduce(plan, ws, o, lse)
+    torch.cuda.synchronize()
+    ob, lb = o_big.float().cpu().numpy(), l_big.cpu().numpy()
+    assert np.all(ob[:guard] == -7.0) and np.all(ob[guard + rows * 512:] == -7.0)
+    assert np.all(lb[:guard] == -7.0) and np.all(lb[guard + rows:] == -7.0)
+    ro, rl = gu.oracle_full(inp)
+    gu.compare(o.double().cpu().numpy().reshape(4, 12, 512), lse.double().cpu().numpy().reshape(4, 12),
+               ro, rl, False, "guarded")
+
+
+def test_identical_keys_give_the_value_row():
+    inp = gen.identical_key_inputs(12, [8, 1], [40, 1000], seed=19)
+    o, lse, _ = gu.run_gpu(inp, force_splits=3)
+    kv = gen.f32_from_bf16_bits(inp.kv).astype(np.float64)
+    np.testing.assert_allclose(o[:8], np.broadcast_to(kv[0, :512], (8, 12, 512)), rtol=2 ** -7, atol=1e-6)
+    np.testing.assert_allclose(o[8:], np.broadcast_to(kv[40, :512], (1, 12, 512)), rtol=2 ** -7, atol=1e-6)
+    ro, rl = gu.oracle_full(inp)
+    assert np.abs(lse - rl).max() <= 1e-3
+
+
+@pytest.mark.parametrize("name", gen.WORKLOADS)
+def test_workload_sampled_rows(name):
+    gu.log(f"workload {name}")
+    inp = gu.workload_inputs(name)
+    o, lse, plan = gu.run_gpu(inp)
+    gu.log(f"  plan: units={plan.num_units} split_tiles={plan.num_split_tiles} "
+           f"fold/tiles/splits/L of seq0={plan.query(0)}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rows = gu.sample_rows(inp, 24 if name != "small" else 48)
+    ro, rl = gu.oracle_rows(inp, rows)
+    gu.compare(o.reshape(-1, 512)[rows], lse.reshape(-1)[rows], ro, rl, inp.kv_fp8, name)
+
+
+@pytest.mark.parametrize("name", ["h12_131k", "h96_125k", "h12_1m_fp8"])
+def test_workload_peaked_sampled_rows(name):
+    gu.log(f"peaked workload {name}")
+    inp = gen.peaked_inputs(gu.workload_inputs(name), beta=10.0, seed=1)
+    o, lse, _ = gu.run_gpu(inp)
+    rows = gu.sample_rows(inp, 16, seed=2)
+    ro, rl = gu.oracle_rows(inp, rows)
+    do, dl, mo = gu.compare(o.reshape(-1, 512)[rows], lse.reshape(-1)[rows], ro, rl, inp.kv_fp8,
+                            f"{name} peaked")
+    assert mo > 5 * gu.TOL_O[inp.kv_fp8]  # the check is discriminating
