@@ -89,6 +89,7 @@ def sample_rows(inp, count, seed=0):
             break
     rng = np.random.default_rng([seed, 11])
     total = int(q_off[-1]) * H
+    count = min(count, total)
     while len(rows) < count:
         rows.add(int(rng.integers(0, total)))
     return np.array(sorted(rows), dtype=np.int64)
