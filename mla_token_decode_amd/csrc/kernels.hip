@@ -124,6 +124,38 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 w) {
   return r;
 }
 
+// O accumulation: an MFMA whose accumulator is constrained to the AGPR file, so
+// the register allocator never copies O between register files.  The compiler
+// cannot see hazards inside inline assembly: the leading s_nop covers a VALU
+// write of the A/B operands just before (the V conversion), and the code
+// around the O uses adds margins for the MFMA-result reads (rescale,
+// epilogue).
+template <bool OA>
+__device__ __forceinline__ void mfma_o(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  if constexpr (OA)
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+// Score MFMA: S^T (VGPRs, read by the softmax) += K . Q^T.  QA places the Q
+// operand in the AGPR file (when it fits next to O) so VGPRs stay free for the
+// softmax; otherwise in VGPRs.  ZERO starts the accumulation from 0.
+template <bool QA, bool ZERO>
+__device__ __forceinline__ void mfma_s(f32x4& acc, const bf16x8& k, const bf16x8& q) {
+  if constexpr (ZERO) {
+    if constexpr (QA)
+      asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "a"(q));
+    else
+      asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "v"(q));
+  } else {
+    if constexpr (QA)
+      asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "a"(q));
+    else
+      asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "v"(q));
+  }
+}
+
 // Multiply one accumulator element in place without leaving the AGPR file, so
 // the loop-carried O accumulators stay AGPR values on every control path.
 __device__ __forceinline__ float scale_agpr(float a, float alpha) {
@@ -171,8 +203,8 @@ __device__ __forceinline__ void issue_tile(const uint8_t* kv_seq, int k0, int va
 template <bool FP8>
 struct FragBases {
   int k[2][2];   // [kt][r]
-  int va[4];     // [c]  (bf16: key 4g + i/4;  fp8: the single tr8 row)
-  int vb[4];     // [c]  (bf16: key 16 + 4g + i/4; unused for fp8)
+  int va[4];     // [c]  (bf16: key 4g + i/4, the key 16 + 4g + i/4 is 16 rows
+                 //       further with the same swizzle;  fp8: the single tr8 row)
 };
 
 template <bool FP8>
@@ -193,21 +225,15 @@ __device__ __forceinline__ FragBases<FP8> frag_bases(int l16, int g) {
   }
   const int i = l16;
   if constexpr (!FP8) {
-    const int ka = 4 * g + (i >> 2), kb = 16 + 4 * g + (i >> 2);
+    const int ka = 4 * g + (i >> 2);
     const int h = (i & 3) >> 1;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      fb.va[c] = ka * C::kRowBytes + 16 * ((2 * c + h) ^ C::swz(ka)) + 8 * (i & 1);
-      fb.vb[c] = kb * C::kRowBytes + 16 * ((2 * c + h) ^ C::swz(kb)) + 8 * (i & 1);
-    }
+    for (int c = 0; c < 4; ++c) fb.va[c] = ka * C::kRowBytes + 16 * ((2 * c + h) ^ C::swz(ka)) + 8 * (i & 1);
   } else {
     const int kk = i >> 1;
     const int key = kk < 4 ? 4 * g + kk : 16 + 4 * g + (kk - 4);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      fb.va[c] = key * C::kRowBytes + 16 * (c ^ C::swz(key)) + 8 * (i & 1);
-      fb.vb[c] = 0;
-    }
+    for (int c = 0; c < 4; ++c) fb.va[c] = key * C::kRowBytes + 16 * (c ^ C::swz(key)) + 8 * (i & 1);
   }
   return fb;
 }
@@ -267,8 +293,9 @@ struct VRaw {
 template <bool FP8, int CT>
 __device__ __forceinline__ void issue_v(VRaw<FP8>& r, lds_u8* tile, const FragBases<FP8>& fb) {
   if constexpr (!FP8) {
+    // keys 16 apart share the swizzle, so the second piece is 16 rows further
     r.a = ds_read_tr16_b64<128 * (CT >> 2)>(tile + fb.va[CT & 3]);
-    r.b = ds_read_tr16_b64<128 * (CT >> 2)>(tile + fb.vb[CT & 3]);
+    r.b = ds_read_tr16_b64<128 * (CT >> 2) + 16 * KvCfg<FP8>::kRowBytes>(tile + fb.va[CT & 3]);
   } else {
     r.a = ds_read_tr8_b64<64 * (CT >> 2)>(tile + fb.va[CT & 3]);
   }
@@ -307,11 +334,11 @@ __device__ __forceinline__ void tile_compute(lds_u8* tile, float* xs_mine, const
                                              const int (&lim)[NRT], int k0, bool edge,
                                              float scale_log2, int g, int lane) {
   // ---- partial S^T over this wave's 288 columns, K fragments one step ahead ----
+  // register files: NRT <= 2 keeps O (16 NRT f32x4) in VGPRs and Q in AGPRs;
+  // NRT = 3 needs O in AGPRs and Q in VGPRs
+  constexpr bool kQinAgpr = NRT <= 2;
+  constexpr bool kOinAgpr = !kQinAgpr;
   f32x4 sacc[2][NRT];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) sacc[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   bf16x8 kf[2][2];
   kf[0][0] = read_k<FP8, 0, 9 * DH>(tile, fb);
   kf[0][1] = read_k<FP8, 1, 9 * DH>(tile, fb);
@@ -325,10 +352,11 @@ __device__ __forceinline__ void tile_compute(lds_u8* tile, float* xs_mine, const
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-        sacc[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[cur][kt], qf[rt][j], sacc[kt][rt], 0, 0, 0);
+      for (int rt = 0; rt < NRT; ++rt) mfma_s<kQinAgpr, j == 0>(sacc[kt][rt], kf[cur][kt], qf[rt][j]);
     __builtin_amdgcn_sched_barrier(0);
   });
+  // the score MFMAs retire before their results are read below
+  asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");
 
   // ---- exchange partials with the other half of the row group ----
 #pragma unroll
@@ -379,10 +407,15 @@ __device__ __forceinline__ void tile_compute(lds_u8* tile, float* xs_mine, const
         // the last MFMA that wrote O retired long ago (a whole QK phase ran
         // since); the nops are a margin for the accumulator read hazard
         asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+        if constexpr (kOinAgpr) {
 #pragma unroll
-        for (int ct = 0; ct < 16; ++ct)
+          for (int ct = 0; ct < 16; ++ct)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) oacc[ct][rt][e] = scale_agpr(oacc[ct][rt][e], alpha);
+            for (int e = 0; e < 4; ++e) oacc[ct][rt][e] = scale_agpr(oacc[ct][rt][e], alpha);
+        } else {
+#pragma unroll
+          for (int ct = 0; ct < 16; ++ct) oacc[ct][rt] *= alpha;
+        }
         asm volatile("s_nop 7" ::: "memory");
       }
       m_run[rt] = m_new;
@@ -412,7 +445,7 @@ __device__ __forceinline__ void tile_compute(lds_u8* tile, float* xs_mine, const
     const bf16x8 vf = finish_v<FP8>(vr[cur]);
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
-      oacc[c][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rt], oacc[c][rt], 0, 0, 0);
+      mfma_o<kOinAgpr>(oacc[c][rt], vf, pf[rt]);
     __builtin_amdgcn_sched_barrier(0);
   });
 }
@@ -548,6 +581,7 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
   }
 
   if (!wave_active) return;
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // last O MFMA retired before reads
 
   // ---- epilogue: this wave's rows x columns [256 dh, 256 dh + 256) ----
   const float ln2 = 0.69314718055994530942f;
@@ -596,12 +630,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_main(const MainArgs ar
     unit_body<FP8, NRT, 0>(args, smem);
 }
 
-// Split-KV merge: one wave per split output row; lane c covers columns
-// 8c .. 8c+7; partials are merged in ascending chunk order.
-__global__ __launch_bounds__(kThreads) void mla_decode_reduce_kernel(const ReduceArgs args) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int gr = blockIdx.x * kWaves + wave;
+// Split-KV merge.  One 512-thread block per (split output row, column half):
+// wave w folds chunks s = w, w + 8, ... (lane c owns columns 4c .. 4c+3 of the
+// half), then the 8 waves' sums are added in wave order through LDS.  Every
+// sum has a fixed order, so replays are bitwise identical.
+constexpr int kRedThreads = 512;
+constexpr int kRedWaves = kRedThreads / 64;
+
+__device__ __forceinline__ float wave_max64(float v) {
+  v = wave_max_across_groups(v);          // lanes l, l^16, l^32, l^48
+#pragma unroll
+  for (int d = 8; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d));
+  return v;
+}
+
+__global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_kernel(const ReduceArgs args) {
+  __shared__ f32x4 red_acc[kRedWaves][64];
+  __shared__ float red_w[kRedWaves];
+  const int gr = blockIdx.x >> 1;
+  const int half = blockIdx.x & 1;
   if (gr >= args.num_rows) return;
   int b = 0;
   while (b + 1 < args.num_seqs && args.row0[b + 1] <= gr) ++b;
@@ -612,34 +659,43 @@ __global__ __launch_bounds__(kThreads) void mla_decode_reduce_kernel(const Reduc
   const int r = local % R;
   const int S = sd.S;
   const int64_t pbase = (int64_t)sd.part_row0 + (int64_t)t * S * R + r;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
 
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, args.part_lse[pbase + (int64_t)s * R]);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, args.part_lse[pbase + (int64_t)s * R]);
+  M = wave_max64(M);
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.0f;
-  for (int s = 0; s < S; ++s) {
+  const float* po = args.part_o + 256 * half + 4 * lane;
+#pragma unroll 4
+  for (int s = wave; s < S; s += kRedWaves) {
     const int64_t prow = pbase + (int64_t)s * R;
     const float ls = args.part_lse[prow];
-    if (ls == -INFINITY) continue;
+    if (ls == -INFINITY) continue;  // a chunk this row cannot see: weight 0
     const float w = __expf(ls - M);
     W += w;
-    const f32x4* src = (const f32x4*)(args.part_o + prow * kDv + 8 * lane);
-    const f32x4 a = src[0], c = src[1];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] += w * a[e];
-      acc[4 + e] += w * c[e];
-    }
+    acc += w * *(const f32x4*)(po + prow * kDv);
   }
-  const float inv = 1.0f / W;
+  red_acc[wave][lane] = acc;
+  if (lane == 0) red_w[wave] = W;
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4 tot = red_acc[0][lane];
+  float Wt = red_w[0];
+#pragma unroll
+  for (int w2 = 1; w2 < kRedWaves; ++w2) {
+    tot += red_acc[w2][lane];
+    Wt += red_w[w2];
+  }
+  const float inv = 1.0f / Wt;
   const int64_t orow = (int64_t)sd.q_row0 + (int64_t)t * R + r;
-  uint4 pk;
-  pk.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  pk.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  pk.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-  pk.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-  *(uint4*)(args.o + orow * kDv + 8 * lane) = pk;
-  if (lane == 0) args.lse[orow] = M + __logf(W);
+  uint2 pk;
+  pk.x = pack_bf16x2(tot[0] * inv, tot[1] * inv);
+  pk.y = pack_bf16x2(tot[2] * inv, tot[3] * inv);
+  *(uint2*)(args.o + orow * kDv + 256 * half + 4 * lane) = pk;
+  if (half == 0 && lane == 0) args.lse[orow] = M + __logf(Wt);
 }
 
 // ------------------------------------------------------------- launchers
@@ -664,9 +720,9 @@ hipError_t launch_main(const MainArgs& a, bool fp8, int nrt, hipStream_t stream)
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
-  const int grid = (a.num_rows + kWaves - 1) / kWaves;
+  const int grid = 2 * a.num_rows;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_decode_reduce_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(mla_decode_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, stream, a);
   return hipGetLastError();
 }
 
