@@ -1,27 +1,31 @@
 // MLA speculative-verify decode kernels for gfx950 (MI355X, CDNA4).
 //
-// Main kernel: one workgroup (4 waves, 256 threads) per work unit = one
-// folded tile (R = H*F rows: F verify tokens x H heads, contiguous in Q) and
-// one split-KV chunk of its sequence.  The KV chunk is streamed once from HBM
-// into LDS and shared by all R rows -- the fold_sq idea of "[Kimi-K3] Allow
-// DSPARK verify on cutedsl_mla (fold_sq)" (sglang PR #33650), section
-// "Decision rule", paragraph "Why".  Split chunks write normalised partials
-// that the reduce kernel merges (same PR, section "GPU timeline").
+// Main kernel: one workgroup (4 waves, 256 threads) per work unit = up to 64
+// rows of one folded tile (F verify tokens x H heads, contiguous in Q) and one
+// split-KV chunk of its sequence.  The chunk is streamed once from HBM and
+// shared by all rows of the unit -- the fold_sq idea of "[Kimi-K3] Allow DSPARK
+// verify on cutedsl_mla (fold_sq)" (sglang PR #33650), section "Decision rule",
+// paragraph "Why".  Split chunks write normalised partials that the reduce
+// kernel merges (same PR, section "GPU timeline").
 //
-// Work split inside a workgroup (4 waves, one per SIMD): wave w = (row group
-// rg = w / 2, half dh = w % 2).  A row group is up to 48 rows (NRT 16-row
-// MFMA tiles); the wave pair of a group splits the 576 score columns and the
-// 512 value columns in halves:
-//   S^T[key][row] partial = K[:, 288dh:288dh+288] . Q^T  (bf16 MFMA 16x16x32;
-//                  A = K from LDS, B = the wave's Q half held in VGPRs)
+// Loader: every thread keeps two (bf16) or three (fp8) 32-key KV tiles in
+// flight in registers (inline-assembly buffer loads with explicit vmcnt
+// waits), then writes each tile into a two-slot LDS ring in the bf16 row
+// layout; fp8-e4m3 rows are converted to bf16 there, once per element
+// (exact), so one compute loop serves both cache formats.  The per-tensor fp8
+// scale is folded into the logit scale and the O epilogue.
+//
+// Work split inside a workgroup: wave w = (row group rg = w / 2, half
+// dh = w % 2).  A row group is up to 32 rows (NRT 16-row MFMA tiles); the
+// wave pair splits the 576 score columns and the 512 value columns in halves:
+//   S^T[key][row] partial = K[:, 288dh:+288] . Q^T   (bf16 MFMA 16x16x32;
+//                  A = K from LDS, B = the wave's Q half held in AGPRs)
 //   the pair sums its two partials through LDS (fp32 a+b == b+a, so both
-//   waves hold bitwise-identical scores, max, P and row sums)
-//   online softmax: a lane holds 4 keys of ONE row (two cross-lane steps for
-//   the row max; per-lane running state)
+//   waves hold bitwise-identical scores, reference, P and row sums)
+//   online softmax: a lane holds 4 keys of ONE row; per-lane running state;
+//                  the base-2 reference moves only for jumps > 60 octaves
 //   O^T[256dh + col][row] += V^T . P^T  (A = V^T fragments read with the
 //                  gfx950 transposing LDS loads, B = P in VGPRs, O in AGPRs)
-// fp8 KV is converted to bf16 in registers (exact) after the LDS read; the
-// per-tensor scale is folded into the logit scale and the O epilogue.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -33,60 +37,60 @@
 namespace mla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-constexpr int kTK = 32;        // keys per KV tile
+constexpr int kTK = 32;        // keys per compute tile
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = 4;
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer: range-checked, zero on OOB
-constexpr float kLazyOctaves = 16.0f;          // softmax reference slack (log2 units)
+// Softmax reference slack in log2 units: P = 2^(x - m_ref) may reach 2^60
+// (bf16 P and fp32 sums have the range); a larger jump moves the reference
+// and rescales O and l.
+constexpr float kLazyOctaves = 60.0f;
+
+// LDS holds every KV tile as bf16 rows: 1152 bytes = 72 chunks of 16 B,
+// physical chunk = logical chunk XOR swz(key) inside aligned groups of 8
+// chunks, so the 16 keys an MFMA operand read touches hit distinct bank slots.
+constexpr int kRowBytes = 2 * kDqk;
+constexpr int kChunks = kRowBytes / 16;        // 72
+constexpr int kTileBytes = kTK * kRowBytes;    // 36864
+constexpr int kSlots = 2;                      // LDS ring of compute tiles
+__device__ __forceinline__ int swz(int key) { return (key & 7) ^ ((key >> 3) & 1); }
+
+// One staged KV tile per thread: 2304 pieces of the tile (16 B of bf16 or 8 B
+// of fp8, i.e. 8 elements each), piece li = tid + 256 m, m = 0..8.
+constexpr int kPieces = kTK * kChunks / kThreads;  // 9
 
 template <bool FP8>
-struct KvCfg;
-
-// bf16 KV: 1152-byte rows = 72 chunks of 16 B.  Physical chunk = logical chunk
-// XOR swz(key) inside aligned groups of 8 chunks, so the 16 keys one MFMA
-// operand read touches land in distinct 16-B bank slots.
-template <>
-struct KvCfg<false> {
-  static constexpr int kRowBytes = 2 * kDqk;
-  static constexpr int kChunks = kRowBytes / 16;
-  static constexpr int kTileBytes = kTK * kRowBytes;  // 36864
-  static constexpr int kStages = 3;
-  static constexpr int kInstr = kTileBytes / 1024;    // 16 B x 64 lanes per load
-  static constexpr int kLoaderWaves = 4;
-  static constexpr int kInstrPerWave = kInstr / kLoaderWaves;  // 9
-  __device__ static int swz(int key) { return (key & 7) ^ ((key >> 3) & 1); }
+struct Stage {
+  using piece_t = typename std::conditional<FP8, u32x2, u32x4>::type;
+  static constexpr int kSets = FP8 ? 3 : 2;   // tiles in flight per thread
+  static constexpr int kGlobalRowBytes = FP8 ? kDqk : 2 * kDqk;
+  piece_t p[kPieces];
 };
-
-// fp8 KV: 576-byte rows = 36 chunks; XOR inside aligned groups of 4 chunks.
-template <>
-struct KvCfg<true> {
-  static constexpr int kRowBytes = kDqk;
-  static constexpr int kChunks = kRowBytes / 16;
-  static constexpr int kTileBytes = kTK * kRowBytes;  // 18432
-  static constexpr int kStages = 4;
-  static constexpr int kInstr = kTileBytes / 1024;    // 18
-  static constexpr int kLoaderWaves = 2;
-  static constexpr int kInstrPerWave = kInstr / kLoaderWaves;  // 9
-  __device__ static int swz(int key) { return (key >> 2) & 3; }
-};
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            (int)kRsrcWord3);
+}
+
+// A pointer every lane agrees on, moved to scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+
+// Workgroup barrier that orders LDS traffic only (global loads stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) with
@@ -113,60 +117,13 @@ __device__ __forceinline__ float wave_sum_across_groups(float v) {
 }
 
 // 8 fp8 codes (two dwords) -> 8 bf16, exact (OCP E4M3FN -> bf16 never rounds).
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 w) {
-  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w[0], 1.0f, false);
-  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w[0], 1.0f, true);
-  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w[1], 1.0f, false);
-  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w[1], 1.0f, true);
-  bf16x8 r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
-}
-
-// O accumulation: an MFMA whose accumulator is constrained to the AGPR file, so
-// the register allocator never copies O between register files.  The compiler
-// cannot see hazards inside inline assembly: the leading s_nop covers a VALU
-// write of the A/B operands just before (the V conversion), and the code
-// around the O uses adds margins for the MFMA-result reads (rescale,
-// epilogue).
-template <bool OA>
-__device__ __forceinline__ void mfma_o(f32x4& acc, const bf16x8& a, const bf16x8& b) {
-  if constexpr (OA)
-    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-  else
-    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-
-// Score MFMA: S^T (VGPRs, read by the softmax) += K . Q^T.  QA places the Q
-// operand in the AGPR file (when it fits next to O) so VGPRs stay free for the
-// softmax; otherwise in VGPRs.  ZERO starts the accumulation from 0.
-template <bool QA, bool ZERO>
-__device__ __forceinline__ void mfma_s(f32x4& acc, const bf16x8& k, const bf16x8& q) {
-  if constexpr (ZERO) {
-    if constexpr (QA)
-      asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "a"(q));
-    else
-      asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "v"(q));
-  } else {
-    if constexpr (QA)
-      asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "a"(q));
-    else
-      asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "v"(q));
-  }
-}
-
-// Multiply one accumulator element in place without leaving the AGPR file, so
-// the loop-carried O accumulators stay AGPR values on every control path.
-__device__ __forceinline__ float scale_agpr(float a, float alpha) {
-  float t;
-  asm volatile(
-      "v_accvgpr_read_b32 %1, %0\n\t"
-      "v_mul_f32 %1, %1, %2\n\t"
-      "v_accvgpr_write_b32 %0, %1"
-      : "+a"(a), "=&v"(t)
-      : "v"(alpha));
-  return a;
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 w) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+  return u32x4{__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+               __builtin_bit_cast(unsigned, c), __builtin_bit_cast(unsigned, d)};
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -175,145 +132,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)xu | ((uint32_t)yu << 16);
 }
 
-// Issue the DMA of one KV tile (keys [k0, k0 + 32) of a unit, clipped to
-// `valid` keys; rows past it read as zero) into an LDS stage.
-template <bool FP8>
-__device__ __forceinline__ void issue_tile(const uint8_t* kv_seq, int k0, int valid, lds_u8* stage,
-                                           const int* src_off, int wave) {
-  using C = KvCfg<FP8>;
-  if (wave >= C::kLoaderWaves) return;
-  const int rows = valid < kTK ? valid : kTK;
-  __amdgpu_buffer_rsrc_t r =
-      make_rsrc(kv_seq + (int64_t)k0 * C::kRowBytes, (uint32_t)(rows * C::kRowBytes));
-#pragma unroll
-  for (int m = 0; m < C::kInstrPerWave; ++m) {
-    const int j = wave + C::kLoaderWaves * m;  // which 1-KB block of the tile
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(stage + j * 1024),
-                                             16, src_off[m], 0, 0, 0);
-  }
-}
-
-// Per-lane LDS byte offsets of the K and V fragments inside a tile.  The XOR
-// swizzle only touches the low bits of the chunk index, so every read is
-// `lane base (chosen by a few low bits of the step) + compile-time offset`:
-//  bf16 K, step ks = 2a + r:  chunk (4 ks + g) ^ sw = 8a + ((4r + g) ^ sw)
-//  bf16 V, tile ct = 4a + c:  chunk (2 ct + h) ^ sw = 8a + ((2c + h) ^ sw)
-//  fp8  K, step ks = 2a + r:  chunk (2 ks + g/2) ^ sw = 4a + ((2r + g/2) ^ sw)
-//  fp8  V, tile ct = 4a + c:  chunk ct ^ sw = 4a + (c ^ sw)
-template <bool FP8>
-struct FragBases {
-  int k[2][2];   // [kt][r]
-  int va[4];     // [c]  (bf16: key 4g + i/4, the key 16 + 4g + i/4 is 16 rows
-                 //       further with the same swizzle;  fp8: the single tr8 row)
-};
-
-template <bool FP8>
-__device__ __forceinline__ FragBases<FP8> frag_bases(int l16, int g) {
-  using C = KvCfg<FP8>;
-  FragBases<FP8> fb;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const int key = 16 * kt + l16;
-    const int sw = C::swz(key);
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      if constexpr (!FP8)
-        fb.k[kt][r] = key * C::kRowBytes + 16 * ((4 * r + g) ^ sw);
-      else
-        fb.k[kt][r] = key * C::kRowBytes + 16 * ((2 * r + (g >> 1)) ^ sw) + 8 * (g & 1);
-    }
-  }
-  const int i = l16;
-  if constexpr (!FP8) {
-    const int ka = 4 * g + (i >> 2);
-    const int h = (i & 3) >> 1;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) fb.va[c] = ka * C::kRowBytes + 16 * ((2 * c + h) ^ C::swz(ka)) + 8 * (i & 1);
-  } else {
-    const int kk = i >> 1;
-    const int key = kk < 4 ? 4 * g + kk : 16 + 4 * g + (kk - 4);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) fb.va[c] = key * C::kRowBytes + 16 * (c ^ C::swz(key)) + 8 * (i & 1);
-  }
-  return fb;
-}
-
-// K fragment (A operand of S^T = K Q^T): key 16 kt + l16, d = 32 ks + 8 g .. +8.
-template <bool FP8, int KT, int KS>
-__device__ __forceinline__ bf16x8 read_k(lds_u8* tile, const FragBases<FP8>& fb) {
-  if constexpr (!FP8) {
-    return *(const bf16x8*)(tile + fb.k[KT][KS & 1] + 128 * (KS >> 1));
-  } else {
-    const i32x2 w = *(const i32x2*)(tile + fb.k[KT][KS & 1] + 64 * (KS >> 1));
-    return fp8x8_to_bf16(w);
-  }
-}
-
-// V^T fragment (A operand of O^T = V^T P^T) for column tile CT: lane (g, i)
-// gets column 16 CT + i; element e is key 4 g + e (e < 4) or 16 + 4 g + e - 4.
-// The gfx950 transposing reads deliver it: in each 16-lane group, lane i
-// points at a 4 (bf16) or 8 (fp8) element piece of one key row, and lane j
-// receives element j of every row of the group's block.
-// The transposing-read builtins do not fold constant offsets, which makes the
-// compiler keep one address register per column tile; these wrappers emit the
-// instruction with its immediate offset.  Their results are not tracked by the
-// compiler's LDS wait counting: use them only through wait_lds<N>(), which
-// waits until at most N of the LDS reads issued after the needed one are
-// outstanding (LDS reads complete in order) and ties the data to that wait.
-template <int OFF>
-__device__ __forceinline__ i32x2 ds_read_tr16_b64(const lds_u8* addr) {
-  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
-  i32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-  return r;
-}
-template <int OFF>
-__device__ __forceinline__ i32x2 ds_read_tr8_b64(const lds_u8* addr) {
-  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
-  i32x2 r;
-  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-  return r;
-}
-template <int N>
-__device__ __forceinline__ void wait_lds(i32x2& a, i32x2& b) {
-  static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N) : "memory");
-}
-
-// Raw (unconverted) V^T fragment for column tile CT: bf16 -> two tr16 pieces,
-// fp8 -> one tr8 piece.  Lane (g, i) gets column 16 CT + i; element e is key
-// 4 g + e (e < 4) or 16 + 4 g + e - 4.  In each 16-lane group of a
-// transposing read, lane i points at a 4 (bf16) or 8 (fp8) element piece of
-// one key row and lane j receives element j of every row of the block.
-template <bool FP8>
-struct VRaw {
-  i32x2 a, b;
-};
-
-template <bool FP8, int CT>
-__device__ __forceinline__ void issue_v(VRaw<FP8>& r, lds_u8* tile, const FragBases<FP8>& fb) {
-  if constexpr (!FP8) {
-    // keys 16 apart share the swizzle, so the second piece is 16 rows further
-    r.a = ds_read_tr16_b64<128 * (CT >> 2)>(tile + fb.va[CT & 3]);
-    r.b = ds_read_tr16_b64<128 * (CT >> 2) + 16 * KvCfg<FP8>::kRowBytes>(tile + fb.va[CT & 3]);
-  } else {
-    r.a = ds_read_tr8_b64<64 * (CT >> 2)>(tile + fb.va[CT & 3]);
-  }
-}
-
-// LDS reads issued per V fragment.
-template <bool FP8>
-constexpr int kVReads = FP8 ? 1 : 2;
-
-template <bool FP8>
-__device__ __forceinline__ bf16x8 finish_v(const VRaw<FP8>& r) {
-  if constexpr (!FP8) {
-    const i32x4 w = {r.a[0], r.a[1], r.b[0], r.b[1]};
-    return __builtin_bit_cast(bf16x8, w);
-  } else {
-    return fp8x8_to_bf16(r.a);
-  }
-}
+// ------------------------------------------------------------------ loader
 
 // Compile-time loop helper.
 template <int N, typename F, int I = 0>
@@ -324,39 +143,209 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// One KV tile of compute for a wave of half DH (templated so every LDS
-// offset is a compile-time immediate on top of a few lane bases).
-template <bool FP8, int NRT, int DH>
+// Issue the global loads of compute tile `t` of the unit (keys [32 t, 32 t + 32),
+// rows past `nkeys` read as zero, tiles past the end read nothing) into one
+// staging set.  The loads are inline
+// assembly so that their completion is waited for explicitly (wait_stage):
+// the compiler's own counting drains every set in flight at the loop head.
+template <bool FP8>
+__device__ __forceinline__ void stage_load(Stage<FP8>& st, const uint8_t* kv_unit, int t, int nkeys,
+                                           int tid) {
+  constexpr int RB = Stage<FP8>::kGlobalRowBytes;
+  constexpr int PB = FP8 ? 8 : 16;  // bytes per piece
+  // 0 past the end: no memory access.  (readfirstlane: the clamp may be selected
+  // as a vector instruction, and the descriptor must live in scalar registers.)
+  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kTK, nkeys - t * kTK)));
+  const __amdgpu_buffer_rsrc_t r =
+      make_rsrc(kv_unit + (int64_t)t * kTK * RB, (uint32_t)(rows * RB));
+  const int off = tid * PB;
+#pragma unroll
+  for (int m = 0; m < kPieces; ++m) {
+    const int soff = kThreads * PB * m;
+    if constexpr (FP8)
+      asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen"
+                   : "=&v"(st.p[m]) : "v"(off), "s"(r), "s"(soff) : "memory");
+    else
+      asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen"
+                   : "=&v"(st.p[m]) : "v"(off), "s"(r), "s"(soff) : "memory");
+  }
+}
+
+// Wait until at most N global loads issued after this set's are outstanding
+// (vector memory loads complete in order); the set's registers are tied to the
+// wait so that no use moves above it.
+template <int N, bool FP8>
+__device__ __forceinline__ void wait_stage(Stage<FP8>& st) {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%9)"
+               : "+v"(st.p[0]), "+v"(st.p[1]), "+v"(st.p[2]), "+v"(st.p[3]), "+v"(st.p[4]),
+                 "+v"(st.p[5]), "+v"(st.p[6]), "+v"(st.p[7]), "+v"(st.p[8])
+               : "n"(N)
+               : "memory");
+}
+
+// Write a staged tile into an LDS slot (bf16 rows, swizzled chunks).
+template <bool FP8>
+__device__ __forceinline__ void stage_store(const Stage<FP8>& st, lds_u8* slot, int tid) {
+#pragma unroll
+  for (int m = 0; m < kPieces; ++m) {
+    const int li = tid + kThreads * m;
+    const int key = li / kChunks, c = li % kChunks;
+    u32x4 v;
+    if constexpr (FP8)
+      v = fp8x8_to_bf16(st.p[m]);
+    else
+      v = st.p[m];
+    *(u32x4*)(slot + key * kRowBytes + 16 * (c ^ swz(key))) = v;
+  }
+}
+
+// ------------------------------------------------------------- fragments
+
+// Per-lane LDS byte offsets of the K and V fragments inside a tile.  The XOR
+// swizzle only touches the low bits of the chunk index, so every read is
+// `lane base (chosen by a few low bits of the step) + compile-time offset`:
+//  K, step ks = 2a + r:  chunk (4 ks + g) ^ sw = 8a + ((4r + g) ^ sw)
+//  V, tile ct = 4a + c:  chunk (2 ct + h) ^ sw = 8a + ((2c + h) ^ sw)
+struct FragBases {
+  int k[2][2];  // [kt][r]
+  int va[4];    // [c]: key 4g + i/4; key 16 + 4g + i/4 is 16 rows further, same swizzle
+};
+
+__device__ __forceinline__ FragBases frag_bases(int l16, int g) {
+  FragBases fb;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = 16 * kt + l16;
+    const int sw = swz(key);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) fb.k[kt][r] = key * kRowBytes + 16 * ((4 * r + g) ^ sw);
+  }
+  const int i = l16;
+  const int ka = 4 * g + (i >> 2);
+  const int h = (i & 3) >> 1;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) fb.va[c] = ka * kRowBytes + 16 * ((2 * c + h) ^ swz(ka)) + 8 * (i & 1);
+  return fb;
+}
+
+// K fragment (A operand of S^T = K Q^T): key 16 KT + l16, d = 32 KS + 8 g .. +8.
+template <int KT, int KS>
+__device__ __forceinline__ bf16x8 read_k(lds_u8* tile, const FragBases& fb) {
+  return *(const bf16x8*)(tile + fb.k[KT][KS & 1] + 128 * (KS >> 1));
+}
+
+// The transposing-read builtin does not fold constant offsets, which makes the
+// compiler keep one address register per column tile; this wrapper emits the
+// instruction with its immediate offset.  Its result is not tracked by the
+// compiler's LDS wait counting: use it only through wait_lds<N>(), which waits
+// until at most N of the LDS reads issued after the needed one are outstanding
+// (LDS reads complete in order) and ties the data to that wait.
+template <int OFF>
+__device__ __forceinline__ i32x2 ds_read_tr16_b64(const lds_u8* addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  i32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void wait_lds(i32x2& a, i32x2& b) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N) : "memory");
+}
+
+// V^T fragment for column tile CT as two tr16 pieces: lane (g, i) gets column
+// 16 CT + i; element e is key 4 g + e (e < 4) or 16 + 4 g + e - 4.  In each
+// 16-lane group of a transposing read, lane i points at a 4-element piece of
+// one key row and lane j receives element j of every row of the block.
+struct VRaw {
+  i32x2 a, b;
+};
+template <int CT>
+__device__ __forceinline__ void issue_v(VRaw& r, lds_u8* tile, const FragBases& fb) {
+  r.a = ds_read_tr16_b64<128 * (CT >> 2)>(tile + fb.va[CT & 3]);
+  r.b = ds_read_tr16_b64<128 * (CT >> 2) + 16 * kRowBytes>(tile + fb.va[CT & 3]);
+}
+__device__ __forceinline__ bf16x8 finish_v(const VRaw& r) {
+  const i32x4 w = {r.a[0], r.a[1], r.b[0], r.b[1]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+
+// MFMAs through inline assembly with explicit register files: the compiler's
+// own choice kept moving accumulators between register files every
+// iteration.  Score MFMA: S^T (VGPRs, read by the softmax) += K . Q^T with Q
+// in AGPRs.  O MFMA: O^T (AGPRs) += V^T . P^T.  Operands come from LDS reads
+// (no VALU producer) except P, whose last VALU write is separated from its
+// first use by an explicit s_nop in the caller; MFMA-result reads by VALU are
+// preceded by s_nop margins.
+template <bool ZERO>
+__device__ __forceinline__ void mfma_s(f32x4& acc, const bf16x8& k, const bf16x8& q) {
+  if constexpr (ZERO)
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "a"(q));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "a"(q));
+}
+__device__ __forceinline__ void mfma_o(f32x4& acc, const bf16x8& v, const bf16x8& p) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
+}
+// O = 0, defined in the AGPR file (an MFMA of zeros), so that no definition of
+// O lives in VGPRs.  The zero operand is written by VALU moves just before:
+// an MFMA must not read a VGPR within 2 wait states of its VALU write, and
+// the compiler does not pad around inline assembly, hence the s_nop.
+__device__ __forceinline__ void zero_o(f32x4& acc) {
+  const bf16x8 z = {};
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=&a"(acc) : "v"(z));
+}
+
+// O *= f (rare: a softmax reference move), with whole-tuple accesses only so
+// that O keeps its AGPR home: the tuple goes to a per-wave LDS area straight
+// from its AGPRs, is scaled in VGPRs, and comes back into the same tuple.
+// Each lane touches only its own 16 bytes.
+__device__ __forceinline__ void scale_o(f32x4& acc, float f, lds_u8* spill) {
+  asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(spill), "a"(acc) : "memory");
+  typedef volatile __attribute__((address_space(3))) f32x4 lds_f32x4;
+  const f32x4 t = *(lds_f32x4*)spill;
+  *(lds_f32x4*)spill = t * f;
+  asm volatile("s_waitcnt lgkmcnt(0)\n\tds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+               : "=a"(acc)
+               : "v"(spill)
+               : "memory");
+}
+
+// ---------------------------------------------------------- main kernel
+
+struct UnitCtx {
+  int lo, nkeys, ntiles, min_lim;
+};
+
+// One compute tile for a wave of half DH.
+template <int NRT, int DH>
 __device__ __forceinline__ void tile_compute(lds_u8* tile, float* xs_mine, const float* xs_peer,
-                                             const FragBases<FP8>& fb,
-                                             const bf16x8 (&qf)[NRT][9], f32x4 (&oacc)[16][NRT],
-                                             float (&m_run)[NRT], float (&l_run)[NRT],
-                                             const int (&lim)[NRT], int k0, bool edge,
-                                             float scale_log2, int g, int lane) {
+                                             const FragBases& fb, const bf16x8 (&qf)[NRT][9],
+                                             f32x4 (&oacc)[16][NRT], float (&m_run)[NRT],
+                                             float (&l_run)[NRT], const int (&lim)[NRT], int k0,
+                                             bool edge, float scale_log2, int g, int lane,
+                                             lds_u8* spill) {
   // ---- partial S^T over this wave's 288 columns, K fragments one step ahead ----
-  // register files: NRT <= 2 keeps O (16 NRT f32x4) in VGPRs and Q in AGPRs;
-  // NRT = 3 needs O in AGPRs and Q in VGPRs
-  constexpr bool kQinAgpr = NRT <= 2;
-  constexpr bool kOinAgpr = !kQinAgpr;
   f32x4 sacc[2][NRT];
   bf16x8 kf[2][2];
-  kf[0][0] = read_k<FP8, 0, 9 * DH>(tile, fb);
-  kf[0][1] = read_k<FP8, 1, 9 * DH>(tile, fb);
+  kf[0][0] = read_k<0, 9 * DH>(tile, fb);
+  kf[0][1] = read_k<1, 9 * DH>(tile, fb);
   static_for<9>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     constexpr int cur = j & 1;
     if constexpr (j + 1 < 9) {
-      kf[cur ^ 1][0] = read_k<FP8, 0, 9 * DH + j + 1>(tile, fb);
-      kf[cur ^ 1][1] = read_k<FP8, 1, 9 * DH + j + 1>(tile, fb);
+      kf[cur ^ 1][0] = read_k<0, 9 * DH + j + 1>(tile, fb);
+      kf[cur ^ 1][1] = read_k<1, 9 * DH + j + 1>(tile, fb);
     }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) mfma_s<kQinAgpr, j == 0>(sacc[kt][rt], kf[cur][kt], qf[rt][j]);
+      for (int rt = 0; rt < NRT; ++rt) mfma_s<j == 0>(sacc[kt][rt], kf[cur][kt], qf[rt][j]);
     __builtin_amdgcn_sched_barrier(0);
   });
-  // the score MFMAs retire before their results are read below
-  asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");
+  asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");  // score MFMAs retire before VALU reads
 
   // ---- exchange partials with the other half of the row group ----
 #pragma unroll
@@ -364,20 +353,20 @@ __device__ __forceinline__ void tile_compute(lds_u8* tile, float* xs_mine, const
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
       *(f32x4*)(xs_mine + ((rt * 2 + kt) * 64 + lane) * 4) = sacc[kt][rt];
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
       sacc[kt][rt] += *(const f32x4*)(xs_peer + ((rt * 2 + kt) * 64 + lane) * 4);
 
-  VRaw<FP8> vr[2];
-  issue_v<FP8, 16 * DH>(vr[0], tile, fb);
+  VRaw vr[2];
+  issue_v<16 * DH>(vr[0], tile, fb);
 
-  // ---- online softmax (base 2) with a lazy per-row reference m_ref:
-  //      P = 2^(x - m_ref); m_ref moves (and O, l are rescaled) only when a
-  //      row's tile max exceeds it by more than kLazyOctaves, so P <= 2^16 and
-  //      the exact result is unchanged ----
+  // ---- online softmax (base 2) with a lazy per-row reference m_run:
+  //      P = 2^(x - m_run); the first tile that shows a row a key sets its
+  //      reference, which moves only when a tile maximum exceeds it by more
+  //      than kLazyOctaves (then O and l are rescaled: rare) ----
   bf16x8 pf[NRT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
@@ -397,204 +386,187 @@ __device__ __forceinline__ void tile_compute(lds_u8* tile, float* xs_mine, const
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
     mx = wave_max_across_groups(mx);
-    const bool need = mx > m_run[rt] + kLazyOctaves;
-    if (__any(need)) {
-      const bool rescale = need && m_run[rt] != -INFINITY;
-      const float m_new = need ? mx : m_run[rt];
-      if (__any(rescale)) {
-        const float alpha = rescale ? __builtin_amdgcn_exp2f(m_run[rt] - m_new) : 1.0f;
-        l_run[rt] *= alpha;
-        // the last MFMA that wrote O retired long ago (a whole QK phase ran
-        // since); the nops are a margin for the accumulator read hazard
-        asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
-        if constexpr (kOinAgpr) {
+    float m = m_run[rt] == -INFINITY ? mx : m_run[rt];  // O and l are still 0 before
+    const bool jump = mx > m + kLazyOctaves;
+    if (__builtin_amdgcn_ballot_w64(jump) != 0) {  // wave-uniform, rare
+      const float f = jump ? __builtin_amdgcn_exp2f(m - mx) : 1.0f;
+      m = jump ? mx : m;
+      l_run[rt] *= f;
 #pragma unroll
-          for (int ct = 0; ct < 16; ++ct)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) oacc[ct][rt][e] = scale_agpr(oacc[ct][rt][e], alpha);
-        } else {
-#pragma unroll
-          for (int ct = 0; ct < 16; ++ct) oacc[ct][rt] *= alpha;
-        }
-        asm volatile("s_nop 7" ::: "memory");
-      }
-      m_run[rt] = m_new;
+      for (int c = 0; c < 16; ++c) scale_o(oacc[c][rt], f, spill);
     }
-    const float mu = m_run[rt] == -INFINITY ? 0.0f : m_run[rt];
+    m_run[rt] = m;
+    const float mu = m == -INFINITY ? 0.0f : m;
     float psum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(x[e] - mu);  // v_exp_f32; tiny results flush to 0
+      // v_exp_f32: x - mu <= kLazyOctaves; results below the fp32 normal
+      // range flush to 0
+      const float pe = __builtin_amdgcn_exp2f(x[e] - mu);
       psum += pe;
       pf[rt][e] = (__bf16)pe;
     }
     l_run[rt] += psum;
   }
   __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 1" ::: "memory");  // last VALU write of P before the first O MFMA
 
   // ---- O^T[256 DH + ...] += V^T P^T, V fragments one column tile ahead ----
   static_for<16>([&](auto cc) {
     constexpr int c = decltype(cc)::value;
     constexpr int cur = c & 1;
     if constexpr (c + 1 < 16) {
-      issue_v<FP8, 16 * DH + c + 1>(vr[cur ^ 1], tile, fb);
-      wait_lds<kVReads<FP8>>(vr[cur].a, vr[cur].b);
+      issue_v<16 * DH + c + 1>(vr[cur ^ 1], tile, fb);
+      wait_lds<2>(vr[cur].a, vr[cur].b);
     } else {
       wait_lds<0>(vr[cur].a, vr[cur].b);
     }
-    const bf16x8 vf = finish_v<FP8>(vr[cur]);
+    const bf16x8 vf = finish_v(vr[cur]);
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-      mfma_o<kOinAgpr>(oacc[c][rt], vf, pf[rt]);
+    for (int rt = 0; rt < NRT; ++rt) mfma_o(oacc[c][rt], vf, pf[rt]);
     __builtin_amdgcn_sched_barrier(0);
   });
 }
 
+// The whole KV chunk of a unit: staged loads run NS tiles ahead of the
+// compute, through a two-slot LDS ring.  The tile loop is unrolled by NS so
+// that staging set k always holds tiles = k mod NS, and every load and wait
+// is unconditional (tiles past the end load nothing): the staged registers
+// then never need a copy while their loads are in flight (a copy would read
+// them before the data arrives).
 template <bool FP8, int NRT, int DH>
-__device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* smem) {
-  using C = KvCfg<FP8>;
-  lds_u8* lds = (lds_u8*)smem;
+__device__ __forceinline__ void unit_pass(const UnitCtx& u, const uint8_t* kv_unit, lds_u8* lds,
+                                          float* xs_mine, const float* xs_peer,
+                                          const FragBases& fb, const bf16x8 (&qf)[NRT][9],
+                                          f32x4 (&oacc)[16][NRT], float (&m_run)[NRT],
+                                          float (&l_run)[NRT], const int (&lim)[NRT],
+                                          bool wave_active, float scale_log2, int tid, int g,
+                                          int lane, lds_u8* spill) {
+  constexpr int NS = Stage<FP8>::kSets;
+  constexpr int kAhead = (NS - 1) * kPieces;  // loads issued after a set's own
+  Stage<FP8> st[NS];
+  if (u.ntiles <= 0) return;
+  // prologue: tiles 0 .. NS-1 in flight, tile 0 stored to slot 0, tile NS issued
+#pragma unroll
+  for (int k = 0; k < NS; ++k) stage_load<FP8>(st[k], kv_unit, k, u.nkeys, tid);
+  wait_stage<kAhead, FP8>(st[0]);
+  stage_store<FP8>(st[0], lds, tid);
+  stage_load<FP8>(st[0], kv_unit, NS, u.nkeys, tid);
 
-  // ---- work unit: XCD-aware order (consecutive units share an XCD's L2) ----
+  for (int base = 0; base < u.ntiles; base += NS) {
+    static_for<NS>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int kn = (k + 1) % NS;  // set of tile it + 1
+      const int it = base + k;
+      lds_barrier();  // tile `it` in its slot; everyone is done with tile it-1
+      wait_stage<kAhead, FP8>(st[kn]);
+      if (it + 1 < u.ntiles) stage_store<FP8>(st[kn], lds + ((it + 1) & 1) * kTileBytes, tid);
+      stage_load<FP8>(st[kn], kv_unit, it + 1 + NS, u.nkeys, tid);
+      if (it < u.ntiles) {
+        lds_u8* tile = lds + (it & 1) * kTileBytes;
+        const int k0 = it * kTK;
+        const bool edge = k0 + kTK - 1 > u.min_lim;
+        if (wave_active) {
+          tile_compute<NRT, DH>(tile, xs_mine, xs_peer, fb, qf, oacc, m_run, l_run, lim, k0,
+                                edge, scale_log2, g, lane, spill);
+        } else {
+          lds_barrier();  // matches the pair exchange barrier of active waves
+        }
+      }
+    });
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads issued past the end
+}
+
+// Everything a unit needs, copied out of the launch arguments (all fields are
+// workgroup-uniform).
+struct UnitSetup {
+  UnitCtx uc;
+  int t, s, R, H, S, rowb0, RU, row0, tail0, hi_eff, part_row0;
+  float scale_log2, o_scale;
+  const uint16_t* q;
+  const uint8_t* kv_unit;  // first KV row of the unit's chunk
+  uint16_t* o;
+  float* lse;
+  float* part_lse;
+  float* part_o;
+};
+
+template <bool FP8>
+__device__ __forceinline__ bool unit_setup(const MainArgs& args, UnitSetup& us) {
   const int p = blockIdx.x;
-  const int u = (p % kNumXcd) * args.units_per_xcd + p / kNumXcd;
-  if (u >= args.num_units) return;
+  const int u = (p % kNumXcd) * args.units_per_xcd + p / kNumXcd;  // XCD-aware order
+  if (u >= args.num_units) return false;
   int b = 0;
   while (b + 1 < args.num_seqs && args.seqs[b + 1].unit0 <= u) ++b;
-  const SeqDesc sd = args.seqs[b];
+  const SeqDesc& sd = args.seqs[b];
   const int v = u - sd.unit0;
   const int per_chunk = sd.T * sd.NRB;  // units sharing one KV chunk are consecutive
-  const int s = v / per_chunk;
-  const int t = (v % per_chunk) / sd.NRB;
+  us.s = v / per_chunk;
+  us.t = (v % per_chunk) / sd.NRB;
   const int rb = v % sd.NRB;
-  const int R = sd.R;
-  const int H = args.H;
-  const int rowb0 = rb * sd.RBS;                 // first tile row of this unit
-  const int RU = min(sd.RBS, R - rowb0);         // rows of this unit
-  const int row0 = sd.q_row0 + t * R + rowb0;    // first Q/O row of this unit
-  const int lo = s * sd.L;
-  const int hi = min(lo + sd.L, sd.n);
-  const int tail0 = sd.n - sd.qlen + t * sd.F;   // tile row r sees keys <= tail0 + r / H
-  const int vis_lo = tail0 + rowb0 / H;          // every unit row sees keys <= vis_lo
-  const int vis_hi = tail0 + (rowb0 + RU - 1) / H;
-  const int hi_eff = min(hi, vis_hi + 1);        // no unit row sees keys >= hi_eff
-  const int nkeys = hi_eff - lo;                 // may be <= 0 (chunk hidden from every row)
-  const int ntiles = nkeys > 0 ? (nkeys + kTK - 1) / kTK : 0;
+  us.R = sd.R;
+  us.H = args.H;
+  us.S = sd.S;
+  us.part_row0 = sd.part_row0;
+  us.scale_log2 = args.scale_log2;
+  us.o_scale = args.o_scale;
+  us.q = args.q;
+  us.o = args.o;
+  us.lse = args.lse;
+  us.part_lse = args.part_lse;
+  us.part_o = args.part_o;
+  us.rowb0 = rb * sd.RBS;                          // first tile row of this unit
+  us.RU = min(sd.RBS, us.R - us.rowb0);            // rows of this unit
+  us.row0 = sd.q_row0 + us.t * us.R + us.rowb0;    // first Q/O row of this unit
+  us.uc.lo = us.s * sd.L;
+  const int hi = min(us.uc.lo + sd.L, sd.n);
+  us.tail0 = sd.n - sd.qlen + us.t * sd.F;         // tile row r sees keys <= tail0 + r / H
+  const int vis_lo = us.tail0 + us.rowb0 / us.H;   // every unit row sees keys <= vis_lo
+  const int vis_hi = us.tail0 + (us.rowb0 + us.RU - 1) / us.H;
+  us.hi_eff = min(hi, vis_hi + 1);                 // no unit row sees keys >= hi_eff
+  us.uc.nkeys = us.hi_eff - us.uc.lo;              // may be <= 0 (chunk hidden from every row)
+  us.uc.ntiles = us.uc.nkeys > 0 ? (us.uc.nkeys + kTK - 1) / kTK : 0;
+  us.uc.min_lim = min(us.hi_eff - 1, vis_lo) - us.uc.lo;  // every row sees keys <= this
+  us.kv_unit = args.kv + ((int64_t)sd.kv_row0 + us.uc.lo) * Stage<FP8>::kGlobalRowBytes;
+  return true;
+}
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int l16 = lane & 15;
-  const int g = lane >> 4;
-  const int rg = wave >> 1;
-  constexpr int dh = DH;
-  const int grow0 = rg * 16 * NRT;  // first unit row of this wave's group
-  const bool wave_active = grow0 < RU;
-
-  // ---- Q fragments (B operand): row grow0 + 16 rt + l16, d = 288 dh + 32 j + 8 g ----
-  bf16x8 qf[NRT][9];
-  {
-    __amdgpu_buffer_rsrc_t qr = make_rsrc(args.q + (int64_t)row0 * kDqk, (uint32_t)(RU * kDqk * 2));
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const int row = grow0 + 16 * rt + l16;
-#pragma unroll
-      for (int j = 0; j < 9; ++j) {
-        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
-            qr, row * (kDqk * 2) + dh * 576 + j * 64 + g * 16, 0, 0);
-        qf[rt][j] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-  }
-
-  // ---- loader offsets: instruction m of this wave fills LDS block j; lane
-  //      `lane` of it writes physical chunk 64 j + lane, which holds the
-  //      logical chunk (row, pc ^ swz(row)) of the tile ----
-  int src_off[C::kInstrPerWave];
-#pragma unroll
-  for (int m = 0; m < C::kInstrPerWave; ++m) {
-    const int j = (wave < C::kLoaderWaves ? wave : 0) + C::kLoaderWaves * m;
-    const int cidx = j * 64 + lane;
-    const int row = cidx / C::kChunks;
-    const int pc = cidx % C::kChunks;
-    src_off[m] = row * C::kRowBytes + ((pc ^ C::swz(row)) * 16);
-  }
-
-  const uint8_t* kv_seq = args.kv + ((int64_t)sd.kv_row0 + lo) * C::kRowBytes;
-
-  // ---- per-lane softmax state (lane owns unit row grow0 + 16 rt + l16) ----
-  float m_run[NRT], l_run[NRT];
-  int lim[NRT];
+// Q fragments (B operand): row grow0 + 16 rt + l16, d = 288 DH + 32 j + 8 g,
+// loaded straight into AGPRs (their only use is as an MFMA operand).
+template <int NRT, int DH>
+__device__ __forceinline__ void load_q(const UnitSetup& us, int grow0, int l16, int g,
+                                       bf16x8 (&qf)[NRT][9]) {
+  const __amdgpu_buffer_rsrc_t qr =
+      make_rsrc(us.q + (int64_t)us.row0 * kDqk, (uint32_t)(us.RU * kDqk * 2));
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.0f;
     const int row = grow0 + 16 * rt + l16;
-    const int rv = row < RU ? row : RU - 1;
-    lim[rt] = min(hi_eff - 1, tail0 + (rowb0 + rv) / H) - lo;  // last visible key, unit-relative
-  }
-  const int min_lim = min(hi_eff - 1, vis_lo) - lo;  // every row sees keys <= this
-
-  f32x4 oacc[16][NRT];
 #pragma unroll
-  for (int c = 0; c < 16; ++c)
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) oacc[c][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // ---- prologue: tiles 0 .. kStages-2 in flight ----
-#pragma unroll
-  for (int st = 0; st < C::kStages - 1; ++st)
-    if (st < ntiles)
-      issue_tile<FP8>(kv_seq, st * kTK, nkeys - st * kTK, lds + st * C::kTileBytes, src_off, wave);
-
-  const FragBases<FP8> fb = frag_bases<FP8>(l16, g);
-  float* xs = (float*)(smem + C::kStages * C::kTileBytes);
-  float* xs_mine = xs + wave * NRT * 2 * 256;
-  const float* xs_peer = xs + (wave ^ 1) * NRT * 2 * 256;
-  const float scale_log2 = args.scale_log2;
-
-  for (int it = 0; it < ntiles; ++it) {
-    // tile `it` landed (this wave's part); later tiles may still be in flight
-    const int ahead = min(C::kStages - 2, ntiles - 1 - it);
-    if constexpr (C::kStages == 3) {
-      if (ahead >= 1) wait_vmcnt<C::kInstrPerWave>(); else wait_vmcnt<0>();
-    } else {
-      if (ahead >= 2) wait_vmcnt<2 * C::kInstrPerWave>();
-      else if (ahead == 1) wait_vmcnt<C::kInstrPerWave>();
-      else wait_vmcnt<0>();
-    }
-    __syncthreads();  // tile `it` visible to all; the stage of tile it-1 is free
-    if (it + C::kStages - 1 < ntiles) {
-      const int nt = it + C::kStages - 1;
-      issue_tile<FP8>(kv_seq, nt * kTK, nkeys - nt * kTK,
-                      lds + (nt % C::kStages) * C::kTileBytes, src_off, wave);
-    }
-    lds_u8* tile = lds + (it % C::kStages) * C::kTileBytes;
-    const int k0 = it * kTK;  // unit-relative first key of the tile
-    const bool edge = k0 + kTK - 1 > min_lim;
-    if (wave_active) {
-      tile_compute<FP8, NRT, DH>(tile, xs_mine, xs_peer, fb, qf, oacc, m_run, l_run, lim, k0, edge,
-                                 scale_log2, g, lane);
-    } else {
-      __syncthreads();  // matches the pair exchange barrier of active waves
+    for (int j = 0; j < 9; ++j) {
+      const int off = row * (kDqk * 2) + DH * 576 + j * 64 + g * 16;
+      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=a"(qf[rt][j]) : "v"(off), "s"(qr));
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
-  if (!wave_active) return;
+template <int NRT, int DH>
+__device__ __forceinline__ void epilogue(const UnitSetup& us, int grow0,
+                                         int l16, int g, f32x4 (&oacc)[16][NRT],
+                                         const float (&m_run)[NRT], const float (&l_run)[NRT]) {
   asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // last O MFMA retired before reads
-
-  // ---- epilogue: this wave's rows x columns [256 dh, 256 dh + 256) ----
   const float ln2 = 0.69314718055994530942f;
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const float lt = wave_sum_across_groups(l_run[rt]);
     const int row = grow0 + 16 * rt + l16;
-    const bool valid = row < RU;
-    if (sd.S == 1) {
-      const float inv = args.o_scale / lt;
-      const int64_t orow = (int64_t)row0 + row;
+    const bool valid = row < us.RU;
+    if (us.S == 1) {
+      const float inv = us.o_scale / lt;
+      const int64_t orow = (int64_t)us.row0 + row;
       if (valid) {
-        uint16_t* op = args.o + orow * kDv + 256 * dh + 4 * g;
+        uint16_t* op = us.o + orow * kDv + 256 * DH + 4 * g;
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
           const f32x4 o4 = oacc[c][rt] * inv;
@@ -603,28 +575,76 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
           pk.y = pack_bf16x2(o4[2], o4[3]);
           *(uint2*)(op + 16 * c) = pk;
         }
-        if (g == 0 && dh == 0) args.lse[orow] = (m_run[rt] + log2f(lt)) * ln2;
+        if (g == 0 && DH == 0) us.lse[orow] = (m_run[rt] + log2f(lt)) * ln2;
       }
     } else {
-      const int64_t prow = (int64_t)sd.part_row0 + ((int64_t)t * sd.S + s) * R + rowb0 + row;
+      const int64_t prow =
+          (int64_t)us.part_row0 + ((int64_t)us.t * us.S + us.s) * us.R + us.rowb0 + row;
       const bool empty = !(lt > 0.0f);
-      const float inv = empty ? 0.0f : args.o_scale / lt;
+      const float inv = empty ? 0.0f : us.o_scale / lt;
       if (valid) {
-        float* pp = args.part_o + prow * kDv + 256 * dh + 4 * g;
+        float* pp = us.part_o + prow * kDv + 256 * DH + 4 * g;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) *(f32x4*)(pp + 16 * c) = oacc[c][rt] * inv;
-        if (g == 0 && dh == 0) args.part_lse[prow] = empty ? -INFINITY : (m_run[rt] + log2f(lt)) * ln2;
+        for (int c = 0; c < 16; ++c) *(f32x4*)(pp + 16 * c) = empty ? f32x4{0.f, 0.f, 0.f, 0.f} : oacc[c][rt] * inv;
+        if (g == 0 && DH == 0)
+          us.part_lse[prow] = empty ? -INFINITY : (m_run[rt] + log2f(lt)) * ln2;
       }
     }
   }
 }
 
+template <bool FP8, int NRT, int DH>
+__device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* smem) {
+  UnitSetup us;
+  if (!unit_setup<FP8>(args, us)) return;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int grow0 = (wave >> 1) * 16 * NRT;  // first unit row of this wave's row group
+  const bool wave_active = grow0 < us.RU;
+  int lim[NRT];  // last key (chunk-relative) the lane's row may see
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int row = grow0 + 16 * rt + l16;
+    const int rv = row < us.RU ? row : us.RU - 1;
+    lim[rt] = min(us.hi_eff - 1, us.tail0 + (us.rowb0 + rv) / us.H) - us.uc.lo;
+  }
+  const FragBases fb = frag_bases(l16, g);
+  lds_u8* lds = (lds_u8*)smem;
+  float* xs = (float*)(smem + kSlots * kTileBytes);
+  float* xs_mine = xs + wave * NRT * 2 * 256;
+  const float* xs_peer = xs + (wave ^ 1) * NRT * 2 * 256;
+  lds_u8* spill = lds + kSlots * kTileBytes + kWaves * NRT * 2 * 1024 + wave * 1024 + lane * 16;
+
+  bf16x8 qf[NRT][9];
+  load_q<NRT, DH>(us, grow0, l16, g, qf);
+  // per-lane softmax state: lane owns unit row grow0 + 16 rt + l16
+  float m_run[NRT], l_run[NRT];
+  f32x4 oacc[16][NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.0f;
+  }
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) zero_o(oacc[c][rt]);
+
+  unit_pass<FP8, NRT, DH>(us.uc, us.kv_unit, lds, xs_mine, xs_peer, fb, qf, oacc, m_run, l_run,
+                          lim, wave_active, us.scale_log2, tid, g, lane, spill);
+  if (wave_active) epilogue<NRT, DH>(us, grow0, l16, g, oacc, m_run, l_run);
+}
+
 template <bool FP8, int NRT>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_main(const MainArgs args) {
-  using C = KvCfg<FP8>;
   constexpr int kXsBytes = kWaves * NRT * 2 * 1024;  // score partials exchanged by wave pairs
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::kStages * C::kTileBytes + kXsBytes];
-  if ((threadIdx.x >> 6) & 1)
+  constexpr int kSpillBytes = kWaves * 1024;         // per-wave area of the O rescale
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSlots * kTileBytes + kXsBytes +
+                                                               kSpillBytes];
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1)
     unit_body<FP8, NRT, 1>(args, smem);
   else
     unit_body<FP8, NRT, 0>(args, smem);

@@ -248,6 +248,35 @@ def planted_inputs(H: int, q_len, kv_len, marker_positions, fp8: bool = False,
     return Inputs(H, q_len, kv_len, q_bits, bf16_bits_from_f32(kvf), False, 1.0)
 
 
+def escalating_inputs(H: int, q_len, kv_len, targets, fp8: bool = False, seed: int = 0) -> Inputs:
+    """Stress input for the running softmax reference.  Query rows are random
+    +-1 sign vectors; keys are N(0,1)*0.1 except planted ones.  targets: list of
+    (sequence b, token i, head h, [p_1, p_2, ...]); the 64 rope columns of key
+    p_j of sequence b are set to 2^(j+4) times the rope signs of query row
+    (i, h) of b (its 512 value columns stay random, so |O| stays small).  With
+    the softmax scale 1/24 that row's score at p_j is 64 * 2^(j+4) / 24 *
+    log2(e), i.e. about 123 * 2^(j-1) octaves: every planted key lifts the row's
+    running maximum by more than 60 octaves."""
+    q_len = np.asarray(q_len, np.int32)
+    kv_len = np.asarray(kv_len, np.int32)
+    sum_q, sum_n = int(q_len.sum()), int(kv_len.sum())
+    rng = np.random.default_rng([seed, 7])
+    qf = np.where(rng.random((sum_q, H, DQK)) < 0.5, -1.0, 1.0).astype(np.float32)
+    kvf = (rng.standard_normal((sum_n, DQK)) * 0.1).astype(np.float32)
+    q_off = np.concatenate([[0], np.cumsum(q_len)]).astype(np.int64)
+    kv_off = np.concatenate([[0], np.cumsum(kv_len)]).astype(np.int64)
+    for (b, i, h, positions) in targets:
+        for j, p in enumerate(positions, start=1):
+            kvf[kv_off[b] + p, DV:] = np.float32(2.0 ** (j + 4)) * qf[q_off[b] + i, h, DV:]
+    q_bits = bf16_bits_from_f32(qf)
+    if fp8:
+        amax = np.float32(np.max(np.abs(kvf)))
+        scale = np.float32(amax / np.float32(E4M3_MAX))
+        return Inputs(H, q_len, kv_len, q_bits, e4m3_codes_from_f32(kvf / scale), True,
+                      float(scale))
+    return Inputs(H, q_len, kv_len, q_bits, bf16_bits_from_f32(kvf), False, 1.0)
+
+
 def identical_key_inputs(H: int, q_len, kv_len, seed: int) -> Inputs:
     """Every KV row of a sequence equals one random row: each query row's
     output is that row's first 512 columns and its LSE is s + ln(visible)."""

@@ -94,6 +94,41 @@ def test_replay_is_bitwise_deterministic(fp8):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_large_logit_jumps_move_the_reference(fp8):
+    """Rows whose running maximum rises by more than 60 octaves after their
+    first tile, several times, in and across split chunks: the kernel moves
+    its softmax reference and rescales O and l in place."""
+    H, q_len, kv_len = 12, [4, 2], [1000, 3000]
+    targets = [(0, 0, 0, [100, 300, 700, 990]),    # four jumps inside one sequence
+               (0, 3, 11, [31, 32, 600]),          # last key of tile 0, first of tile 1
+               (0, 2, 6, [0, 64, 65, 500]),
+               (1, 1, 5, [5, 1500, 2999]),         # 2999: the last key this row sees
+               (1, 0, 0, [2000, 2500])]
+    inp = gen.escalating_inputs(H, q_len, kv_len, targets, fp8=fp8, seed=23)
+    # the input is discriminating: each planted key lifts its row's running
+    # maximum (base-2 logits) by more than 60 octaves
+    import oracle
+    q = gen.f32_from_bf16_bits(inp.q_bits).astype(np.float64)
+    if fp8:
+        table = np.array([oracle.e4m3_to_double(c) for c in range(256)])
+        kvd = table[inp.kv] * inp.kv_scale
+    else:
+        kvd = gen.f32_from_bf16_bits(inp.kv).astype(np.float64)
+    q_off, kv_off = np.concatenate([[0], np.cumsum(q_len)]), np.concatenate([[0], np.cumsum(kv_len)])
+    for (b, i, h, pos) in targets:
+        n = kv_len[b]
+        lim = n - q_len[b] + i
+        x = kvd[kv_off[b]:kv_off[b] + lim + 1] @ q[q_off[b] + i, h] * inp.sm_scale / np.log(2.0)
+        for p in pos:
+            before = x[:p].max() if p > 0 else -np.inf
+            assert x[p] > before + 60.0 or p == 0, (b, i, h, p, x[p], before)
+    ro, rl = gu.oracle_full(inp)
+    for splits in (1, 3, 7):
+        o, lse, plan = gu.run_gpu(inp, force_splits=splits)
+        gu.compare(o, lse, ro, rl, fp8, f"escalating splits={splits} units={plan.num_units}")
+
+
 def test_poisoned_workspace_is_never_read_unwritten():
     inp = gen.random_inputs(12, [8, 2], [3000, 77], False, seed=13)
     ro, rl = gu.oracle_full(inp)

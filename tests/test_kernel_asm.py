@@ -1,0 +1,53 @@
+"""CPU checks of the main kernel's gfx950 assembly (hipcc cross-compiles it
+here with the library's own flags): hazards around the inline-assembly
+MFMAs, no copies of registers that staged loads are filling, and no
+register-file moves inside the KV tile loop."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from mla_token_decode_amd import build as hipbuild
+from tests import asm_scan
+
+HIPCC = hipbuild.HIPCC
+
+
+@pytest.fixture(scope="module")
+def kernels(tmp_path_factory):
+    if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "kernels.s"
+    src = os.path.join(hipbuild.CSRC, "kernels.hip")
+    subprocess.run([HIPCC, *hipbuild.compile_flags(), "-S", "--cuda-device-only", "-o", str(out), src],
+                   check=True)
+    ks = asm_scan.kernels(out.read_text())
+    assert len(ks) == 4, sorted(ks)  # {bf16, fp8} x {16, 32 rows per row group}
+    return ks
+
+
+def test_no_unpadded_mfma_hazards(kernels):
+    for name, lines in kernels.items():
+        assert asm_scan.mfma_hazards(lines) == [], name
+
+
+def test_tile_loop_has_staged_loads_and_never_copies_them(kernels):
+    for name, lines in kernels.items():
+        assert asm_scan.staged_loads_in_loops(lines) > 0, name  # the scan sees the loads
+        assert asm_scan.staged_copies_in_loops(lines) == [], name
+        assert asm_scan.staged_copies_in_prologues(lines) == [], name
+
+
+def test_tile_loop_keeps_register_files(kernels):
+    for name, lines in kernels.items():
+        assert asm_scan.accvgpr_moves_in_loops(lines) == [], name
+
+
+def test_scan_detects_a_planted_hazard():
+    planted = ["\tv_mov_b64_e32 v[6:7], s[4:5]",
+               "\tv_mfma_f32_16x16x32_bf16 a[0:3], v[4:7], v[4:7], 0",
+               "\ts_nop 15",
+               "\tv_accvgpr_read_b32 v8, a1"]
+    found = asm_scan.mfma_hazards(planted)
+    assert len(found) == 2, found
