@@ -19,6 +19,7 @@ the headline workload's rows on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -35,6 +36,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 METRIC = "µs/call + KV-read HBM GB/s (% roofline), H=12 q=8 ctx=1M bf16/fp8"
 HEADLINE = "h12_1m_fp8"
 PAGES_FP8_1M_US = 168.2  # B300, cute-dsl fold_sq, H=12 q=8 ctx~1M fp8 (context, other hardware)
+KERNEL_SOURCE = os.path.join(ROOT, "mla_token_decode_amd", "csrc", "kernels.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mla_decode_main_fp8_h12_q8_1m_hbm_traffic.txt")
 
 
 def log(msg):
@@ -102,6 +105,31 @@ def measure(inp, dev, steps, warmup, flush, **plan_opts):
     }
 
 
+def kernel_source_sha256():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per main-kernel launch of the headline workload from the
+    committed FETCH_SIZE / WRITE_SIZE counter summary (each counter calibrated
+    against the 1 GiB read+write flush kernel of the same run).  None when the
+    summary is missing or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    try:
+        return {"fetch": int(kv["calibrated_fetch_bytes_per_launch"]),
+                "write": int(kv["calibrated_write_bytes_per_launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
 def flops(inp):
     """Algorithmic flops: 2 * rows * visible keys * (576 + 512), causal tail exact."""
     total = 0
@@ -138,6 +166,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--cpu-rows", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -191,8 +221,11 @@ def main():
             del wdev, winp
             torch.cuda.empty_cache()
 
-    log("cpu baseline")
-    cpu = cpu_baseline(inp, args.cpu_rows)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline")
+        cpu = cpu_baseline(inp, args.cpu_rows)
+    traffic = measured_traffic()
 
     main_us = head["main_us_mean"]
     achieved = head["kv_bytes"] / (main_us * 1e-6) / 1e9
@@ -215,10 +248,15 @@ def main():
                    "frac_hbm_roofline": round(head["frac_hbm_peak"], 4),
                    "timing": "cold cache (1 GiB rewrite between steps), HIP events, median"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": (traffic["fetch"] + traffic["write"]) if traffic else None,
+                     "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
+                     "traffic_fetch": traffic["fetch"] if traffic else None,
+                     "traffic_write": traffic["write"] if traffic else None,
                      "kernel": "mla_decode_main (fp8 KV)",
                      "algorithmic_bytes": head["kv_bytes"],
-                     "kernel_us_mean": round(main_us, 2)},
+                     "kernel_us_mean": round(main_us, 2),
+                     "kernel_source_sha256": kernel_source_sha256()},
         "cpu_baseline": cpu,
         "per_workload": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                              for kk, vv in v.items()} for k, v in per.items()},
