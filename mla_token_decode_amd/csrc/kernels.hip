@@ -60,7 +60,6 @@ constexpr float kLazyOctaves = 60.0f;
 constexpr int kRowBytes = 2 * kDqk;
 constexpr int kChunks = kRowBytes / 16;        // 72
 constexpr int kTileBytes = kTK * kRowBytes;    // 36864
-constexpr int kSlots = 2;                      // LDS ring of compute tiles
 __device__ __forceinline__ int swz(int key) { return (key & 7) ^ ((key >> 3) & 1); }
 
 // One staged KV tile per thread: 2304 pieces of the tile (16 B of bf16 or 8 B
@@ -143,32 +142,42 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Issue the global loads of compute tile `t` of the unit (keys [32 t, 32 t + 32),
-// rows past `nkeys` read as zero, tiles past the end read nothing) into one
-// staging set.  The loads are inline
-// assembly so that their completion is waited for explicitly (wait_stage):
-// the compiler's own counting drains every set in flight at the loop head.
+// Descriptor of compute tile `t` of the unit (keys [32 t, 32 t + 32)): rows
+// past `nkeys` read as zero, tiles past the end read nothing.  (readfirstlane:
+// the clamp may be selected as a vector instruction, and the descriptor must
+// live in scalar registers.)
+template <bool FP8>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* kv_unit, int t, int nkeys) {
+  constexpr int RB = Stage<FP8>::kGlobalRowBytes;
+  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kTK, nkeys - t * kTK)));
+  return make_rsrc(kv_unit + (int64_t)t * kTK * RB, (uint32_t)(rows * RB));
+}
+
+// Issue the global load of piece M of compute tile `t` into a staging set.
+// The loads are inline assembly so that their completion is waited for
+// explicitly (wait_stage): the compiler's own counting drains every set in
+// flight at the loop head.
+template <bool FP8, int M>
+__device__ __forceinline__ void stage_load_piece(Stage<FP8>& st, const uint8_t* kv_unit, int t,
+                                                 int nkeys, int tid) {
+  constexpr int PB = FP8 ? 8 : 16;  // bytes per piece
+  const __amdgpu_buffer_rsrc_t r = tile_rsrc<FP8>(kv_unit, t, nkeys);
+  const int off = tid * PB;
+  const int soff = kThreads * PB * M;
+  if constexpr (FP8)
+    asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen"
+                 : "=&v"(st.p[M]) : "v"(off), "s"(r), "s"(soff) : "memory");
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen"
+                 : "=&v"(st.p[M]) : "v"(off), "s"(r), "s"(soff) : "memory");
+}
+
 template <bool FP8>
 __device__ __forceinline__ void stage_load(Stage<FP8>& st, const uint8_t* kv_unit, int t, int nkeys,
                                            int tid) {
-  constexpr int RB = Stage<FP8>::kGlobalRowBytes;
-  constexpr int PB = FP8 ? 8 : 16;  // bytes per piece
-  // 0 past the end: no memory access.  (readfirstlane: the clamp may be selected
-  // as a vector instruction, and the descriptor must live in scalar registers.)
-  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kTK, nkeys - t * kTK)));
-  const __amdgpu_buffer_rsrc_t r =
-      make_rsrc(kv_unit + (int64_t)t * kTK * RB, (uint32_t)(rows * RB));
-  const int off = tid * PB;
-#pragma unroll
-  for (int m = 0; m < kPieces; ++m) {
-    const int soff = kThreads * PB * m;
-    if constexpr (FP8)
-      asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen"
-                   : "=&v"(st.p[m]) : "v"(off), "s"(r), "s"(soff) : "memory");
-    else
-      asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen"
-                   : "=&v"(st.p[m]) : "v"(off), "s"(r), "s"(soff) : "memory");
-  }
+  static_for<kPieces>([&](auto mc) {
+    stage_load_piece<FP8, decltype(mc)::value>(st, kv_unit, t, nkeys, tid);
+  });
 }
 
 // Wait until at most N global loads issued after this set's are outstanding
@@ -184,20 +193,22 @@ __device__ __forceinline__ void wait_stage(Stage<FP8>& st) {
                : "memory");
 }
 
-// Write a staged tile into an LDS slot (bf16 rows, swizzled chunks).
+// Write piece M of a staged tile into an LDS slot (bf16 rows, swizzled chunks).
+template <bool FP8, int M>
+__device__ __forceinline__ void stage_store_piece(const Stage<FP8>& st, lds_u8* slot, int tid) {
+  const int li = tid + kThreads * M;
+  const int key = li / kChunks, c = li % kChunks;
+  u32x4 v;
+  if constexpr (FP8)
+    v = fp8x8_to_bf16(st.p[M]);
+  else
+    v = st.p[M];
+  *(u32x4*)(slot + key * kRowBytes + 16 * (c ^ swz(key))) = v;
+}
+
 template <bool FP8>
 __device__ __forceinline__ void stage_store(const Stage<FP8>& st, lds_u8* slot, int tid) {
-#pragma unroll
-  for (int m = 0; m < kPieces; ++m) {
-    const int li = tid + kThreads * m;
-    const int key = li / kChunks, c = li % kChunks;
-    u32x4 v;
-    if constexpr (FP8)
-      v = fp8x8_to_bf16(st.p[m]);
-    else
-      v = st.p[m];
-    *(u32x4*)(slot + key * kRowBytes + 16 * (c ^ swz(key))) = v;
-  }
+  static_for<kPieces>([&](auto mc) { stage_store_piece<FP8, decltype(mc)::value>(st, slot, tid); });
 }
 
 // ------------------------------------------------------------- fragments
@@ -279,12 +290,23 @@ __device__ __forceinline__ bf16x8 finish_v(const VRaw& r) {
 // (no VALU producer) except P, whose last VALU write is separated from its
 // first use by an explicit s_nop in the caller; MFMA-result reads by VALU are
 // preceded by s_nop margins.
-template <bool ZERO>
+template <bool ZERO, bool QA>
 __device__ __forceinline__ void mfma_s(f32x4& acc, const bf16x8& k, const bf16x8& q) {
-  if constexpr (ZERO)
+  if constexpr (ZERO && QA)
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "a"(q));
-  else
+  else if constexpr (ZERO)
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "v"(q));
+  else if constexpr (QA)
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "a"(q));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "v"(q));
+}
+// Q fragment (rt, j) of a wave lives in AGPRs while they last: O takes
+// 64 NRT AGPRs of the 256, Q fragments fill the rest in order, the remaining
+// ones (only with NRT = 3) live in VGPRs.
+template <int NRT>
+constexpr bool q_in_agpr(int rt, int j) {
+  return 64 * NRT + 4 * (rt * 9 + j + 1) <= 256;
 }
 __device__ __forceinline__ void mfma_o(f32x4& acc, const bf16x8& v, const bf16x8& p) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
@@ -314,169 +336,26 @@ __device__ __forceinline__ void scale_o(f32x4& acc, float f, lds_u8* spill) {
 }
 
 // ---------------------------------------------------------- main kernel
+//
+// Per workgroup: a ring of kRing LDS tile slots and, per tile, one barrier.
+// Iteration t of a unit (tile t's full scores are already in registers):
+//   score phase   S^T MFMAs of tile t+1 (K from its slot), interleaved one by
+//                 one with the softmax of tile t (VALU work runs while the
+//                 MFMAs execute);
+//   PV phase      O MFMAs of tile t (V from its slot), interleaved with the
+//                 exchange write of tile t+1's partial scores and with the
+//                 staging of tile t+2 (LDS store of a staged set, next loads);
+//   barrier       partials and the new slot become visible, tile t's slot
+//                 frees;
+//   exchange read tile t+1's full scores = own partial + peer partial.
+// The last iteration computes the scores of a tile past the end (stale slot
+// contents, discarded).
+
+constexpr int kRing = 3;
 
 struct UnitCtx {
   int lo, nkeys, ntiles, min_lim;
 };
-
-// One compute tile for a wave of half DH.
-template <int NRT, int DH>
-__device__ __forceinline__ void tile_compute(lds_u8* tile, float* xs_mine, const float* xs_peer,
-                                             const FragBases& fb, const bf16x8 (&qf)[NRT][9],
-                                             f32x4 (&oacc)[16][NRT], float (&m_run)[NRT],
-                                             float (&l_run)[NRT], const int (&lim)[NRT], int k0,
-                                             bool edge, float scale_log2, int g, int lane,
-                                             lds_u8* spill) {
-  // ---- partial S^T over this wave's 288 columns, K fragments one step ahead ----
-  f32x4 sacc[2][NRT];
-  bf16x8 kf[2][2];
-  kf[0][0] = read_k<0, 9 * DH>(tile, fb);
-  kf[0][1] = read_k<1, 9 * DH>(tile, fb);
-  static_for<9>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    constexpr int cur = j & 1;
-    if constexpr (j + 1 < 9) {
-      kf[cur ^ 1][0] = read_k<0, 9 * DH + j + 1>(tile, fb);
-      kf[cur ^ 1][1] = read_k<1, 9 * DH + j + 1>(tile, fb);
-    }
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) mfma_s<j == 0>(sacc[kt][rt], kf[cur][kt], qf[rt][j]);
-    __builtin_amdgcn_sched_barrier(0);
-  });
-  asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");  // score MFMAs retire before VALU reads
-
-  // ---- exchange partials with the other half of the row group ----
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-      *(f32x4*)(xs_mine + ((rt * 2 + kt) * 64 + lane) * 4) = sacc[kt][rt];
-  lds_barrier();
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-      sacc[kt][rt] += *(const f32x4*)(xs_peer + ((rt * 2 + kt) * 64 + lane) * 4);
-
-  VRaw vr[2];
-  issue_v<16 * DH>(vr[0], tile, fb);
-
-  // ---- online softmax (base 2) with a lazy per-row reference m_run:
-  //      P = 2^(x - m_run); the first tile that shows a row a key sets its
-  //      reference, which moves only when a tile maximum exceeds it by more
-  //      than kLazyOctaves (then O and l are rescaled: rare) ----
-  bf16x8 pf[NRT];
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    float x[8];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float val = sacc[kt][rt][i] * scale_log2;
-        if (edge) {
-          const int key = k0 + 16 * kt + 4 * g + i;
-          val = key <= lim[rt] ? val : -INFINITY;
-        }
-        x[kt * 4 + i] = val;
-      }
-    float mx = x[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-    mx = wave_max_across_groups(mx);
-    float m = m_run[rt] == -INFINITY ? mx : m_run[rt];  // O and l are still 0 before
-    const bool jump = mx > m + kLazyOctaves;
-    if (__builtin_amdgcn_ballot_w64(jump) != 0) {  // wave-uniform, rare
-      const float f = jump ? __builtin_amdgcn_exp2f(m - mx) : 1.0f;
-      m = jump ? mx : m;
-      l_run[rt] *= f;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) scale_o(oacc[c][rt], f, spill);
-    }
-    m_run[rt] = m;
-    const float mu = m == -INFINITY ? 0.0f : m;
-    float psum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // v_exp_f32: x - mu <= kLazyOctaves; results below the fp32 normal
-      // range flush to 0
-      const float pe = __builtin_amdgcn_exp2f(x[e] - mu);
-      psum += pe;
-      pf[rt][e] = (__bf16)pe;
-    }
-    l_run[rt] += psum;
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 1" ::: "memory");  // last VALU write of P before the first O MFMA
-
-  // ---- O^T[256 DH + ...] += V^T P^T, V fragments one column tile ahead ----
-  static_for<16>([&](auto cc) {
-    constexpr int c = decltype(cc)::value;
-    constexpr int cur = c & 1;
-    if constexpr (c + 1 < 16) {
-      issue_v<16 * DH + c + 1>(vr[cur ^ 1], tile, fb);
-      wait_lds<2>(vr[cur].a, vr[cur].b);
-    } else {
-      wait_lds<0>(vr[cur].a, vr[cur].b);
-    }
-    const bf16x8 vf = finish_v(vr[cur]);
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) mfma_o(oacc[c][rt], vf, pf[rt]);
-    __builtin_amdgcn_sched_barrier(0);
-  });
-}
-
-// The whole KV chunk of a unit: staged loads run NS tiles ahead of the
-// compute, through a two-slot LDS ring.  The tile loop is unrolled by NS so
-// that staging set k always holds tiles = k mod NS, and every load and wait
-// is unconditional (tiles past the end load nothing): the staged registers
-// then never need a copy while their loads are in flight (a copy would read
-// them before the data arrives).
-template <bool FP8, int NRT, int DH>
-__device__ __forceinline__ void unit_pass(const UnitCtx& u, const uint8_t* kv_unit, lds_u8* lds,
-                                          float* xs_mine, const float* xs_peer,
-                                          const FragBases& fb, const bf16x8 (&qf)[NRT][9],
-                                          f32x4 (&oacc)[16][NRT], float (&m_run)[NRT],
-                                          float (&l_run)[NRT], const int (&lim)[NRT],
-                                          bool wave_active, float scale_log2, int tid, int g,
-                                          int lane, lds_u8* spill) {
-  constexpr int NS = Stage<FP8>::kSets;
-  constexpr int kAhead = (NS - 1) * kPieces;  // loads issued after a set's own
-  Stage<FP8> st[NS];
-  if (u.ntiles <= 0) return;
-  // prologue: tiles 0 .. NS-1 in flight, tile 0 stored to slot 0, tile NS issued
-#pragma unroll
-  for (int k = 0; k < NS; ++k) stage_load<FP8>(st[k], kv_unit, k, u.nkeys, tid);
-  wait_stage<kAhead, FP8>(st[0]);
-  stage_store<FP8>(st[0], lds, tid);
-  stage_load<FP8>(st[0], kv_unit, NS, u.nkeys, tid);
-
-  for (int base = 0; base < u.ntiles; base += NS) {
-    static_for<NS>([&](auto kc) {
-      constexpr int k = decltype(kc)::value;
-      constexpr int kn = (k + 1) % NS;  // set of tile it + 1
-      const int it = base + k;
-      lds_barrier();  // tile `it` in its slot; everyone is done with tile it-1
-      wait_stage<kAhead, FP8>(st[kn]);
-      if (it + 1 < u.ntiles) stage_store<FP8>(st[kn], lds + ((it + 1) & 1) * kTileBytes, tid);
-      stage_load<FP8>(st[kn], kv_unit, it + 1 + NS, u.nkeys, tid);
-      if (it < u.ntiles) {
-        lds_u8* tile = lds + (it & 1) * kTileBytes;
-        const int k0 = it * kTK;
-        const bool edge = k0 + kTK - 1 > u.min_lim;
-        if (wave_active) {
-          tile_compute<NRT, DH>(tile, xs_mine, xs_peer, fb, qf, oacc, m_run, l_run, lim, k0,
-                                edge, scale_log2, g, lane, spill);
-        } else {
-          lds_barrier();  // matches the pair exchange barrier of active waves
-        }
-      }
-    });
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads issued past the end
-}
 
 // Everything a unit needs, copied out of the launch arguments (all fields are
 // workgroup-uniform).
@@ -532,22 +411,31 @@ __device__ __forceinline__ bool unit_setup(const MainArgs& args, UnitSetup& us) 
   return true;
 }
 
-// Q fragments (B operand): row grow0 + 16 rt + l16, d = 288 DH + 32 j + 8 g,
-// loaded straight into AGPRs (their only use is as an MFMA operand).
+// One Q fragment (MFMA B operand) straight from memory into its register file.
+template <bool QA>
+__device__ __forceinline__ void load_q_frag(bf16x8& dst, int off, __amdgpu_buffer_rsrc_t r) {
+  if constexpr (QA)
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=a"(dst) : "v"(off), "s"(r));
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(dst) : "v"(off), "s"(r));
+}
+
+// Q fragments: row grow0 + 16 rt + l16, d = 288 DH + 32 j + 8 g.  Rows past the
+// unit read as zero (range-checked descriptor).
 template <int NRT, int DH>
 __device__ __forceinline__ void load_q(const UnitSetup& us, int grow0, int l16, int g,
                                        bf16x8 (&qf)[NRT][9]) {
   const __amdgpu_buffer_rsrc_t qr =
       make_rsrc(us.q + (int64_t)us.row0 * kDqk, (uint32_t)(us.RU * kDqk * 2));
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
+  static_for<NRT>([&](auto rc) {
+    constexpr int rt = decltype(rc)::value;
     const int row = grow0 + 16 * rt + l16;
-#pragma unroll
-    for (int j = 0; j < 9; ++j) {
-      const int off = row * (kDqk * 2) + DH * 576 + j * 64 + g * 16;
-      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=a"(qf[rt][j]) : "v"(off), "s"(qr));
-    }
-  }
+    static_for<9>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      load_q_frag<q_in_agpr<NRT>(rt, j)>(qf[rt][j], row * (kDqk * 2) + DH * 576 + j * 64 + g * 16,
+                                          qr);
+    });
+  });
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -585,12 +473,260 @@ __device__ __forceinline__ void epilogue(const UnitSetup& us, int grow0,
       if (valid) {
         float* pp = us.part_o + prow * kDv + 256 * DH + 4 * g;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) *(f32x4*)(pp + 16 * c) = empty ? f32x4{0.f, 0.f, 0.f, 0.f} : oacc[c][rt] * inv;
+        for (int c = 0; c < 16; ++c)
+          *(f32x4*)(pp + 16 * c) = empty ? f32x4{0.f, 0.f, 0.f, 0.f} : oacc[c][rt] * inv;
         if (g == 0 && DH == 0)
           us.part_lse[prow] = empty ? -INFINITY : (m_run[rt] + log2f(lt)) * ln2;
       }
     }
   }
+}
+
+// Call f(i) for the slices i of a phase that go after MFMA number `pos` when
+// `nslices` slices are spread over `nmfma` MFMAs.
+template <int NSLICES, int NMFMA, int POS, typename F>
+__device__ __forceinline__ void slices_at(F&& f) {
+  static_for<NSLICES>([&](auto sc) {
+    constexpr int s = decltype(sc)::value;
+    constexpr int at = (s * NMFMA) / NSLICES;
+    if constexpr (at == POS) f(sc);
+  });
+}
+
+// Score phase: S^T partial (this wave's 288 columns) of one tile; K fragments
+// one step ahead; slice(i) of the interleaved work runs after MFMA i.
+template <int NRT, int DH, typename W>
+__device__ __forceinline__ void score_phase(lds_u8* tile, const FragBases& fb,
+                                            const bf16x8 (&qf)[NRT][9], f32x4 (&sacc)[2][NRT],
+                                            W&& slice) {
+  bf16x8 kf[2][2];
+  kf[0][0] = read_k<0, 9 * DH>(tile, fb);
+  kf[0][1] = read_k<1, 9 * DH>(tile, fb);
+  static_for<9>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int cur = j & 1;
+    if constexpr (j + 1 < 9) {
+      kf[cur ^ 1][0] = read_k<0, 9 * DH + j + 1>(tile, fb);
+      kf[cur ^ 1][1] = read_k<1, 9 * DH + j + 1>(tile, fb);
+    }
+    static_for<2 * NRT>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int kt = i / NRT, rt = i % NRT;
+      mfma_s<j == 0, q_in_agpr<NRT>(rt, j)>(sacc[kt][rt], kf[cur][kt], qf[rt][j]);
+      slice(std::integral_constant<int, j * 2 * NRT + i>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  });
+}
+
+// PV phase: O^T[256 DH + ...] += V^T P^T of one tile; V fragments one column
+// tile ahead (vr[0] issued by the caller); slice(i) runs after MFMA i.
+template <int NRT, int DH, typename W>
+__device__ __forceinline__ void pv_phase(lds_u8* tile, const FragBases& fb,
+                                         const bf16x8 (&pf)[NRT], f32x4 (&oacc)[16][NRT],
+                                         VRaw (&vr)[2], W&& slice) {
+  asm volatile("s_nop 1" ::: "memory");  // last VALU write of P before the first O MFMA
+  static_for<16>([&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    constexpr int cur = c & 1;
+    if constexpr (c + 1 < 16) {
+      issue_v<16 * DH + c + 1>(vr[cur ^ 1], tile, fb);
+      wait_lds<2>(vr[cur].a, vr[cur].b);
+    } else {
+      wait_lds<0>(vr[cur].a, vr[cur].b);
+    }
+    const bf16x8 vf = finish_v(vr[cur]);
+    static_for<NRT>([&](auto rc) {
+      constexpr int rt = decltype(rc)::value;
+      mfma_o(oacc[c][rt], vf, pf[rt]);
+      slice(std::integral_constant<int, c * NRT + rt>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  });
+}
+
+// Online softmax of one tile (base 2) with a lazy per-row reference m_run:
+// P = 2^(x - m_run); the first tile that shows a row a key sets its
+// reference, which moves only when a tile maximum exceeds it by more than
+// kLazyOctaves (then O and l are rescaled: rare).  Split into 8 slices per
+// 16-row tile so that it can run between MFMAs of the other phase.
+template <int NRT>
+struct SoftTile {
+  float x[NRT][8];
+  float mx[NRT], mu[NRT], psum[NRT];
+};
+
+template <int NRT, int S>
+__device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, const f32x4 (&sfull)[2][NRT],
+                                              bf16x8 (&pf)[NRT], float (&m_run)[NRT],
+                                              float (&l_run)[NRT], f32x4 (&oacc)[16][NRT],
+                                              const int (&lim)[NRT], int k0, bool edge,
+                                              float scale_log2, int g, lds_u8* spill) {
+  constexpr int rt = S / 8, ph = S % 8;
+  if constexpr (ph <= 1) {  // scaled, masked logits of 4 keys
+    constexpr int kt = ph;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float val = sfull[kt][rt][i] * scale_log2;
+      if (edge) {
+        const int key = k0 + 16 * kt + 4 * g + i;
+        val = key <= lim[rt] ? val : -INFINITY;
+      }
+      w.x[rt][4 * kt + i] = val;
+    }
+  } else if constexpr (ph == 2) {
+    float mx = w.x[rt][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, w.x[rt][e]);
+    w.mx[rt] = mx;
+  } else if constexpr (ph == 3) {
+    w.mx[rt] = wave_max_across_groups(w.mx[rt]);
+  } else if constexpr (ph == 4) {
+    const float mx = w.mx[rt];
+    float m = m_run[rt] == -INFINITY ? mx : m_run[rt];  // O and l are still 0 before
+    const bool jump = mx > m + kLazyOctaves;
+    if (__builtin_amdgcn_ballot_w64(jump) != 0) {  // wave-uniform, rare
+      asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // O MFMAs retired
+      const float f = jump ? __builtin_amdgcn_exp2f(m - mx) : 1.0f;
+      m = jump ? mx : m;
+      l_run[rt] *= f;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) scale_o(oacc[c][rt], f, spill);
+    }
+    m_run[rt] = m;
+    w.mu[rt] = m == -INFINITY ? 0.0f : m;
+  } else if constexpr (ph <= 6) {  // P of 4 keys: x - mu <= kLazyOctaves
+    constexpr int kt = ph - 5;
+    float psum = kt == 0 ? 0.0f : w.psum[rt];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // v_exp_f32: results below the fp32 normal range flush to 0
+      const float pe = __builtin_amdgcn_exp2f(w.x[rt][4 * kt + i] - w.mu[rt]);
+      psum += pe;
+      pf[rt][4 * kt + i] = (__bf16)pe;
+    }
+    w.psum[rt] = psum;
+  } else {
+    l_run[rt] += w.psum[rt];
+  }
+}
+
+// The whole KV chunk of a unit, software-pipelined as described above.  The
+// tile loop is unrolled by the number of staging sets so that set k always
+// holds tiles = k mod NS; every global load and wait is unconditional (tiles
+// past the end load nothing), so the staged registers never need a copy while
+// their loads are in flight (the compiler does not know that an
+// inline-assembly load completes later).
+template <bool FP8, int NRT, int DH>
+__device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, float* xs,
+                                              int wave, const FragBases& fb,
+                                              const bf16x8 (&qf)[NRT][9], f32x4 (&oacc)[16][NRT],
+                                              float (&m_run)[NRT], float (&l_run)[NRT],
+                                              const int (&lim)[NRT], int tid, int g, int lane) {
+  constexpr int NS = Stage<FP8>::kSets;
+  constexpr int kAhead = (NS - 1) * kPieces;  // loads issued after a set's own
+  constexpr int kXsWave = NRT * 2 * 256;      // floats of one wave's partial scores
+  const UnitCtx u = us.uc;
+  const uint8_t* kv = us.kv_unit;
+  if (u.ntiles <= 0) return;
+
+  Stage<FP8> st[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) stage_load<FP8>(st[k], kv, k, u.nkeys, tid);
+  wait_stage<kAhead, FP8>(st[0]);
+  stage_store<FP8>(st[0], lds, tid);
+  stage_load<FP8>(st[0], kv, NS, u.nkeys, tid);
+  wait_stage<kAhead, FP8>(st[1]);
+  stage_store<FP8>(st[1], lds + kTileBytes, tid);
+  stage_load<FP8>(st[1], kv, NS + 1, u.nkeys, tid);
+  lds_barrier();
+
+  // full scores of tile 0
+  f32x4 sacc[2][NRT], sfull[2][NRT];
+  score_phase<NRT, DH>(lds, fb, qf, sacc, [](auto) {});
+  asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");  // score MFMAs retire before the reads
+  {
+    float* mine = xs + wave * kXsWave;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        *(f32x4*)(mine + ((rt * 2 + kt) * 64 + lane) * 4) = sacc[kt][rt];
+  }
+  lds_barrier();
+  {
+    const float* peer = xs + (wave ^ 1) * kXsWave;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        sfull[kt][rt] = sacc[kt][rt] + *(const f32x4*)(peer + ((rt * 2 + kt) * 64 + lane) * 4);
+  }
+
+  VRaw vr[2];
+  bf16x8 pf[NRT];
+  SoftTile<NRT> sw;
+  for (int base = 0; base < u.ntiles; base += NS) {
+    static_for<NS>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int ks = (k + 2) % NS;  // staging set of tile t + 2
+      const int t = base + k;
+      if (t < u.ntiles) {
+        const int par = (t + 1) & 1;  // exchange buffer of tile t + 1
+        float* mine = xs + (par * kWaves + wave) * kXsWave;
+        const float* peer = xs + (par * kWaves + (wave ^ 1)) * kXsWave;
+        lds_u8* spill = (lds_u8*)mine + lane * 16;  // free until the exchange write below
+        lds_u8* slot_t = lds + (t % kRing) * kTileBytes;
+        lds_u8* slot_n = lds + ((t + 1) % kRing) * kTileBytes;
+        lds_u8* slot_s = lds + ((t + 2) % kRing) * kTileBytes;
+        const int k0 = t * kTK;
+        const bool edge = k0 + kTK - 1 > u.min_lim;
+        issue_v<16 * DH>(vr[0], slot_t, fb);
+
+        // scores of tile t + 1  ||  softmax of tile t
+        constexpr int kScoreMfma = 18 * NRT, kSoftSlices = 8 * NRT;
+        score_phase<NRT, DH>(slot_n, fb, qf, sacc, [&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          slices_at<kSoftSlices, kScoreMfma, i>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            softmax_slice<NRT, s>(sw, sfull, pf, m_run, l_run, oacc, lim, k0, edge, us.scale_log2,
+                                  g, spill);
+          });
+        });
+
+        // O of tile t  ||  exchange write of tile t+1, staging of tile t + 2
+        constexpr int kPvMfma = 16 * NRT;
+        constexpr int kStageSlices = NRT + 1 + 2 * kPieces;
+        pv_phase<NRT, DH>(slot_t, fb, pf, oacc, vr, [&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          slices_at<kStageSlices, kPvMfma, i>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            if constexpr (s < NRT) {  // partial scores of tile t + 1
+              if constexpr (s == 0) asm volatile("s_nop 15" ::: "memory");
+#pragma unroll
+              for (int kt = 0; kt < 2; ++kt)
+                *(f32x4*)(mine + ((s * 2 + kt) * 64 + lane) * 4) = sacc[kt][s];
+            } else if constexpr (s == NRT) {
+              wait_stage<kAhead, FP8>(st[ks]);
+            } else if constexpr (s < NRT + 1 + kPieces) {
+              stage_store_piece<FP8, s - NRT - 1>(st[ks], slot_s, tid);
+            } else {
+              stage_load_piece<FP8, s - NRT - 1 - kPieces>(st[ks], kv, t + 2 + NS, u.nkeys, tid);
+            }
+          });
+        });
+
+        lds_barrier();
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+            sfull[kt][rt] =
+                sacc[kt][rt] + *(const f32x4*)(peer + ((rt * 2 + kt) * 64 + lane) * 4);
+      }
+    });
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads issued past the end
 }
 
 template <bool FP8, int NRT, int DH>
@@ -603,7 +739,6 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
   const int l16 = lane & 15;
   const int g = lane >> 4;
   const int grow0 = (wave >> 1) * 16 * NRT;  // first unit row of this wave's row group
-  const bool wave_active = grow0 < us.RU;
   int lim[NRT];  // last key (chunk-relative) the lane's row may see
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
@@ -613,11 +748,10 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
   }
   const FragBases fb = frag_bases(l16, g);
   lds_u8* lds = (lds_u8*)smem;
-  float* xs = (float*)(smem + kSlots * kTileBytes);
-  float* xs_mine = xs + wave * NRT * 2 * 256;
-  const float* xs_peer = xs + (wave ^ 1) * NRT * 2 * 256;
-  lds_u8* spill = lds + kSlots * kTileBytes + kWaves * NRT * 2 * 1024 + wave * 1024 + lane * 16;
+  float* xs = (float*)(smem + kRing * kTileBytes);
 
+  // Rows past the unit hold zero Q and run the same instruction stream (their
+  // outputs are never written): no branch splits the staged registers.
   bf16x8 qf[NRT][9];
   load_q<NRT, DH>(us, grow0, l16, g, qf);
   // per-lane softmax state: lane owns unit row grow0 + 16 rt + l16
@@ -633,17 +767,18 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) zero_o(oacc[c][rt]);
 
-  unit_pass<FP8, NRT, DH>(us.uc, us.kv_unit, lds, xs_mine, xs_peer, fb, qf, oacc, m_run, l_run,
-                          lim, wave_active, us.scale_log2, tid, g, lane, spill);
-  if (wave_active) epilogue<NRT, DH>(us, grow0, l16, g, oacc, m_run, l_run);
+  unit_pipeline<FP8, NRT, DH>(us, lds, xs, wave, fb, qf, oacc, m_run, l_run, lim, tid, g, lane);
+  epilogue<NRT, DH>(us, grow0, l16, g, oacc, m_run, l_run);
+}
+
+template <int NRT>
+constexpr int main_lds_bytes() {
+  return kRing * kTileBytes + 2 * kWaves * NRT * 2 * 1024;  // tile ring + 2 exchange buffers
 }
 
 template <bool FP8, int NRT>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_main(const MainArgs args) {
-  constexpr int kXsBytes = kWaves * NRT * 2 * 1024;  // score partials exchanged by wave pairs
-  constexpr int kSpillBytes = kWaves * 1024;         // per-wave area of the O rescale
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSlots * kTileBytes + kXsBytes +
-                                                               kSpillBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[main_lds_bytes<NRT>()];
   if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1)
     unit_body<FP8, NRT, 1>(args, smem);
   else
@@ -724,14 +859,16 @@ template <bool FP8>
 static void launch_main_t(const MainArgs& a, int nrt, int grid, hipStream_t stream) {
   if (nrt <= 1)
     hipLaunchKernelGGL((mla_decode_main<FP8, 1>), dim3(grid), dim3(kThreads), 0, stream, a);
-  else
+  else if (nrt == 2)
     hipLaunchKernelGGL((mla_decode_main<FP8, 2>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((mla_decode_main<FP8, 3>), dim3(grid), dim3(kThreads), 0, stream, a);
 }
 
 hipError_t launch_main(const MainArgs& a, bool fp8, int nrt, hipStream_t stream) {
   const int grid = ((a.num_units + kNumXcd - 1) / kNumXcd) * kNumXcd;
   if (grid == 0) return hipSuccess;
-  if (nrt < 1 || nrt > 2) return hipErrorInvalidValue;
+  if (nrt < 1 || nrt > 3) return hipErrorInvalidValue;
   if (fp8)
     launch_main_t<true>(a, nrt, grid, stream);
   else

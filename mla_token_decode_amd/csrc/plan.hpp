@@ -15,7 +15,7 @@ constexpr int kDv = MLA_DV;              // 512
 constexpr int kMaxRows = MLA_MAX_TILE_ROWS;  // 128
 constexpr int kGranule = MLA_KV_GRANULE;     // 64 keys
 constexpr int kMaxSeqPerLaunch = 60;     // sequence descriptors travel in kernel arguments
-constexpr int kMaxUnitRows = 64;         // rows one workgroup processes (2 groups x 2 MFMA tiles)
+constexpr int kMaxUnitRows = 96;         // rows one workgroup processes (2 groups x 3 MFMA tiles)
 constexpr int kNumXcd = 8;               // MI355X: 8 XCDs, workgroups dealt round-robin
 
 // One sequence as the kernels see it.  All counts fit int32 for any cache that

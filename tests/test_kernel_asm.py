@@ -23,7 +23,7 @@ def kernels(tmp_path_factory):
     subprocess.run([HIPCC, *hipbuild.compile_flags(), "-S", "--cuda-device-only", "-o", str(out), src],
                    check=True)
     ks = asm_scan.kernels(out.read_text())
-    assert len(ks) == 4, sorted(ks)  # {bf16, fp8} x {16, 32 rows per row group}
+    assert len(ks) == 6, sorted(ks)  # {bf16, fp8} x {16, 32, 48 rows per row group}
     return ks
 
 
