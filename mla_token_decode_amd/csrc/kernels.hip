@@ -97,13 +97,27 @@ __device__ __forceinline__ void lds_barrier() {
 // rows of one operand with the even rows of the other, permlane32_swap the
 // upper half with the lower half; feeding the same value to both operands and
 // combining the two results gives every lane the value of its partner.
+// Maxima of values that are never NaN, as plain instructions: fmaxf would
+// first quiet possible signalling NaNs of operands the compiler cannot see the
+// origin of (inline-assembly results), one extra instruction per operand.
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ float wave_max_across_groups(float v) {
   const unsigned u = __builtin_bit_cast(unsigned, v);
   auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = fmaxf(__builtin_bit_cast(float, (unsigned)r16[0]), __builtin_bit_cast(float, (unsigned)r16[1]));
+  v = max2(__builtin_bit_cast(float, (unsigned)r16[0]), __builtin_bit_cast(float, (unsigned)r16[1]));
   const unsigned w = __builtin_bit_cast(unsigned, v);
   auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)r32[0]), __builtin_bit_cast(float, (unsigned)r32[1]));
+  return max2(__builtin_bit_cast(float, (unsigned)r32[0]), __builtin_bit_cast(float, (unsigned)r32[1]));
 }
 
 __device__ __forceinline__ float wave_sum_across_groups(float v) {
@@ -493,21 +507,32 @@ __device__ __forceinline__ void slices_at(F&& f) {
   });
 }
 
+// LDS read-ahead: K steps and V column tiles in flight ahead of the MFMA that
+// needs them, as deep as the register budget of each row-tile count allows
+// (one step is 2 NRT MFMAs, one column tile NRT MFMAs).
+template <int NRT, bool FP8>
+constexpr int k_ahead() { return NRT == 1 ? 4 : NRT == 2 ? 2 : 1; }
+template <int NRT, bool FP8>
+constexpr int v_ahead() { return NRT == 1 ? 7 : NRT == 2 ? 4 : (FP8 ? 2 : 1); }
+
 // Score phase: S^T partial (this wave's 288 columns) of one tile; K fragments
-// one step ahead; slice(i) of the interleaved work runs after MFMA i.
-template <int NRT, int DH, typename W>
+// DK steps ahead; slice(i) of the interleaved work runs after MFMA i.
+template <int NRT, int DH, int DK, typename W>
 __device__ __forceinline__ void score_phase(lds_u8* tile, const FragBases& fb,
                                             const bf16x8 (&qf)[NRT][9], f32x4 (&sacc)[2][NRT],
                                             W&& slice) {
-  bf16x8 kf[2][2];
-  kf[0][0] = read_k<0, 9 * DH>(tile, fb);
-  kf[0][1] = read_k<1, 9 * DH>(tile, fb);
+  bf16x8 kf[DK + 1][2];
+  static_for<DK>([&](auto sc) {
+    constexpr int j = decltype(sc)::value;
+    kf[j][0] = read_k<0, 9 * DH + j>(tile, fb);
+    kf[j][1] = read_k<1, 9 * DH + j>(tile, fb);
+  });
   static_for<9>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    constexpr int cur = j & 1;
-    if constexpr (j + 1 < 9) {
-      kf[cur ^ 1][0] = read_k<0, 9 * DH + j + 1>(tile, fb);
-      kf[cur ^ 1][1] = read_k<1, 9 * DH + j + 1>(tile, fb);
+    constexpr int cur = j % (DK + 1);
+    if constexpr (j + DK < 9) {
+      kf[(j + DK) % (DK + 1)][0] = read_k<0, 9 * DH + j + DK>(tile, fb);
+      kf[(j + DK) % (DK + 1)][1] = read_k<1, 9 * DH + j + DK>(tile, fb);
     }
     static_for<2 * NRT>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
@@ -519,21 +544,31 @@ __device__ __forceinline__ void score_phase(lds_u8* tile, const FragBases& fb,
   });
 }
 
-// PV phase: O^T[256 DH + ...] += V^T P^T of one tile; V fragments one column
-// tile ahead (vr[0] issued by the caller); slice(i) runs after MFMA i.
-template <int NRT, int DH, typename W>
+// Issue the V reads of column tiles 0 .. DV-1 (of this wave's half).
+template <int DH, int DV>
+__device__ __forceinline__ void issue_v_head(VRaw (&vr)[DV + 1], lds_u8* tile, const FragBases& fb) {
+  static_for<DV>([&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    issue_v<16 * DH + c>(vr[c], tile, fb);
+  });
+}
+
+// PV phase: O^T[256 DH + ...] += V^T P^T of one tile; V fragments DV column
+// tiles ahead (the first DV issued by the caller); slice(i) runs after MFMA i.
+template <int NRT, int DH, int DV, typename W>
 __device__ __forceinline__ void pv_phase(lds_u8* tile, const FragBases& fb,
                                          const bf16x8 (&pf)[NRT], f32x4 (&oacc)[16][NRT],
-                                         VRaw (&vr)[2], W&& slice) {
+                                         VRaw (&vr)[DV + 1], W&& slice) {
+  static_assert(DV >= 1 && 2 * DV < 16, "read-ahead depth");
   asm volatile("s_nop 1" ::: "memory");  // last VALU write of P before the first O MFMA
   static_for<16>([&](auto cc) {
     constexpr int c = decltype(cc)::value;
-    constexpr int cur = c & 1;
-    if constexpr (c + 1 < 16) {
-      issue_v<16 * DH + c + 1>(vr[cur ^ 1], tile, fb);
-      wait_lds<2>(vr[cur].a, vr[cur].b);
+    constexpr int cur = c % (DV + 1);
+    if constexpr (c + DV < 16) {
+      issue_v<16 * DH + c + DV>(vr[(c + DV) % (DV + 1)], tile, fb);
+      wait_lds<2 * DV>(vr[cur].a, vr[cur].b);
     } else {
-      wait_lds<0>(vr[cur].a, vr[cur].b);
+      wait_lds<2 * (15 - c)>(vr[cur].a, vr[cur].b);
     }
     const bf16x8 vf = finish_v(vr[cur]);
     static_for<NRT>([&](auto rc) {
@@ -546,68 +581,89 @@ __device__ __forceinline__ void pv_phase(lds_u8* tile, const FragBases& fb,
 }
 
 // Online softmax of one tile (base 2) with a lazy per-row reference m_run:
-// P = 2^(x - m_run); the first tile that shows a row a key sets its
-// reference, which moves only when a tile maximum exceeds it by more than
-// kLazyOctaves (then O and l are rescaled: rare).  Split into 8 slices per
-// 16-row tile so that it can run between MFMAs of the other phase.
+// P = 2^(c s - m_run) with c = sm_scale * kv_scale * log2(e) > 0; the first
+// tile that shows a row a key sets its reference, which moves only when a
+// tile maximum exceeds it by more than kLazyOctaves (then O and l are
+// rescaled: rare).  Split into kSoftSlices phases, each over all row tiles
+// (independent chains the scheduler can interleave), so that it can run
+// between MFMAs of the other phase.  The row maximum is taken on raw scores
+// (c > 0 keeps the order) and c is folded into one FMA per key.
+constexpr int kSoftSlices = 7;
+
 template <int NRT>
 struct SoftTile {
-  float x[NRT][8];
-  float mx[NRT], mu[NRT], psum[NRT];
+  float mx[NRT], nmu[NRT], psum[NRT];
 };
 
-template <int NRT, int S>
-__device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, const f32x4 (&sfull)[2][NRT],
+template <int NRT, int PH>
+__device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, f32x4 (&sfull)[2][NRT],
                                               bf16x8 (&pf)[NRT], float (&m_run)[NRT],
                                               float (&l_run)[NRT], f32x4 (&oacc)[16][NRT],
-                                              const int (&lim)[NRT], int k0, bool edge,
-                                              float scale_log2, int g, lds_u8* spill) {
-  constexpr int rt = S / 8, ph = S % 8;
-  if constexpr (ph <= 1) {  // scaled, masked logits of 4 keys
-    constexpr int kt = ph;
+                                              const int (&lim)[NRT], int k0, bool edge, float c,
+                                              int g, lds_u8* spill) {
+  if constexpr (PH == 0) {  // keys past a row's causal limit (last tiles of a chunk only)
+    if (edge) {
+      asm volatile("" ::: "memory");  // keep this a branch: interior tiles skip it
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float val = sfull[kt][rt][i] * scale_log2;
-      if (edge) {
-        const int key = k0 + 16 * kt + 4 * g + i;
-        val = key <= lim[rt] ? val : -INFINITY;
-      }
-      w.x[rt][4 * kt + i] = val;
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + 16 * kt + 4 * g + i;
+            sfull[kt][rt][i] = key <= lim[rt] ? sfull[kt][rt][i] : -INFINITY;
+          }
     }
-  } else if constexpr (ph == 2) {
-    float mx = w.x[rt][0];
+  } else if constexpr (PH == 1) {  // lane maximum over its 8 keys
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, w.x[rt][e]);
-    w.mx[rt] = mx;
-  } else if constexpr (ph == 3) {
-    w.mx[rt] = wave_max_across_groups(w.mx[rt]);
-  } else if constexpr (ph == 4) {
-    const float mx = w.mx[rt];
-    float m = m_run[rt] == -INFINITY ? mx : m_run[rt];  // O and l are still 0 before
-    const bool jump = mx > m + kLazyOctaves;
-    if (__builtin_amdgcn_ballot_w64(jump) != 0) {  // wave-uniform, rare
+    for (int rt = 0; rt < NRT; ++rt) {
+      const f32x4 a = sfull[0][rt], b = sfull[1][rt];
+      w.mx[rt] = max2(max3(a[0], a[1], a[2]), max3(a[3], b[0], max3(b[1], b[2], b[3])));
+    }
+  } else if constexpr (PH == 2) {  // row maximum (the 4 lane groups), scaled
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) w.mx[rt] = wave_max_across_groups(w.mx[rt]) * c;
+  } else if constexpr (PH == 3) {  // reference; rare exact rescale
+    bool jump_any = false;
+    float m[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      m[rt] = m_run[rt] == -INFINITY ? w.mx[rt] : m_run[rt];  // O and l are still 0 before
+      jump_any = jump_any || w.mx[rt] > m[rt] + kLazyOctaves;
+    }
+    if (__builtin_amdgcn_ballot_w64(jump_any) != 0) {  // wave-uniform, rare
       asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // O MFMAs retired
-      const float f = jump ? __builtin_amdgcn_exp2f(m - mx) : 1.0f;
-      m = jump ? mx : m;
-      l_run[rt] *= f;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) scale_o(oacc[c][rt], f, spill);
-    }
-    m_run[rt] = m;
-    w.mu[rt] = m == -INFINITY ? 0.0f : m;
-  } else if constexpr (ph <= 6) {  // P of 4 keys: x - mu <= kLazyOctaves
-    constexpr int kt = ph - 5;
-    float psum = kt == 0 ? 0.0f : w.psum[rt];
+      for (int rt = 0; rt < NRT; ++rt) {
+        const bool jump = w.mx[rt] > m[rt] + kLazyOctaves;
+        const float f = jump ? __builtin_amdgcn_exp2f(m[rt] - w.mx[rt]) : 1.0f;
+        m[rt] = jump ? w.mx[rt] : m[rt];
+        l_run[rt] *= f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // v_exp_f32: results below the fp32 normal range flush to 0
-      const float pe = __builtin_amdgcn_exp2f(w.x[rt][4 * kt + i] - w.mu[rt]);
-      psum += pe;
-      pf[rt][4 * kt + i] = (__bf16)pe;
+        for (int cc = 0; cc < 16; ++cc) scale_o(oacc[cc][rt], f, spill);
+      }
     }
-    w.psum[rt] = psum;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      m_run[rt] = m[rt];
+      w.nmu[rt] = m[rt] == -INFINITY ? 0.0f : -m[rt];
+    }
+  } else if constexpr (PH <= 5) {  // P of 4 keys per row tile: c s - m <= kLazyOctaves
+    constexpr int kt = PH - 4;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)  // v_exp_f32: results below the fp32 normal range flush to 0
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sfull[kt][rt][i], c, w.nmu[rt]));
+      const float ps = (p[0] + p[1]) + (p[2] + p[3]);
+      w.psum[rt] = kt == 0 ? ps : w.psum[rt] + ps;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pf[rt][4 * kt + i] = (__bf16)p[i];
+    }
   } else {
-    l_run[rt] += w.psum[rt];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) l_run[rt] += w.psum[rt];
   }
 }
 
@@ -626,6 +682,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
   constexpr int NS = Stage<FP8>::kSets;
   constexpr int kAhead = (NS - 1) * kPieces;  // loads issued after a set's own
   constexpr int kXsWave = NRT * 2 * 256;      // floats of one wave's partial scores
+  constexpr int DK = k_ahead<NRT, FP8>(), DV = v_ahead<NRT, FP8>();
   const UnitCtx u = us.uc;
   const uint8_t* kv = us.kv_unit;
   if (u.ntiles <= 0) return;
@@ -643,7 +700,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
 
   // full scores of tile 0
   f32x4 sacc[2][NRT], sfull[2][NRT];
-  score_phase<NRT, DH>(lds, fb, qf, sacc, [](auto) {});
+  score_phase<NRT, DH, DK>(lds, fb, qf, sacc, [](auto) {});
   asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");  // score MFMAs retire before the reads
   {
     float* mine = xs + wave * kXsWave;
@@ -663,7 +720,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         sfull[kt][rt] = sacc[kt][rt] + *(const f32x4*)(peer + ((rt * 2 + kt) * 64 + lane) * 4);
   }
 
-  VRaw vr[2];
+  VRaw vr[DV + 1];
   bf16x8 pf[NRT];
   SoftTile<NRT> sw;
   for (int base = 0; base < u.ntiles; base += NS) {
@@ -681,11 +738,11 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         lds_u8* slot_s = lds + ((t + 2) % kRing) * kTileBytes;
         const int k0 = t * kTK;
         const bool edge = k0 + kTK - 1 > u.min_lim;
-        issue_v<16 * DH>(vr[0], slot_t, fb);
+        issue_v_head<DH, DV>(vr, slot_t, fb);
 
         // scores of tile t + 1  ||  softmax of tile t
-        constexpr int kScoreMfma = 18 * NRT, kSoftSlices = 8 * NRT;
-        score_phase<NRT, DH>(slot_n, fb, qf, sacc, [&](auto ic) {
+        constexpr int kScoreMfma = 18 * NRT;
+        score_phase<NRT, DH, DK>(slot_n, fb, qf, sacc, [&](auto ic) {
           constexpr int i = decltype(ic)::value;
           slices_at<kSoftSlices, kScoreMfma, i>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
@@ -697,7 +754,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         // O of tile t  ||  exchange write of tile t+1, staging of tile t + 2
         constexpr int kPvMfma = 16 * NRT;
         constexpr int kStageSlices = NRT + 1 + 2 * kPieces;
-        pv_phase<NRT, DH>(slot_t, fb, pf, oacc, vr, [&](auto ic) {
+        pv_phase<NRT, DH, DV>(slot_t, fb, pf, oacc, vr, [&](auto ic) {
           constexpr int i = decltype(ic)::value;
           slices_at<kStageSlices, kPvMfma, i>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
