@@ -69,10 +69,15 @@ constexpr int kPieces = kTK * kChunks / kThreads;  // 9
 template <bool FP8>
 struct Stage {
   using piece_t = typename std::conditional<FP8, u32x2, u32x4>::type;
-  static constexpr int kSets = FP8 ? 3 : 2;   // tiles in flight per thread
   static constexpr int kGlobalRowBytes = FP8 ? kDqk : 2 * kDqk;
   piece_t p[kPieces];
 };
+
+// Staging sets (tiles in flight per thread): as many as the register budget
+// of each row-tile count allows; with 3 row tiles a bf16 set is 36 VGPRs and
+// one set, issued one iteration ahead of its LDS store, is what fits.
+template <bool FP8, int NRT>
+constexpr int stage_sets() { return FP8 ? 3 : (NRT == 3 ? 1 : 2); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -679,7 +684,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
                                               const bf16x8 (&qf)[NRT][9], f32x4 (&oacc)[16][NRT],
                                               float (&m_run)[NRT], float (&l_run)[NRT],
                                               const int (&lim)[NRT], int tid, int g, int lane) {
-  constexpr int NS = Stage<FP8>::kSets;
+  constexpr int NS = stage_sets<FP8, NRT>();
   constexpr int kAhead = (NS - 1) * kPieces;  // loads issued after a set's own
   constexpr int kXsWave = NRT * 2 * 256;      // floats of one wave's partial scores
   constexpr int DK = k_ahead<NRT, FP8>(), DV = v_ahead<NRT, FP8>();
@@ -687,15 +692,16 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
   const uint8_t* kv = us.kv_unit;
   if (u.ntiles <= 0) return;
 
+  // prologue: tiles 0 and 1 into their slots; tile k always travels in set k % NS
   Stage<FP8> st[NS];
 #pragma unroll
   for (int k = 0; k < NS; ++k) stage_load<FP8>(st[k], kv, k, u.nkeys, tid);
-  wait_stage<kAhead, FP8>(st[0]);
-  stage_store<FP8>(st[0], lds, tid);
-  stage_load<FP8>(st[0], kv, NS, u.nkeys, tid);
-  wait_stage<kAhead, FP8>(st[1]);
-  stage_store<FP8>(st[1], lds + kTileBytes, tid);
-  stage_load<FP8>(st[1], kv, NS + 1, u.nkeys, tid);
+  static_for<2>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    wait_stage<kAhead, FP8>(st[j % NS]);
+    stage_store<FP8>(st[j % NS], lds + j * kTileBytes, tid);
+    stage_load<FP8>(st[j % NS], kv, j + NS, u.nkeys, tid);
+  });
   lds_barrier();
 
   // full scores of tile 0
