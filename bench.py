@@ -8,7 +8,9 @@ kernel (mla_decode_run) plus the split-KV merge (mla_decode_reduce).  The plan
 is built once per workload beforehand (a host-side prepared plan).  Before
 every timed step a 1 GiB buffer is rewritten so the KV is read from HBM, not
 from the 256 MB Infinity Cache (cold-cache timing).  Times come from HIP events
-recorded on the stream the kernels are launched on.
+recorded on the stream the kernels are launched on: the per-call time from
+events around the whole call only; the main-kernel time (roofline) from a
+second set of steps with one more event between the two kernels.
 
 Prints ONE JSON line.  The headline workload is fp8-e4m3 KV, bf16 Q, batch 1,
 H=12, q=8, ctx=1048576; `value` is its median us per call.  `per_workload`
@@ -72,20 +74,29 @@ def measure(inp, dev, steps, warmup, flush, **plan_opts):
         flush.add_(1)
         step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    # the call: events only around run + reduce
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     t0 = time.perf_counter()
     for k in range(steps):
         flush.add_(1)  # evict L2 / Infinity Cache (untimed: outside the events)
+        ev[k][0].record(stream)
+        step()
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tot = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(steps)]) * 1e3
+    # breakdown: a middle event splits the main kernel from the merge
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        flush.add_(1)
         ev[k][0].record(stream)
         mb.mla_decode_run(plan, q, kv, inp.sm_scale, inp.kv_scale, o, lse, ws, ws.numel(), stream)
         ev[k][1].record(stream)
         mb.mla_decode_reduce(plan, ws, o, lse, stream)
         ev[k][2].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     main = np.array([ev[k][0].elapsed_time(ev[k][1]) for k in range(steps)]) * 1e3
     red = np.array([ev[k][1].elapsed_time(ev[k][2]) for k in range(steps)]) * 1e3
-    tot = main + red
     kv_bytes = inp.kv.nbytes
     med = float(np.median(tot))
     return {
@@ -163,7 +174,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed calls per workload (the GPU clocks settle over ~50)")
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--cpu-rows", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true",

@@ -848,12 +848,14 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_main(const MainArgs ar
     unit_body<FP8, NRT, 0>(args, smem);
 }
 
-// Split-KV merge.  One 512-thread block per (split output row, column half):
-// wave w folds chunks s = w, w + 8, ... (lane c owns columns 4c .. 4c+3 of the
-// half), then the 8 waves' sums are added in wave order through LDS.  Every
-// sum has a fixed order, so replays are bitwise identical.
-constexpr int kRedThreads = 512;
-constexpr int kRedWaves = kRedThreads / 64;
+// Split-KV merge.  One 256-thread block per (split output row, quarter of the
+// 512 value columns).  Lane (half p, column group cg) of wave w owns columns
+// 4 cg .. 4 cg + 3 of the quarter and folds chunks s = 8 i + (2 w + p) in
+// ascending order; the 8 partial sums are then added in a fixed order through
+// LDS, so replays are bitwise identical.
+constexpr int kRedThreads = 256;
+constexpr int kRedParts = 2 * kRedThreads / 64;  // (wave, lane half) partial sums
+constexpr int kRedCols = 128;                     // value columns per block
 
 __device__ __forceinline__ float wave_max64(float v) {
   v = wave_max_across_groups(v);          // lanes l, l^16, l^32, l^48
@@ -863,10 +865,10 @@ __device__ __forceinline__ float wave_max64(float v) {
 }
 
 __global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_kernel(const ReduceArgs args) {
-  __shared__ f32x4 red_acc[kRedWaves][64];
-  __shared__ float red_w[kRedWaves];
-  const int gr = blockIdx.x >> 1;
-  const int half = blockIdx.x & 1;
+  __shared__ f32x4 red_acc[kRedParts][32];
+  __shared__ float red_w[kRedParts];
+  const int gr = blockIdx.x >> 2;
+  const int quarter = blockIdx.x & 3;
   if (gr >= args.num_rows) return;
   int b = 0;
   while (b + 1 < args.num_seqs && args.row0[b + 1] <= gr) ++b;
@@ -879,6 +881,8 @@ __global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_kernel(const Re
   const int64_t pbase = (int64_t)sd.part_row0 + (int64_t)t * S * R + r;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
+  const int part = 2 * wave + (lane >> 5);
+  const int cg = lane & 31;
 
   float M = -INFINITY;
   for (int s = lane; s < S; s += 64) M = fmaxf(M, args.part_lse[pbase + (int64_t)s * R]);
@@ -886,9 +890,9 @@ __global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_kernel(const Re
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.0f;
-  const float* po = args.part_o + 256 * half + 4 * lane;
+  const float* po = args.part_o + kRedCols * quarter + 4 * cg;
 #pragma unroll 4
-  for (int s = wave; s < S; s += kRedWaves) {
+  for (int s = part; s < S; s += kRedParts) {
     const int64_t prow = pbase + (int64_t)s * R;
     const float ls = args.part_lse[prow];
     if (ls == -INFINITY) continue;  // a chunk this row cannot see: weight 0
@@ -896,24 +900,24 @@ __global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_kernel(const Re
     W += w;
     acc += w * *(const f32x4*)(po + prow * kDv);
   }
-  red_acc[wave][lane] = acc;
-  if (lane == 0) red_w[wave] = W;
+  red_acc[part][cg] = acc;
+  if (cg == 0) red_w[part] = W;
   __syncthreads();
-  if (wave != 0) return;
-  f32x4 tot = red_acc[0][lane];
+  if (threadIdx.x >= 32) return;
+  f32x4 tot = red_acc[0][cg];
   float Wt = red_w[0];
 #pragma unroll
-  for (int w2 = 1; w2 < kRedWaves; ++w2) {
-    tot += red_acc[w2][lane];
-    Wt += red_w[w2];
+  for (int k = 1; k < kRedParts; ++k) {
+    tot += red_acc[k][cg];
+    Wt += red_w[k];
   }
   const float inv = 1.0f / Wt;
   const int64_t orow = (int64_t)sd.q_row0 + (int64_t)t * R + r;
   uint2 pk;
   pk.x = pack_bf16x2(tot[0] * inv, tot[1] * inv);
   pk.y = pack_bf16x2(tot[2] * inv, tot[3] * inv);
-  *(uint2*)(args.o + orow * kDv + 256 * half + 4 * lane) = pk;
-  if (half == 0 && lane == 0) args.lse[orow] = M + __logf(Wt);
+  *(uint2*)(args.o + orow * kDv + kRedCols * quarter + 4 * cg) = pk;
+  if (quarter == 0 && cg == 0) args.lse[orow] = M + __logf(Wt);
 }
 
 // ------------------------------------------------------------- launchers
@@ -940,7 +944,7 @@ hipError_t launch_main(const MainArgs& a, bool fp8, int nrt, hipStream_t stream)
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
-  const int grid = 2 * a.num_rows;
+  const int grid = (kDv / kRedCols) * a.num_rows;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(mla_decode_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, stream, a);
   return hipGetLastError();
