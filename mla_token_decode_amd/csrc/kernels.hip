@@ -371,6 +371,9 @@ __device__ __forceinline__ void scale_o(f32x4& acc, float f, lds_u8* spill) {
 // contents, discarded).
 
 constexpr int kRing = 3;
+// Where the staging of tile t + 2 runs: between the score MFMAs (which carry
+// only the 7 softmax slices) rather than between the PV MFMAs.
+constexpr bool kStageWithScores = true;
 
 struct UnitCtx {
   int lo, nkeys, ntiles, min_lim;
@@ -672,6 +675,43 @@ __device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, f32x4 (&sfull)[2
   }
 }
 
+// A row group with no row of the unit only takes its share of the staging
+// (same loads, stores and barriers as unit_pipeline, no LDS reads, no MFMAs).
+// It is a separate loop, so its staged registers never meet the other's.
+template <bool FP8, int NRT>
+__device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* lds, int tid) {
+  constexpr int NS = stage_sets<FP8, NRT>();
+  constexpr int kAhead = (NS - 1) * kPieces;
+  const UnitCtx u = us.uc;
+  const uint8_t* kv = us.kv_unit;
+  if (u.ntiles <= 0) return;
+  Stage<FP8> st[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) stage_load<FP8>(st[k], kv, k, u.nkeys, tid);
+  static_for<2>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    wait_stage<kAhead, FP8>(st[j % NS]);
+    stage_store<FP8>(st[j % NS], lds + j * kTileBytes, tid);
+    stage_load<FP8>(st[j % NS], kv, j + NS, u.nkeys, tid);
+  });
+  lds_barrier();
+  lds_barrier();  // the exchange of tile 0's scores
+  for (int base = 0; base < u.ntiles; base += NS) {
+    static_for<NS>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int ks = (k + 2) % NS;
+      const int t = base + k;
+      if (t < u.ntiles) {
+        wait_stage<kAhead, FP8>(st[ks]);
+        stage_store<FP8>(st[ks], lds + ((t + 2) % kRing) * kTileBytes, tid);
+        stage_load<FP8>(st[ks], kv, t + 2 + NS, u.nkeys, tid);
+        lds_barrier();
+      }
+    });
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads issued past the end
+}
+
 // The whole KV chunk of a unit, software-pipelined as described above.  The
 // tile loop is unrolled by the number of staging sets so that set k always
 // holds tiles = k mod NS; every global load and wait is unconditional (tiles
@@ -746,7 +786,20 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         const bool edge = k0 + kTK - 1 > u.min_lim;
         issue_v_head<DH, DV>(vr, slot_t, fb);
 
-        // scores of tile t + 1  ||  softmax of tile t
+        // staging of tile t + 2: wait for its loads, LDS store, next loads
+        constexpr int kStageSlices = 1 + 2 * kPieces;
+        auto stage_slice = [&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          if constexpr (s == 0) {
+            wait_stage<kAhead, FP8>(st[ks]);
+          } else if constexpr (s < 1 + kPieces) {
+            stage_store_piece<FP8, s - 1>(st[ks], slot_s, tid);
+          } else {
+            stage_load_piece<FP8, s - 1 - kPieces>(st[ks], kv, t + 2 + NS, u.nkeys, tid);
+          }
+        };
+
+        // scores of tile t + 1  ||  softmax of tile t (and the staging)
         constexpr int kScoreMfma = 18 * NRT;
         score_phase<NRT, DH, DK>(slot_n, fb, qf, sacc, [&](auto ic) {
           constexpr int i = decltype(ic)::value;
@@ -755,28 +808,21 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
             softmax_slice<NRT, s>(sw, sfull, pf, m_run, l_run, oacc, lim, k0, edge, us.scale_log2,
                                   g, spill);
           });
+          if constexpr (kStageWithScores) slices_at<kStageSlices, kScoreMfma, i>(stage_slice);
         });
 
-        // O of tile t  ||  exchange write of tile t+1, staging of tile t + 2
+        // O of tile t  ||  exchange write of tile t + 1 (and the staging)
         constexpr int kPvMfma = 16 * NRT;
-        constexpr int kStageSlices = NRT + 1 + 2 * kPieces;
         pv_phase<NRT, DH, DV>(slot_t, fb, pf, oacc, vr, [&](auto ic) {
           constexpr int i = decltype(ic)::value;
-          slices_at<kStageSlices, kPvMfma, i>([&](auto sc) {
+          slices_at<NRT, kPvMfma, i>([&](auto sc) {  // partial scores of tile t + 1
             constexpr int s = decltype(sc)::value;
-            if constexpr (s < NRT) {  // partial scores of tile t + 1
-              if constexpr (s == 0) asm volatile("s_nop 15" ::: "memory");
+            if constexpr (s == 0) asm volatile("s_nop 15" ::: "memory");
 #pragma unroll
-              for (int kt = 0; kt < 2; ++kt)
-                *(f32x4*)(mine + ((s * 2 + kt) * 64 + lane) * 4) = sacc[kt][s];
-            } else if constexpr (s == NRT) {
-              wait_stage<kAhead, FP8>(st[ks]);
-            } else if constexpr (s < NRT + 1 + kPieces) {
-              stage_store_piece<FP8, s - NRT - 1>(st[ks], slot_s, tid);
-            } else {
-              stage_load_piece<FP8, s - NRT - 1 - kPieces>(st[ks], kv, t + 2 + NS, u.nkeys, tid);
-            }
+            for (int kt = 0; kt < 2; ++kt)
+              *(f32x4*)(mine + ((s * 2 + kt) * 64 + lane) * 4) = sacc[kt][s];
           });
+          if constexpr (!kStageWithScores) slices_at<kStageSlices, kPvMfma, i>(stage_slice);
         });
 
         lds_barrier();
@@ -802,6 +848,7 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
   const int l16 = lane & 15;
   const int g = lane >> 4;
   const int grow0 = (wave >> 1) * 16 * NRT;  // first unit row of this wave's row group
+  const bool wave_active = grow0 < us.RU;     // the row group holds a row of the unit
   int lim[NRT];  // last key (chunk-relative) the lane's row may see
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
@@ -813,8 +860,8 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
   lds_u8* lds = (lds_u8*)smem;
   float* xs = (float*)(smem + kRing * kTileBytes);
 
-  // Rows past the unit hold zero Q and run the same instruction stream (their
-  // outputs are never written): no branch splits the staged registers.
+  // Rows past the unit hold zero Q (their outputs are never written); a row
+  // group with no row of the unit only stages (unit_staging_only).
   bf16x8 qf[NRT][9];
   load_q<NRT, DH>(us, grow0, l16, g, qf);
   // per-lane softmax state: lane owns unit row grow0 + 16 rt + l16
@@ -830,6 +877,10 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) zero_o(oacc[c][rt]);
 
+  if (!wave_active) {
+    unit_staging_only<FP8, NRT>(us, lds, tid);
+    return;
+  }
   unit_pipeline<FP8, NRT, DH>(us, lds, xs, wave, fb, qf, oacc, m_run, l_run, lim, tid, g, lane);
   epilogue<NRT, DH>(us, grow0, l16, g, oacc, m_run, l_run);
 }

@@ -8,8 +8,9 @@ inline assembly nor knows that an inline-assembly load completes later, so:
 * a VALU write of a VGPR must be at least 2 wait states before an MFMA that
   reads it, and an MFMA result must not be touched by a non-MFMA instruction
   within 19 wait states (the longest MFMA used here);
-* a register that a staged load targets must not be copied anywhere in the
-  tile loop (the copy would read it before the data arrives);
+* a register that a staged load targets must not be copied anywhere in a
+  loop that issues staged loads, nor between a prologue's loads and its loop
+  (the copy would read it before the data arrives);
 * the tile loop must not move MFMA accumulators or operands between register
   files (v_accvgpr_*), which is what keeps the loop short.
 """
@@ -114,26 +115,56 @@ def tile_loops(lines):
             if any("v_mfma" in lines[k] for k in idx)}
 
 
+def staging_loops(lines):
+    """{label: line indices} of the loops that issue staged loads."""
+    return {lab: idx for lab, idx in _loops(lines).items()
+            if any(STAGED_LOAD.search(lines[k]) for k in idx)}
+
+
+def _written(line):
+    """Registers an instruction line writes (first operand; both operands of a
+    lane swap); stores and scalar instructions write none we track."""
+    t = line.strip()
+    if not t or t.startswith(";") or t.startswith("."):
+        return set()
+    op, _, rest = t.partition(" ")
+    ops = [o.strip() for o in rest.split(";")[0].split(",")] if rest else []
+    if not ops or "store" in op or "write" in op or op.startswith("s_"):
+        return set()
+    if op.startswith("v_permlane") and "swap" in op:
+        return regs(ops[0]) | regs(ops[1])
+    return regs(ops[0])
+
+
+def _copy_of_staged(lines, order, pos, src):
+    """Walking back from order[pos] (wrapping around the loop), is the last
+    write of any register in src a staged load?"""
+    n = len(order)
+    for step in range(1, n):
+        line = lines[order[(pos - step) % n]]
+        w = _written(line)
+        if w & src:
+            return bool(STAGED_LOAD.search(line))
+    return False
+
+
 def staged_copies_in_loops(lines) -> list:
-    """Register copies whose source is a staged-load destination of the same loop."""
+    """Register copies that read a staged-load destination before anything
+    else has redefined it, i.e. copies of data that may still be in flight."""
     found = []
-    for lab, idx in tile_loops(lines).items():
-        staged = set()
-        for k in idx:
-            m = STAGED_LOAD.search(lines[k])
-            if m:
-                staged |= regs(m.group(1))
-        for k in idx:
+    for lab, idx in staging_loops(lines).items():
+        order = sorted(idx)
+        for pos, k in enumerate(order):
             m = re.search(r"v_mov_b(?:32|64)_e32 (v\S+), (v\S+)", lines[k])
-            if m and regs(m.group(2)) & staged:
+            if m and _copy_of_staged(lines, order, pos, regs(m.group(2))):
                 found.append(f"{lab}: {lines[k].strip()}")
     return found
 
 
 def staged_copies_in_prologues(lines) -> list:
-    """Copies of staged-load destinations between a prologue's first staged
-    load and the start of its tile loop (layout order)."""
-    loop_lines = set(k for idx in tile_loops(lines).values() for k in idx)
+    """Copies of staged-load destinations between a prologue's loads and the
+    start of its loop (layout order) before anything redefined them."""
+    loop_lines = set(k for idx in staging_loops(lines).values() for k in idx)
     found = []
     staged = set()
     for n, line in enumerate(lines):
@@ -147,11 +178,12 @@ def staged_copies_in_prologues(lines) -> list:
         m = re.search(r"v_mov_b(?:32|64)_e32 (v\S+), (v\S+)", line)
         if m and regs(m.group(2)) & staged:
             found.append(f"line {n}: {line.strip()}")
+        staged -= _written(line)
     return found
 
 
 def staged_loads_in_loops(lines) -> int:
-    return sum(1 for idx in tile_loops(lines).values() for k in idx
+    return sum(1 for idx in staging_loops(lines).values() for k in idx
                if STAGED_LOAD.search(lines[k]))
 
 

@@ -51,3 +51,15 @@ def test_scan_detects_a_planted_hazard():
                "\tv_accvgpr_read_b32 v8, a1"]
     found = asm_scan.mfma_hazards(planted)
     assert len(found) == 2, found
+
+
+def test_scan_detects_a_planted_staged_copy():
+    loop = [".LBB0_1:                                ; =>This Inner Loop Header: Depth=1",
+            "\tbuffer_load_dwordx2 v[10:11], v1, s[4:7], s8 offen",
+            "\tv_mfma_f32_16x16x32_bf16 v[0:3], v[4:7], v[4:7], v[0:3]",
+            "\tv_mov_b64_e32 v[20:21], v[10:11]",
+            "\ts_cbranch_scc1 .LBB0_1"]
+    assert len(asm_scan.staged_copies_in_loops(loop)) == 1
+    # the register was redefined (reused for another value) before the copy: no flag
+    reused = loop[:3] + ["\tv_add_f32_e32 v10, v2, v3"] + loop[3:]
+    assert asm_scan.staged_copies_in_loops(reused) == []
