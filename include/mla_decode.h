@@ -74,6 +74,7 @@ typedef enum {
 #define MLA_DV 512           /* value width: first 512 columns of the KV row */
 #define MLA_MAX_TILE_ROWS 128 /* H * F must not exceed this */
 #define MLA_KV_GRANULE 64    /* split-KV chunk lengths are multiples of this */
+#define MLA_MAX_SHARDS 1024  /* most shards mla_merge_shards combines */
 
 typedef struct mla_plan mla_plan; /* opaque, host-owned */
 
@@ -105,6 +106,28 @@ mla_status mla_decode_plan(int32_t batch, int32_t num_heads, const int32_t* q_le
                            const mla_plan_options* opts, mla_plan** plan_out,
                            size_t* workspace_bytes_out);
 
+/* Build a plan for one shard of each sequence's keys (decode context
+ * parallelism: every rank holds a contiguous range of a sequence's cached
+ * keys and decodes the same verify rows over it; "[Kimi-K3] Allow DSPARK
+ * verify on cutedsl_mla (fold_sq)" (sglang PR #33650), section "Which decode
+ * backend?", the TP1+DCP8 rows; "bench(cake_mla_varq_dcp_decode): ..."
+ * (flashinfer PR #5588), which benchmarks that decode).
+ *  As mla_decode_plan, except: kv_len[b] >= 1 is the number of keys this
+ *  shard holds (any size, also fewer than q_len[b]), and causal_end[b] >= 1
+ *  (HOST array) places the causal limit in the shard's local key indices:
+ *  verify token i sees the local keys j <= causal_end[b] - q_len[b] + i.  For
+ *  a shard that starts at global key `offset` of a sequence of `total` keys,
+ *  causal_end = total - offset; for the whole sequence, causal_end = kv_len
+ *  (which is mla_decode_plan).  A row that sees no key of the shard gets
+ *  O = 0 and LSE = -inf.  The outputs of the shards of one sequence combine
+ *  with mla_merge_shards.
+ *  Errors: as mla_decode_plan; INVALID_ARGUMENT also for causal_end == NULL
+ *  or causal_end[b] < 1. */
+mla_status mla_decode_plan_shard(int32_t batch, int32_t num_heads, const int32_t* q_len,
+                                 const int32_t* kv_len, const int32_t* causal_end,
+                                 mla_kv_dtype kv_dtype, const mla_plan_options* opts,
+                                 mla_plan** plan_out, size_t* workspace_bytes_out);
+
 /* Enqueue the main decode kernel(s) on `stream` (a hipStream_t; NULL = the
  * default stream) and return.
  *  q:   device bf16 [sum q_len, H, 576], token-major then head, row-major.
@@ -132,6 +155,22 @@ mla_status mla_decode_run(const mla_plan* plan, const void* q, const void* kv, f
 mla_status mla_decode_reduce(const mla_plan* plan, const void* workspace, void* o, float* lse,
                              void* stream);
 
+/* Enqueue the combination of per-shard results on `stream`: for every row r,
+ * in ascending shard order w, M = max_w lse_w[r], lse[r] = M + ln sum_w
+ * exp(lse_w[r] - M), O[r] = sum_w exp(lse_w[r] - lse[r]) * O_w[r]; shards a
+ * row sees nothing of (lse = -inf) get weight 0; a row no shard shows a key
+ * gets O = 0, LSE = -inf.  The same merge as mla_decode_reduce, for results
+ * that were gathered from several ranks (the page sections cited at
+ * mla_decode_plan_shard).
+ *  o_shards:   device bf16 [num_shards][num_rows][512] (each shard's O).
+ *  lse_shards: device fp32 [num_shards][num_rows] (each shard's LSE).
+ *  o: device bf16 [num_rows][512]; lse: device fp32 [num_rows] (outputs; they
+ *  must not overlap the inputs).  1 <= num_shards <= MLA_MAX_SHARDS,
+ *  num_rows >= 1; all pointers 16-byte aligned.
+ *  Errors: INVALID_ARGUMENT, UNSUPPORTED (device is not gfx950), DEVICE. */
+mla_status mla_merge_shards(int32_t num_rows, int32_t num_shards, const void* o_shards,
+                            const float* lse_shards, void* o, float* lse, void* stream);
+
 /* Free a plan (NULL is allowed). */
 void mla_plan_destroy(mla_plan* plan);
 
@@ -149,7 +188,7 @@ mla_status mla_plan_query(const mla_plan* plan, int32_t seq, int32_t* fold, int3
 
 /* Whole-plan facts: main-kernel work units (one workgroup each), tiles that
  * are split (rows merged by the reduce), main-kernel launches (one per slice
- * of up to 64 sequences), and the workspace bytes. Any pointer may be NULL. */
+ * of up to 60 sequences), and the workspace bytes. Any pointer may be NULL. */
 mla_status mla_plan_info(const mla_plan* plan, int32_t* num_units, int32_t* num_split_tiles,
                          int32_t* num_launches, size_t* workspace_bytes);
 

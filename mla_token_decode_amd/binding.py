@@ -25,8 +25,11 @@ DQK = 576
 DV = 512
 KV_GRANULE = 64
 
-EXPORTED = ["mla_decode_plan", "mla_decode_run", "mla_decode_reduce", "mla_plan_destroy",
-            "mla_last_error", "mla_plan_query", "mla_plan_info"]
+MAX_SHARDS = 1024
+
+EXPORTED = ["mla_decode_plan", "mla_decode_plan_shard", "mla_decode_run", "mla_decode_reduce",
+            "mla_merge_shards", "mla_plan_destroy", "mla_last_error", "mla_plan_query",
+            "mla_plan_info"]
 
 _lock = threading.Lock()
 _lib = None
@@ -59,6 +62,15 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(_Options), ctypes.POINTER(ctypes.c_void_p),
                                       ctypes.POINTER(ctypes.c_size_t)]
         L.mla_decode_plan.restype = ctypes.c_int
+        L.mla_decode_plan_shard.argtypes = [ctypes.c_int32, ctypes.c_int32, i32p, i32p, i32p,
+                                            ctypes.c_int, ctypes.POINTER(_Options),
+                                            ctypes.POINTER(ctypes.c_void_p),
+                                            ctypes.POINTER(ctypes.c_size_t)]
+        L.mla_decode_plan_shard.restype = ctypes.c_int
+        L.mla_merge_shards.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+        L.mla_merge_shards.restype = ctypes.c_int
         L.mla_decode_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
                                      ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p]
@@ -105,8 +117,10 @@ def _stream(stream):
 class Plan:
     """Owns an mla_plan (host memory); free with close() or by garbage collection."""
 
-    def __init__(self, num_heads, q_len, kv_len, kv_fp8=False, *, force_fold=0, force_splits=0,
-                 num_cus=0):
+    def __init__(self, num_heads, q_len, kv_len, kv_fp8=False, *, causal_end=None, force_fold=0,
+                 force_splits=0, num_cus=0):
+        """causal_end: None (mla_decode_plan), or per-sequence causal ends of a
+        key shard (mla_decode_plan_shard)."""
         L = lib()
         q_len = [int(v) for v in q_len]
         kv_len = [int(v) for v in kv_len]
@@ -119,9 +133,19 @@ class Plan:
         handle = ctypes.c_void_p()
         ws = ctypes.c_size_t(0)
         self._h = None
-        _check(L.mla_decode_plan(n, int(num_heads), qa, ka,
-                                 MLA_KV_FP8_E4M3 if kv_fp8 else MLA_KV_BF16, ctypes.byref(opts),
-                                 ctypes.byref(handle), ctypes.byref(ws)))
+        dtype = MLA_KV_FP8_E4M3 if kv_fp8 else MLA_KV_BF16
+        if causal_end is None:
+            _check(L.mla_decode_plan(n, int(num_heads), qa, ka, dtype, ctypes.byref(opts),
+                                     ctypes.byref(handle), ctypes.byref(ws)))
+        else:
+            causal_end = [int(v) for v in causal_end]
+            if len(causal_end) != n:
+                raise ValueError("causal_end must have one entry per sequence")
+            ca = (ctypes.c_int32 * max(n, 1))(*causal_end)
+            _check(L.mla_decode_plan_shard(n, int(num_heads), qa, ka, ca, dtype,
+                                           ctypes.byref(opts), ctypes.byref(handle),
+                                           ctypes.byref(ws)))
+        self.causal_end = causal_end
         self._h = handle
         self.num_heads = int(num_heads)
         self.q_len = q_len
@@ -174,6 +198,19 @@ def mla_decode_run(plan: Plan, q, kv, sm_scale: float, kv_scale: float, o, lse, 
 def mla_decode_reduce(plan: Plan, workspace, o, lse, stream=None):
     _check(lib().mla_decode_reduce(plan.handle, _ptr(workspace), _ptr(o), _ptr(lse),
                                    _stream(stream)))
+
+
+def mla_merge_shards(o_shards, lse_shards, o, lse, stream=None):
+    """Combine per-shard results: o_shards bf16 [W, rows, 512] (or [W, ..., 512]),
+    lse_shards fp32 [W, rows] (matching), into o bf16 [rows, 512], lse [rows]."""
+    num_shards = int(o_shards.shape[0])
+    num_rows = int(lse_shards[0].numel())
+    if int(lse_shards.shape[0]) != num_shards or int(o_shards[0].numel()) != num_rows * DV:
+        raise ValueError("o_shards must be [W, rows, 512] and lse_shards [W, rows]")
+    if int(o.numel()) != num_rows * DV or int(lse.numel()) != num_rows:
+        raise ValueError("o must hold rows x 512 values and lse rows values")
+    _check(lib().mla_merge_shards(num_rows, num_shards, _ptr(o_shards), _ptr(lse_shards), _ptr(o),
+                                  _ptr(lse), _stream(stream)))
 
 
 def alloc_outputs(plan: Plan, device="cuda"):

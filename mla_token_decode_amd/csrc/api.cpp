@@ -14,6 +14,7 @@ namespace mla {
 const char* last_error();
 hipError_t launch_main(const MainArgs& a, bool fp8, int nrt, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 namespace {
 
@@ -62,10 +63,10 @@ using namespace mla;
 
 extern "C" {
 
-mla_status mla_decode_plan(int32_t batch, int32_t num_heads, const int32_t* q_len,
-                           const int32_t* kv_len, mla_kv_dtype kv_dtype,
-                           const mla_plan_options* opts, mla_plan** plan_out,
-                           size_t* workspace_bytes_out) {
+static mla_status plan_common(int32_t batch, int32_t num_heads, const int32_t* q_len,
+                              const int32_t* kv_len, const int32_t* causal_end,
+                              mla_kv_dtype kv_dtype, const mla_plan_options* opts,
+                              mla_plan** plan_out, size_t* workspace_bytes_out) {
   if (!plan_out) {
     set_error("plan_out must be non-null");
     return MLA_ERR_INVALID_ARGUMENT;
@@ -84,7 +85,7 @@ mla_status mla_decode_plan(int32_t batch, int32_t num_heads, const int32_t* q_le
     set_error("out of host memory");
     return MLA_ERR_INVALID_ARGUMENT;
   }
-  mla_status st = build_plan(batch, num_heads, q_len, kv_len, kv_dtype, &o, p);
+  mla_status st = build_plan(batch, num_heads, q_len, kv_len, causal_end, kv_dtype, &o, p);
   if (st != MLA_OK) {
     delete p;
     return st;
@@ -92,6 +93,27 @@ mla_status mla_decode_plan(int32_t batch, int32_t num_heads, const int32_t* q_le
   *plan_out = p;
   if (workspace_bytes_out) *workspace_bytes_out = p->workspace_bytes;
   return MLA_OK;
+}
+
+mla_status mla_decode_plan(int32_t batch, int32_t num_heads, const int32_t* q_len,
+                           const int32_t* kv_len, mla_kv_dtype kv_dtype,
+                           const mla_plan_options* opts, mla_plan** plan_out,
+                           size_t* workspace_bytes_out) {
+  return plan_common(batch, num_heads, q_len, kv_len, nullptr, kv_dtype, opts, plan_out,
+                     workspace_bytes_out);
+}
+
+mla_status mla_decode_plan_shard(int32_t batch, int32_t num_heads, const int32_t* q_len,
+                                 const int32_t* kv_len, const int32_t* causal_end,
+                                 mla_kv_dtype kv_dtype, const mla_plan_options* opts,
+                                 mla_plan** plan_out, size_t* workspace_bytes_out) {
+  if (!causal_end) {
+    if (plan_out) *plan_out = nullptr;
+    set_error("causal_end must be a non-null host array");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  return plan_common(batch, num_heads, q_len, kv_len, causal_end, kv_dtype, opts, plan_out,
+                     workspace_bytes_out);
 }
 
 void mla_plan_destroy(mla_plan* plan) { delete plan; }
@@ -239,6 +261,38 @@ mla_status mla_decode_reduce(const mla_plan* plan, const void* workspace, void* 
       set_error("reduce kernel launch failed: %s", hipGetErrorString(e));
       return MLA_ERR_DEVICE;
     }
+  }
+  return MLA_OK;
+}
+
+mla_status mla_merge_shards(int32_t num_rows, int32_t num_shards, const void* o_shards,
+                            const float* lse_shards, void* o, float* lse, void* stream) {
+  if (num_rows < 1 || num_shards < 1 || num_shards > MLA_MAX_SHARDS) {
+    set_error("need num_rows >= 1 and 1 <= num_shards <= %d (got %d, %d)", MLA_MAX_SHARDS,
+              num_rows, num_shards);
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (!o_shards || !lse_shards || !o || !lse) {
+    set_error("o_shards, lse_shards, o and lse must be non-null device pointers");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (!aligned16(o_shards) || !aligned16(lse_shards) || !aligned16(o) || !aligned16(lse)) {
+    set_error("o_shards, lse_shards, o and lse must be 16-byte aligned");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  mla_status st = current_device(nullptr);
+  if (st != MLA_OK) return st;
+  MergeArgs a;
+  a.o_shards = static_cast<const uint16_t*>(o_shards);
+  a.lse_shards = lse_shards;
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.num_rows = num_rows;
+  a.num_shards = num_shards;
+  hipError_t e = launch_merge(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_error("merge kernel launch failed: %s", hipGetErrorString(e));
+    return MLA_ERR_DEVICE;
   }
   return MLA_OK;
 }

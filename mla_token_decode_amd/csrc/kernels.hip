@@ -422,7 +422,7 @@ __device__ __forceinline__ bool unit_setup(const MainArgs& args, UnitSetup& us) 
   us.row0 = sd.q_row0 + us.t * us.R + us.rowb0;    // first Q/O row of this unit
   us.uc.lo = us.s * sd.L;
   const int hi = min(us.uc.lo + sd.L, sd.n);
-  us.tail0 = sd.n - sd.qlen + us.t * sd.F;         // tile row r sees keys <= tail0 + r / H
+  us.tail0 = sd.ce - sd.qlen + us.t * sd.F;        // tile row r sees keys <= tail0 + r / H
   const int vis_lo = us.tail0 + us.rowb0 / us.H;   // every unit row sees keys <= vis_lo
   const int vis_hi = us.tail0 + (us.rowb0 + us.RU - 1) / us.H;
   us.hi_eff = min(hi, vis_hi + 1);                 // no unit row sees keys >= hi_eff
@@ -473,19 +473,22 @@ __device__ __forceinline__ void epilogue(const UnitSetup& us, int grow0,
     const int row = grow0 + 16 * rt + l16;
     const bool valid = row < us.RU;
     if (us.S == 1) {
-      const float inv = us.o_scale / lt;
+      // a row that sees no key (only possible for a key shard): O = 0, LSE = -inf
+      const bool empty = !(lt > 0.0f);
+      const float inv = empty ? 0.0f : us.o_scale / lt;
       const int64_t orow = (int64_t)us.row0 + row;
       if (valid) {
         uint16_t* op = us.o + orow * kDv + 256 * DH + 4 * g;
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-          const f32x4 o4 = oacc[c][rt] * inv;
+          const f32x4 o4 = empty ? f32x4{0.f, 0.f, 0.f, 0.f} : oacc[c][rt] * inv;
           uint2 pk;
           pk.x = pack_bf16x2(o4[0], o4[1]);
           pk.y = pack_bf16x2(o4[2], o4[3]);
           *(uint2*)(op + 16 * c) = pk;
         }
-        if (g == 0 && DH == 0) us.lse[orow] = (m_run[rt] + log2f(lt)) * ln2;
+        if (g == 0 && DH == 0)
+          us.lse[orow] = empty ? -INFINITY : (m_run[rt] + log2f(lt)) * ln2;
       }
     } else {
       const int64_t prow =
@@ -962,13 +965,69 @@ __global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_kernel(const Re
     tot += red_acc[k][cg];
     Wt += red_w[k];
   }
-  const float inv = 1.0f / Wt;
+  const bool empty = !(Wt > 0.0f);  // no chunk shows this row a key (key shards only)
+  const float inv = empty ? 0.0f : 1.0f / Wt;
   const int64_t orow = (int64_t)sd.q_row0 + (int64_t)t * R + r;
   uint2 pk;
   pk.x = pack_bf16x2(tot[0] * inv, tot[1] * inv);
   pk.y = pack_bf16x2(tot[2] * inv, tot[3] * inv);
   *(uint2*)(args.o + orow * kDv + kRedCols * quarter + 4 * cg) = pk;
-  if (quarter == 0 && cg == 0) args.lse[orow] = M + __logf(Wt);
+  if (quarter == 0 && cg == 0) args.lse[orow] = empty ? -INFINITY : M + __logf(Wt);
+}
+
+// Combination of per-shard results (bf16 O, fp32 LSE), same arithmetic and
+// fixed order as the split-KV merge: one 256-thread block per (row, quarter of
+// the columns); lane (half p, column group cg) of wave w folds shards
+// s = 8 i + (2 w + p) in ascending order, then the 8 partial sums are added
+// in order through LDS.
+__global__ __launch_bounds__(kRedThreads) void mla_merge_shards_kernel(const MergeArgs args) {
+  __shared__ f32x4 red_acc[kRedParts][32];
+  __shared__ float red_w[kRedParts];
+  const int row = blockIdx.x >> 2;
+  const int quarter = blockIdx.x & 3;
+  if (row >= args.num_rows) return;
+  const int W = args.num_shards;
+  const int64_t rows = args.num_rows;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int part = 2 * wave + (lane >> 5);
+  const int cg = lane & 31;
+
+  float M = -INFINITY;
+  for (int s = lane; s < W; s += 64) M = fmaxf(M, args.lse_shards[s * rows + row]);
+  M = wave_max64(M);
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float Wsum = 0.0f;
+  const uint16_t* po = args.o_shards + kRedCols * quarter + 4 * cg;
+  for (int s = part; s < W; s += kRedParts) {
+    const float ls = args.lse_shards[s * rows + row];
+    if (ls == -INFINITY) continue;
+    const float w = __expf(ls - M);
+    Wsum += w;
+    const uint2 pk = *(const uint2*)(po + (s * rows + row) * kDv);
+    const f32x4 v = {__builtin_bit_cast(float, pk.x << 16), __builtin_bit_cast(float, pk.x & 0xffff0000u),
+                     __builtin_bit_cast(float, pk.y << 16), __builtin_bit_cast(float, pk.y & 0xffff0000u)};
+    acc += w * v;
+  }
+  red_acc[part][cg] = acc;
+  if (cg == 0) red_w[part] = Wsum;
+  __syncthreads();
+  if (threadIdx.x >= 32) return;
+  f32x4 tot = red_acc[0][cg];
+  float Wt = red_w[0];
+#pragma unroll
+  for (int k = 1; k < kRedParts; ++k) {
+    tot += red_acc[k][cg];
+    Wt += red_w[k];
+  }
+  const bool empty = !(Wt > 0.0f);
+  const float inv = empty ? 0.0f : 1.0f / Wt;
+  uint2 pk;
+  pk.x = pack_bf16x2(tot[0] * inv, tot[1] * inv);
+  pk.y = pack_bf16x2(tot[2] * inv, tot[3] * inv);
+  *(uint2*)(args.o + (int64_t)row * kDv + kRedCols * quarter + 4 * cg) = pk;
+  if (quarter == 0 && cg == 0) args.lse[row] = empty ? -INFINITY : M + __logf(Wt);
 }
 
 // ------------------------------------------------------------- launchers
@@ -998,6 +1057,12 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
   const int grid = (kDv / kRedCols) * a.num_rows;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(mla_decode_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
+  const int grid = (kDv / kRedCols) * a.num_rows;
+  hipLaunchKernelGGL(mla_merge_shards_kernel, dim3(grid), dim3(kRedThreads), 0, stream, a);
   return hipGetLastError();
 }
 

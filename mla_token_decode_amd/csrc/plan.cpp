@@ -84,7 +84,8 @@ double plan_cost(const std::vector<int32_t>& q_len, const std::vector<int32_t>& 
 }  // namespace
 
 mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int32_t* kv_len,
-                      mla_kv_dtype dtype, const mla_plan_options* opts, mla_plan* plan) {
+                      const int32_t* causal_end, mla_kv_dtype dtype,
+                      const mla_plan_options* opts, mla_plan* plan) {
   if (batch < 1) {
     set_error("batch must be >= 1 (got %d)", batch);
     return MLA_ERR_INVALID_ARGUMENT;
@@ -118,9 +119,14 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
   }
   int64_t sum_q = 0, sum_kv = 0;
   for (int b = 0; b < batch; ++b) {
-    if (q_len[b] < 1 || kv_len[b] < q_len[b]) {
+    if (!causal_end && (q_len[b] < 1 || kv_len[b] < q_len[b])) {
       set_error("sequence %d: need 1 <= q_len <= kv_len (got q_len=%d kv_len=%d)", b, q_len[b],
                 kv_len[b]);
+      return MLA_ERR_INVALID_ARGUMENT;
+    }
+    if (causal_end && (q_len[b] < 1 || kv_len[b] < 1 || causal_end[b] < 1)) {
+      set_error("sequence %d: need q_len >= 1, kv_len >= 1 and causal_end >= 1 (got %d, %d, %d)", b,
+                q_len[b], kv_len[b], causal_end[b]);
       return MLA_ERR_INVALID_ARGUMENT;
     }
     sum_q += q_len[b];
@@ -180,6 +186,7 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
     d.q_row0 = static_cast<int32_t>(q_row);
     d.kv_row0 = static_cast<int32_t>(kv_row);
     d.n = kl[b];
+    d.ce = causal_end ? causal_end[b] : kl[b];
     d.qlen = ql[b];
     d.F = F[b];
     d.T = ql[b] / F[b];

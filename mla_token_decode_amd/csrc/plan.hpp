@@ -35,6 +35,7 @@ struct SeqDesc {
   int32_t NRB;        // row blocks per tile (tiles of more than 96 rows are cut)
   int32_t RBS;        // rows per row block (multiple of 16 unless NRB == 1)
   int32_t unit0;      // first work unit of the sequence within its launch
+  int32_t ce;         // causal end: token i sees the keys j <= ce - qlen + i (ce = n normally)
 };
 
 struct MainArgs {
@@ -66,6 +67,15 @@ struct ReduceArgs {
   int32_t row0[kMaxSeqPerLaunch];  // first reduce row of each sequence in this launch
 };
 
+struct MergeArgs {
+  const uint16_t* o_shards;   // bf16 [num_shards][num_rows][512]
+  const float* lse_shards;    // fp32 [num_shards][num_rows]
+  uint16_t* o;                // bf16 [num_rows][512]
+  float* lse;                 // fp32 [num_rows]
+  int32_t num_rows;
+  int32_t num_shards;
+};
+
 struct Launch {
   int seq_begin, seq_end;  // [begin, end) global sequence indices
   int num_units;
@@ -92,7 +102,8 @@ struct mla_plan {
 namespace mla {
 // Implemented in plan.cpp.
 mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int32_t* kv_len,
-                      mla_kv_dtype dtype, const mla_plan_options* opts, mla_plan* plan);
+                      const int32_t* causal_end, mla_kv_dtype dtype,
+                      const mla_plan_options* opts, mla_plan* plan);
 void set_error(const char* fmt, ...);
 int fold_factor(int H, int q, int cap);
 void split_layout(int64_t n, int S, int G, int32_t* L, int32_t* S_eff);

@@ -133,3 +133,39 @@ def test_query_out_of_range():
     p = plan(4, [1, 1], [3, 3])
     with pytest.raises(mb.MlaError):
         p.query(2)
+
+
+def test_shard_plan_validation():
+    # a shard may hold fewer keys than verify tokens
+    p = mb.Plan(12, [8], [5], False, causal_end=[5], num_cus=256)
+    assert p.query(0)[0] == 8
+    for bad in ([0], [-3]):
+        with pytest.raises(mb.MlaError) as e:
+            mb.Plan(12, [8], [100], False, causal_end=bad, num_cus=256)
+        assert e.value.status == mb.MLA_ERR_INVALID_ARGUMENT
+    with pytest.raises(mb.MlaError) as e:
+        mb.Plan(12, [8], [0], False, causal_end=[10], num_cus=256)
+    assert e.value.status == mb.MLA_ERR_INVALID_ARGUMENT
+    # a whole-sequence plan still needs kv_len >= q_len
+    with pytest.raises(mb.MlaError):
+        mb.Plan(12, [8], [5], False, num_cus=256)
+
+
+def test_shard_plan_without_causal_end_is_rejected():
+    L = mb.lib()
+    qa = (ctypes.c_int32 * 1)(8)
+    ka = (ctypes.c_int32 * 1)(100)
+    opts = mb._Options(0, 0, 256)
+    h = ctypes.c_void_p()
+    st = L.mla_decode_plan_shard(1, 12, qa, ka, None, mb.MLA_KV_BF16, ctypes.byref(opts),
+                                 ctypes.byref(h), None)
+    assert st == mb.MLA_ERR_INVALID_ARGUMENT and not h.value
+
+
+def test_merge_shards_argument_checks():
+    L = mb.lib()
+    fake = 1 << 20  # aligned, never dereferenced: the checks reject before any device work
+    for rows, shards in ((0, 2), (4, 0), (4, mb.MAX_SHARDS + 1)):
+        assert L.mla_merge_shards(rows, shards, fake, fake, fake, fake, None) == mb.MLA_ERR_INVALID_ARGUMENT
+    assert L.mla_merge_shards(4, 2, None, fake, fake, fake, None) == mb.MLA_ERR_INVALID_ARGUMENT
+    assert L.mla_merge_shards(4, 2, fake + 4, fake, fake, fake, None) == mb.MLA_ERR_INVALID_ARGUMENT

@@ -357,3 +357,30 @@ def test_rejects_invalid():
     big = gen.random_inputs(129, [1], [2], False, seed=1)
     with pytest.raises(ValueError):
         run_oracle(big)
+
+
+def test_key_shards_merge_to_the_whole_sequence():
+    """Partials over arbitrary key ranges (the causal limit of the whole
+    sequence applied) merged with the log-sum-exp rule equal the direct
+    decode: a check of the partial path against the direct path.  The last
+    shard holds fewer keys than there are verify tokens, so some rows see
+    none of it (lse = -inf, O = 0, weight 0)."""
+    H, q, n = 3, 4, 70
+    inp = gen.random_inputs(H, [q], [n], False, seed=31)
+    inp = gen.peaked_inputs(inp, beta=10.0, seed=2)
+    ro, rl = oracle.mla_decode(inp.q_bits, inp.kv, inp.q_len, inp.kv_len, H)
+    cuts = [0, 17, 40, 68, n]
+    for i in range(q):
+        for h in range(H):
+            parts = [oracle.mla_partial(inp.q_bits, inp.kv, inp.q_len, inp.kv_len, H, 0, i, h, a, b)
+                     for a, b in zip(cuts[:-1], cuts[1:])]
+            lses = np.array([p[1] for p in parts])
+            last_visible = n - q + i
+            for (a, b), (o_w, l_w) in zip(zip(cuts[:-1], cuts[1:]), parts):
+                if a > last_visible:
+                    assert l_w == -np.inf and np.all(o_w == 0.0)
+            M = lses.max()
+            w = np.where(np.isfinite(lses), np.exp(lses - M), 0.0)
+            o = sum(wk * p[0] for wk, p in zip(w, parts)) / w.sum()
+            assert abs(M + np.log(w.sum()) - rl[i, h]) < 1e-12
+            assert np.max(np.abs(o - ro[i, h])) < 1e-12
