@@ -56,6 +56,28 @@ def to_device(inp):
     return q, kv
 
 
+class CacheFlush:
+    """Evicts L2 and the Infinity Cache between timed calls by streaming a
+    1 GiB buffer through them (more than the 8 x 4 MB L2 plus the 256 MB
+    Infinity Cache).  mode "read" sums the buffer into a scalar: the next
+    call reads its KV from HBM and finds no dirty lines to write back.
+    mode "write" rewrites the buffer instead, so the next call also pays for
+    writing back the dirty lines the flush left (up to the cache sizes)."""
+
+    def __init__(self, mode="read"):
+        import torch
+        self.mode = mode
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        self.sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        import torch
+        if self.mode == "read":
+            torch.sum(self.buf, dim=0, out=self.sink)
+        else:
+            self.buf.add_(1)
+
+
 def measure(inp, dev, steps, warmup, flush, **plan_opts):
     """Cold-cache timing of run + reduce.  Returns a stats dict (microseconds)."""
     import torch
@@ -71,14 +93,14 @@ def measure(inp, dev, steps, warmup, flush, **plan_opts):
         mb.mla_decode_reduce(plan, ws, o, lse, stream)
 
     for _ in range(warmup):
-        flush.add_(1)
+        flush()
         step()
     torch.cuda.synchronize()
     # the call: events only around run + reduce
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     t0 = time.perf_counter()
     for k in range(steps):
-        flush.add_(1)  # evict L2 / Infinity Cache (untimed: outside the events)
+        flush()  # evict L2 / Infinity Cache (untimed: outside the events)
         ev[k][0].record(stream)
         step()
         ev[k][1].record(stream)
@@ -88,7 +110,7 @@ def measure(inp, dev, steps, warmup, flush, **plan_opts):
     # breakdown: a middle event splits the main kernel from the merge
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for k in range(steps):
-        flush.add_(1)
+        flush()
         ev[k][0].record(stream)
         mb.mla_decode_run(plan, q, kv, inp.sm_scale, inp.kv_scale, o, lse, ws, ws.numel(), stream)
         ev[k][1].record(stream)
@@ -124,7 +146,7 @@ def kernel_source_sha256():
 def measured_traffic():
     """HBM bytes per main-kernel launch of the headline workload from the
     committed FETCH_SIZE / WRITE_SIZE counter summary (each counter calibrated
-    against the 1 GiB read+write flush kernel of the same run).  None when the
+    against the 1 GiB read + write reference kernel of the same run).  None when the
     summary is missing or was taken on a different kernel source."""
     try:
         with open(TRAFFIC_SUMMARY) as f:
@@ -191,7 +213,11 @@ def main():
     from mla_token_decode_amd import inputs as gen
 
     torch.cuda.set_device(0)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+    flush = CacheFlush("read")
+    # one 1 GiB read + 1 GiB write kernel: the known-size reference that the
+    # FETCH_SIZE / WRITE_SIZE counter summaries are calibrated against
+    flush.buf.add_(1)
+    torch.cuda.synchronize()
 
     log(f"generating {HEADLINE}")
     w = gen.workload(HEADLINE)
@@ -200,6 +226,10 @@ def main():
     log("timing headline")
     head = measure(inp, dev, args.steps, args.warmup, flush)
     log(f"  {head}")
+    dirty = None
+    if not args.quick:
+        dirty = measure(inp, dev, args.steps, args.warmup, CacheFlush("write"))["us_per_call"]
+        log(f"  after a dirtying flush: {dirty:.1f} us")
 
     per = {HEADLINE: head}
     if not args.quick:
@@ -258,7 +288,9 @@ def main():
                    "q": 8, "ctx": 1048576, "kv_dtype": "fp8_e4m3", "q_dtype": "bf16",
                    "kv_gbps": round(head["kv_gbps"], 1),
                    "frac_hbm_roofline": round(head["frac_hbm_peak"], 4),
-                   "timing": "cold cache (1 GiB rewrite between steps), HIP events, median"},
+                   "timing": "cold cache (1 GiB read between steps: no KV and no dirty lines "
+                             "left in L2 / Infinity Cache), HIP events, median",
+                   "us_per_call_after_dirty_flush": round(dirty, 2) if dirty else None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": (traffic["fetch"] + traffic["write"]) if traffic else None,

@@ -595,15 +595,21 @@ __device__ __forceinline__ void pv_phase(lds_u8* tile, const FragBases& fb,
 // P = 2^(c s - m_run) with c = sm_scale * kv_scale * log2(e) > 0; the first
 // tile that shows a row a key sets its reference, which moves only when a
 // tile maximum exceeds it by more than kLazyOctaves (then O and l are
-// rescaled: rare).  Split into kSoftSlices phases, each over all row tiles
-// (independent chains the scheduler can interleave), so that it can run
-// between MFMAs of the other phase.  The row maximum is taken on raw scores
+// rescaled: rare).  Whether any row of the wave needs that is decided from
+// each lane's own maximum over its 8 keys (a row's maximum exceeds a bound
+// exactly when one of its lanes' does), so the cross-lane row maximum is only
+// formed on that rare path (and on a row's first tile).  The work is cut into
+// small slices that run between the MFMAs of the other phase: the edge mask,
+// one lane-maximum slice per row tile, the wave vote, 4 slices of 2 keys per
+// row tile for P, and the row sums.  The maximum is taken on raw scores
 // (c > 0 keeps the order) and c is folded into one FMA per key.
-constexpr int kSoftSlices = 7;
+template <int NRT>
+constexpr int soft_slices() { return 5 * NRT + 3; }
 
 template <int NRT>
 struct SoftTile {
   float mx[NRT], nmu[NRT], psum[NRT];
+  bool jump;
 };
 
 template <int NRT, int PH>
@@ -613,6 +619,7 @@ __device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, f32x4 (&sfull)[2
                                               const int (&lim)[NRT], int k0, bool edge, float c,
                                               int g, lds_u8* spill) {
   if constexpr (PH == 0) {  // keys past a row's causal limit (last tiles of a chunk only)
+    w.jump = false;
     if (edge) {
       asm volatile("" ::: "memory");  // keep this a branch: interior tiles skip it
 #pragma unroll
@@ -625,53 +632,38 @@ __device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, f32x4 (&sfull)[2
             sfull[kt][rt][i] = key <= lim[rt] ? sfull[kt][rt][i] : -INFINITY;
           }
     }
-  } else if constexpr (PH == 1) {  // lane maximum over its 8 keys
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const f32x4 a = sfull[0][rt], b = sfull[1][rt];
-      w.mx[rt] = max2(max3(a[0], a[1], a[2]), max3(a[3], b[0], max3(b[1], b[2], b[3])));
-    }
-  } else if constexpr (PH == 2) {  // row maximum (the 4 lane groups), scaled
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) w.mx[rt] = wave_max_across_groups(w.mx[rt]) * c;
-  } else if constexpr (PH == 3) {  // reference; rare exact rescale
-    bool jump_any = false;
-    float m[NRT];
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      m[rt] = m_run[rt] == -INFINITY ? w.mx[rt] : m_run[rt];  // O and l are still 0 before
-      jump_any = jump_any || w.mx[rt] > m[rt] + kLazyOctaves;
-    }
-    if (__builtin_amdgcn_ballot_w64(jump_any) != 0) {  // wave-uniform, rare
+  } else if constexpr (PH <= NRT) {  // lane maximum over its 8 keys; does it pass the bound?
+    constexpr int rt = PH - 1;
+    const f32x4 a = sfull[0][rt], b = sfull[1][rt];
+    w.mx[rt] = max2(max3(a[0], a[1], a[2]), max3(a[3], b[0], max3(b[1], b[2], b[3])));
+    w.jump = w.jump || w.mx[rt] * c > m_run[rt] + kLazyOctaves;
+  } else if constexpr (PH == NRT + 1) {  // wave vote; rare: row maxima, references, rescale
+    if (__builtin_amdgcn_ballot_w64(w.jump) != 0) {  // wave-uniform
       asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // O MFMAs retired
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
-        const bool jump = w.mx[rt] > m[rt] + kLazyOctaves;
-        const float f = jump ? __builtin_amdgcn_exp2f(m[rt] - w.mx[rt]) : 1.0f;
-        m[rt] = jump ? w.mx[rt] : m[rt];
-        l_run[rt] *= f;
+        const float mx = wave_max_across_groups(w.mx[rt]) * c;
+        const bool first = m_run[rt] == -INFINITY;  // O and l are still 0
+        const bool jump = !first && mx > m_run[rt] + kLazyOctaves;
+        if (__builtin_amdgcn_ballot_w64(jump) != 0) {
+          const float f = jump ? __builtin_amdgcn_exp2f(m_run[rt] - mx) : 1.0f;
+          l_run[rt] *= f;
 #pragma unroll
-        for (int cc = 0; cc < 16; ++cc) scale_o(oacc[cc][rt], f, spill);
+          for (int cc = 0; cc < 16; ++cc) scale_o(oacc[cc][rt], f, spill);
+        }
+        m_run[rt] = (first && mx > -INFINITY) || jump ? mx : m_run[rt];
+        w.nmu[rt] = m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
       }
     }
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      m_run[rt] = m[rt];
-      w.nmu[rt] = m[rt] == -INFINITY ? 0.0f : -m[rt];
-    }
-  } else if constexpr (PH <= 5) {  // P of 4 keys per row tile: c s - m <= kLazyOctaves
-    constexpr int kt = PH - 4;
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)  // v_exp_f32: results below the fp32 normal range flush to 0
-        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sfull[kt][rt][i], c, w.nmu[rt]));
-      const float ps = (p[0] + p[1]) + (p[2] + p[3]);
-      w.psum[rt] = kt == 0 ? ps : w.psum[rt] + ps;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pf[rt][4 * kt + i] = (__bf16)p[i];
-    }
+  } else if constexpr (PH < 5 * NRT + 2) {  // P of 2 keys of one row tile: c s - m <= kLazyOctaves
+    constexpr int j = PH - (NRT + 2);
+    constexpr int rt = j / 4, kt = (j / 2) % 2, h = j % 2;
+    // v_exp_f32: results below the fp32 normal range flush to 0
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sfull[kt][rt][2 * h], c, w.nmu[rt]));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sfull[kt][rt][2 * h + 1], c, w.nmu[rt]));
+    w.psum[rt] = (j % 4 == 0) ? p0 + p1 : w.psum[rt] + (p0 + p1);
+    pf[rt][4 * kt + 2 * h] = (__bf16)p0;
+    pf[rt][4 * kt + 2 * h + 1] = (__bf16)p1;
   } else {
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) l_run[rt] += w.psum[rt];
@@ -772,6 +764,8 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
   VRaw vr[DV + 1];
   bf16x8 pf[NRT];
   SoftTile<NRT> sw;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) sw.nmu[rt] = 0.0f;  // references not set yet (m_run = -inf)
   for (int base = 0; base < u.ntiles; base += NS) {
     static_for<NS>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
@@ -806,7 +800,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         constexpr int kScoreMfma = 18 * NRT;
         score_phase<NRT, DH, DK>(slot_n, fb, qf, sacc, [&](auto ic) {
           constexpr int i = decltype(ic)::value;
-          slices_at<kSoftSlices, kScoreMfma, i>([&](auto sc) {
+          slices_at<soft_slices<NRT>(), kScoreMfma, i>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
             softmax_slice<NRT, s>(sw, sfull, pf, m_run, l_run, oacc, lim, k0, edge, us.scale_log2,
                                   g, spill);
