@@ -527,11 +527,11 @@ template <int NRT, bool FP8>
 constexpr int v_ahead() { return NRT == 1 ? 7 : NRT == 2 ? 4 : (FP8 ? 2 : 1); }
 
 // Score phase: S^T partial (this wave's 288 columns) of one tile; K fragments
-// DK steps ahead; slice(i) of the interleaved work runs after MFMA i.
-template <int NRT, int DH, int DK, typename W>
+// DK steps ahead; pre(i) runs before MFMA i and slice(i) after it.
+template <int NRT, int DH, int DK, typename P, typename W>
 __device__ __forceinline__ void score_phase(lds_u8* tile, const FragBases& fb,
                                             const bf16x8 (&qf)[NRT][9], f32x4 (&sacc)[2][NRT],
-                                            W&& slice) {
+                                            P&& pre, W&& slice) {
   bf16x8 kf[DK + 1][2];
   static_for<DK>([&](auto sc) {
     constexpr int j = decltype(sc)::value;
@@ -548,6 +548,7 @@ __device__ __forceinline__ void score_phase(lds_u8* tile, const FragBases& fb,
     static_for<2 * NRT>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       constexpr int kt = i / NRT, rt = i % NRT;
+      pre(std::integral_constant<int, j * 2 * NRT + i>{});
       mfma_s<j == 0, q_in_agpr<NRT>(rt, j)>(sacc[kt][rt], kf[cur][kt], qf[rt][j]);
       slice(std::integral_constant<int, j * 2 * NRT + i>{});
       __builtin_amdgcn_sched_barrier(0);
@@ -741,7 +742,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
 
   // full scores of tile 0
   f32x4 sacc[2][NRT], sfull[2][NRT];
-  score_phase<NRT, DH, DK>(lds, fb, qf, sacc, [](auto) {});
+  score_phase<NRT, DH, DK>(lds, fb, qf, sacc, [](auto) {}, [](auto) {});
   asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");  // score MFMAs retire before the reads
   {
     float* mine = xs + wave * kXsWave;
@@ -752,13 +753,13 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         *(f32x4*)(mine + ((rt * 2 + kt) * 64 + lane) * 4) = sacc[kt][rt];
   }
   lds_barrier();
-  {
+  {  // the partner's half of the scores; this wave's half is added in the loop
     const float* peer = xs + (wave ^ 1) * kXsWave;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
-        sfull[kt][rt] = sacc[kt][rt] + *(const f32x4*)(peer + ((rt * 2 + kt) * 64 + lane) * 4);
+        sfull[kt][rt] = *(const f32x4*)(peer + ((rt * 2 + kt) * 64 + lane) * 4);
   }
 
   VRaw vr[DV + 1];
@@ -796,11 +797,18 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
           }
         };
 
-        // scores of tile t + 1  ||  softmax of tile t (and the staging)
+        // scores of tile t + 1  ||  softmax of tile t (and the staging); before
+        // the first MFMAs overwrite this wave's half of tile t's scores, it is
+        // added to the partner's half read after the last barrier
         constexpr int kScoreMfma = 18 * NRT;
-        score_phase<NRT, DH, DK>(slot_n, fb, qf, sacc, [&](auto ic) {
+        constexpr int kAdd = 2 * NRT;  // MFMAs of the first step
+        auto add_own = [&](auto ic) {
           constexpr int i = decltype(ic)::value;
-          slices_at<soft_slices<NRT>(), kScoreMfma, i>([&](auto sc) {
+          if constexpr (i < kAdd) sfull[i / NRT][i % NRT] += sacc[i / NRT][i % NRT];
+        };
+        score_phase<NRT, DH, DK>(slot_n, fb, qf, sacc, add_own, [&](auto ic) {
+          constexpr int i = decltype(ic)::value;  // slices start once tile t's scores are whole
+          slices_at<soft_slices<NRT>(), kScoreMfma - kAdd + 1, i - kAdd + 1>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
             softmax_slice<NRT, s>(sw, sfull, pf, m_run, l_run, oacc, lim, k0, edge, us.scale_log2,
                                   g, spill);
@@ -827,8 +835,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
-            sfull[kt][rt] =
-                sacc[kt][rt] + *(const f32x4*)(peer + ((rt * 2 + kt) * 64 + lane) * 4);
+            sfull[kt][rt] = *(const f32x4*)(peer + ((rt * 2 + kt) * 64 + lane) * 4);
       }
     });
   }
