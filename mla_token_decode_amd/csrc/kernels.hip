@@ -903,14 +903,17 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_main(const MainArgs ar
     unit_body<FP8, NRT, 0>(args, smem);
 }
 
-// Split-KV merge.  One 256-thread block per (split output row, quarter of the
-// 512 value columns).  Lane (half p, column group cg) of wave w owns columns
-// 4 cg .. 4 cg + 3 of the quarter and folds chunks s = 8 i + (2 w + p) in
-// ascending order; the 8 partial sums are then added in a fixed order through
-// LDS, so replays are bitwise identical.
+// Split-KV merge.  One 256-thread block per (split output row, 64 of the 512
+// value columns).  Thread (part p, column group cg) owns columns
+// 4 cg .. 4 cg + 3 of the block and folds chunks s = 16 i + p in ascending
+// order (8 loads in flight per thread: eight blocks per row keep enough bytes
+// moving per CU); the 16 partial sums are then added in a fixed order through
+// LDS, so replays are bitwise identical.  A chunk that shows the row no key
+// has LSE = -inf and weight 0 (its O is 0).
 constexpr int kRedThreads = 256;
-constexpr int kRedParts = 2 * kRedThreads / 64;  // (wave, lane half) partial sums
-constexpr int kRedCols = 128;                     // value columns per block
+constexpr int kRedCols = 64;                         // value columns per block
+constexpr int kRedGroups = kRedCols / 4;             // 4-column groups
+constexpr int kRedParts = kRedThreads / kRedGroups;  // partial sums per block
 
 __device__ __forceinline__ float wave_max64(float v) {
   v = wave_max_across_groups(v);          // lanes l, l^16, l^32, l^48
@@ -919,11 +922,36 @@ __device__ __forceinline__ float wave_max64(float v) {
   return v;
 }
 
+__device__ __forceinline__ float merge_weight(float ls, float M) {
+  return ls == -INFINITY ? 0.0f : __expf(ls - M);
+}
+
+// Sums of the per-part folds in part order; writes 4 bf16 columns and the LSE.
+__device__ __forceinline__ void merge_finish(f32x4 (&red_acc)[kRedParts][kRedGroups],
+                                             float (&red_w)[kRedParts], int cg, float M,
+                                             uint16_t* o_row, float* lse_row, bool lse_writer) {
+  f32x4 tot = red_acc[0][cg];
+  float Wt = red_w[0];
+#pragma unroll
+  for (int k = 1; k < kRedParts; ++k) {
+    tot += red_acc[k][cg];
+    Wt += red_w[k];
+  }
+  const bool empty = !(Wt > 0.0f);  // no chunk or shard shows this row a key
+  const float inv = empty ? 0.0f : 1.0f / Wt;
+  uint2 pk;
+  pk.x = pack_bf16x2(tot[0] * inv, tot[1] * inv);
+  pk.y = pack_bf16x2(tot[2] * inv, tot[3] * inv);
+  *(uint2*)(o_row + 4 * cg) = pk;
+  if (lse_writer) *lse_row = empty ? -INFINITY : M + __logf(Wt);
+}
+
 __global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_kernel(const ReduceArgs args) {
-  __shared__ f32x4 red_acc[kRedParts][32];
+  __shared__ f32x4 red_acc[kRedParts][kRedGroups];
   __shared__ float red_w[kRedParts];
-  const int gr = blockIdx.x >> 2;
-  const int quarter = blockIdx.x & 3;
+  constexpr int kBlocksPerRow = kDv / kRedCols;
+  const int gr = blockIdx.x / kBlocksPerRow;
+  const int cb = blockIdx.x % kBlocksPerRow;
   if (gr >= args.num_rows) return;
   int b = 0;
   while (b + 1 < args.num_seqs && args.row0[b + 1] <= gr) ++b;
@@ -934,10 +962,9 @@ __global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_kernel(const Re
   const int r = local % R;
   const int S = sd.S;
   const int64_t pbase = (int64_t)sd.part_row0 + (int64_t)t * S * R + r;
-  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int part = 2 * wave + (lane >> 5);
-  const int cg = lane & 31;
+  const int part = threadIdx.x / kRedGroups;
+  const int cg = threadIdx.x % kRedGroups;
 
   float M = -INFINITY;
   for (int s = lane; s < S; s += 64) M = fmaxf(M, args.part_lse[pbase + (int64_t)s * R]);
@@ -945,54 +972,39 @@ __global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_kernel(const Re
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.0f;
-  const float* po = args.part_o + kRedCols * quarter + 4 * cg;
-#pragma unroll 4
+  const float* po = args.part_o + kRedCols * cb + 4 * cg;
+#pragma unroll 8
   for (int s = part; s < S; s += kRedParts) {
     const int64_t prow = pbase + (int64_t)s * R;
-    const float ls = args.part_lse[prow];
-    if (ls == -INFINITY) continue;  // a chunk this row cannot see: weight 0
-    const float w = __expf(ls - M);
+    const f32x4 v = *(const f32x4*)(po + prow * kDv);
+    const float w = merge_weight(args.part_lse[prow], M);
     W += w;
-    acc += w * *(const f32x4*)(po + prow * kDv);
+    acc += w * v;
   }
   red_acc[part][cg] = acc;
   if (cg == 0) red_w[part] = W;
   __syncthreads();
-  if (threadIdx.x >= 32) return;
-  f32x4 tot = red_acc[0][cg];
-  float Wt = red_w[0];
-#pragma unroll
-  for (int k = 1; k < kRedParts; ++k) {
-    tot += red_acc[k][cg];
-    Wt += red_w[k];
-  }
-  const bool empty = !(Wt > 0.0f);  // no chunk shows this row a key (key shards only)
-  const float inv = empty ? 0.0f : 1.0f / Wt;
+  if (threadIdx.x >= kRedGroups) return;
   const int64_t orow = (int64_t)sd.q_row0 + (int64_t)t * R + r;
-  uint2 pk;
-  pk.x = pack_bf16x2(tot[0] * inv, tot[1] * inv);
-  pk.y = pack_bf16x2(tot[2] * inv, tot[3] * inv);
-  *(uint2*)(args.o + orow * kDv + kRedCols * quarter + 4 * cg) = pk;
-  if (quarter == 0 && cg == 0) args.lse[orow] = empty ? -INFINITY : M + __logf(Wt);
+  merge_finish(red_acc, red_w, cg, M, args.o + orow * kDv + kRedCols * cb, args.lse + orow,
+               cb == 0 && cg == 0);
 }
 
-// Combination of per-shard results (bf16 O, fp32 LSE), same arithmetic and
-// fixed order as the split-KV merge: one 256-thread block per (row, quarter of
-// the columns); lane (half p, column group cg) of wave w folds shards
-// s = 8 i + (2 w + p) in ascending order, then the 8 partial sums are added
-// in order through LDS.
+// Combination of per-shard results (bf16 O, fp32 LSE) with the layout and the
+// fixed order of the split-KV merge above (shards in place of chunks); a
+// shard whose LSE is -inf is skipped without reading its O.
 __global__ __launch_bounds__(kRedThreads) void mla_merge_shards_kernel(const MergeArgs args) {
-  __shared__ f32x4 red_acc[kRedParts][32];
+  __shared__ f32x4 red_acc[kRedParts][kRedGroups];
   __shared__ float red_w[kRedParts];
-  const int row = blockIdx.x >> 2;
-  const int quarter = blockIdx.x & 3;
+  constexpr int kBlocksPerRow = kDv / kRedCols;
+  const int row = blockIdx.x / kBlocksPerRow;
+  const int cb = blockIdx.x % kBlocksPerRow;
   if (row >= args.num_rows) return;
   const int W = args.num_shards;
   const int64_t rows = args.num_rows;
-  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int part = 2 * wave + (lane >> 5);
-  const int cg = lane & 31;
+  const int part = threadIdx.x / kRedGroups;
+  const int cg = threadIdx.x % kRedGroups;
 
   float M = -INFINITY;
   for (int s = lane; s < W; s += 64) M = fmaxf(M, args.lse_shards[s * rows + row]);
@@ -1000,35 +1012,23 @@ __global__ __launch_bounds__(kRedThreads) void mla_merge_shards_kernel(const Mer
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float Wsum = 0.0f;
-  const uint16_t* po = args.o_shards + kRedCols * quarter + 4 * cg;
+  const uint16_t* po = args.o_shards + kRedCols * cb + 4 * cg;
   for (int s = part; s < W; s += kRedParts) {
     const float ls = args.lse_shards[s * rows + row];
-    if (ls == -INFINITY) continue;
-    const float w = __expf(ls - M);
-    Wsum += w;
+    if (ls == -INFINITY) continue;  // a shard that shows the row no key: its O is not read
     const uint2 pk = *(const uint2*)(po + (s * rows + row) * kDv);
     const f32x4 v = {__builtin_bit_cast(float, pk.x << 16), __builtin_bit_cast(float, pk.x & 0xffff0000u),
                      __builtin_bit_cast(float, pk.y << 16), __builtin_bit_cast(float, pk.y & 0xffff0000u)};
+    const float w = __expf(ls - M);
+    Wsum += w;
     acc += w * v;
   }
   red_acc[part][cg] = acc;
   if (cg == 0) red_w[part] = Wsum;
   __syncthreads();
-  if (threadIdx.x >= 32) return;
-  f32x4 tot = red_acc[0][cg];
-  float Wt = red_w[0];
-#pragma unroll
-  for (int k = 1; k < kRedParts; ++k) {
-    tot += red_acc[k][cg];
-    Wt += red_w[k];
-  }
-  const bool empty = !(Wt > 0.0f);
-  const float inv = empty ? 0.0f : 1.0f / Wt;
-  uint2 pk;
-  pk.x = pack_bf16x2(tot[0] * inv, tot[1] * inv);
-  pk.y = pack_bf16x2(tot[2] * inv, tot[3] * inv);
-  *(uint2*)(args.o + (int64_t)row * kDv + kRedCols * quarter + 4 * cg) = pk;
-  if (quarter == 0 && cg == 0) args.lse[row] = empty ? -INFINITY : M + __logf(Wt);
+  if (threadIdx.x >= kRedGroups) return;
+  merge_finish(red_acc, red_w, cg, M, args.o + (int64_t)row * kDv + kRedCols * cb, args.lse + row,
+               cb == 0 && cg == 0);
 }
 
 // ------------------------------------------------------------- launchers
