@@ -654,6 +654,9 @@ __device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, f32x4 (&sfull)[2
         }
         m_run[rt] = (first && mx > -INFINITY) || jump ? mx : m_run[rt];
         w.nmu[rt] = m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
+        // settle both here: merged after the branch they would be selected on
+        // every tile
+        asm volatile("" : "+v"(m_run[rt]), "+v"(w.nmu[rt]));
       }
     }
   } else if constexpr (PH < 5 * NRT + 2) {  // P of 2 keys of one row tile: c s - m <= kLazyOctaves
