@@ -75,6 +75,8 @@ typedef enum {
 #define MLA_MAX_TILE_ROWS 128 /* H * F must not exceed this */
 #define MLA_KV_GRANULE 64    /* split-KV chunk lengths are multiples of this */
 #define MLA_MAX_SHARDS 1024  /* most shards mla_merge_shards combines */
+#define MLA_MIN_PAGE_SIZE 32 /* paged KV: smallest page (keys); sizes are powers of two */
+#define MLA_MAX_PAGE_SIZE (1 << 20) /* paged KV: largest page (keys) */
 
 typedef struct mla_plan mla_plan; /* opaque, host-owned */
 
@@ -146,6 +148,33 @@ mla_status mla_decode_plan_shard(int32_t batch, int32_t num_heads, const int32_t
 mla_status mla_decode_run(const mla_plan* plan, const void* q, const void* kv, float sm_scale,
                           float kv_scale, void* o, float* lse, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* mla_decode_run over a paged KV cache: the serving layout, in which a page
+ * table maps each sequence's key positions to pages of a shared pool (the
+ * Kimi-K3 MLA FP8 "paged attention route" whose description is embedded in
+ * flashinfer PR #5588: section "Summary", and section "Tests", which replays
+ * with a changed page table).  Same plan, same arguments and same results as
+ * mla_decode_run on the gathered KV; only where the rows are read changes.
+ *  kv_pages: device pool [num_pages, page_size, 576] of the plan's dtype,
+ *       16-byte aligned; num_pages >= 1.
+ *  page_size: keys per page, a power of two in [MLA_MIN_PAGE_SIZE,
+ *       MLA_MAX_PAGE_SIZE] (else UNSUPPORTED), so that a 32-key kernel tile
+ *       never crosses a page.
+ *  page_table: device int32 [batch, page_table_stride], 4-byte aligned; key
+ *       j of sequence b lives in row j mod page_size of page
+ *       page_table[b * page_table_stride + j / page_size].  page_table_stride
+ *       must cover the longest sequence (>= ceil(kv_len / page_size)).  The
+ *       table is read on the device when the kernels run, so one plan serves
+ *       any number of tables; entries are clamped to [0, num_pages - 1], so a
+ *       wrong entry reads a wrong page of the pool, never outside it.
+ * The caller keeps the pool and the table unchanged until the kernels have
+ * run.  Errors: those of mla_decode_run, plus UNSUPPORTED for the page size
+ * and INVALID_ARGUMENT for num_pages, the table pointer or its stride. */
+mla_status mla_decode_run_paged(const mla_plan* plan, const void* q, const void* kv_pages,
+                                int32_t num_pages, int32_t page_size, const int32_t* page_table,
+                                int32_t page_table_stride, float sm_scale, float kv_scale, void* o,
+                                float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Enqueue the split-KV merge on `stream`: for every split tile row, in
  * ascending chunk order, M = max_s lse_s, lse = M + ln sum_s exp(lse_s - M),

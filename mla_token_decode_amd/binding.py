@@ -27,9 +27,9 @@ KV_GRANULE = 64
 
 MAX_SHARDS = 1024
 
-EXPORTED = ["mla_decode_plan", "mla_decode_plan_shard", "mla_decode_run", "mla_decode_reduce",
-            "mla_merge_shards", "mla_plan_destroy", "mla_last_error", "mla_plan_query",
-            "mla_plan_info"]
+EXPORTED = ["mla_decode_plan", "mla_decode_plan_shard", "mla_decode_run", "mla_decode_run_paged",
+            "mla_decode_reduce", "mla_merge_shards", "mla_plan_destroy", "mla_last_error",
+            "mla_plan_query", "mla_plan_info"]
 
 _lock = threading.Lock()
 _lib = None
@@ -75,6 +75,12 @@ def lib() -> ctypes.CDLL:
                                      ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p]
         L.mla_decode_run.restype = ctypes.c_int
+        L.mla_decode_run_paged.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_size_t, ctypes.c_void_p]
+        L.mla_decode_run_paged.restype = ctypes.c_int
         L.mla_decode_reduce.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p]
         L.mla_decode_reduce.restype = ctypes.c_int
@@ -193,6 +199,25 @@ def mla_decode_run(plan: Plan, q, kv, sm_scale: float, kv_scale: float, o, lse, 
     _check(lib().mla_decode_run(plan.handle, _ptr(q), _ptr(kv), float(sm_scale), float(kv_scale),
                                 _ptr(o), _ptr(lse), _ptr(workspace), int(workspace_bytes),
                                 _stream(stream)))
+
+
+def mla_decode_run_paged(plan: Plan, q, kv_pages, page_table, sm_scale: float, kv_scale: float, o,
+                         lse, workspace=None, workspace_bytes=None, stream=None):
+    """kv_pages: [num_pages, page_size, 576] pool (bf16, or uint8 e4m3 codes);
+    page_table: int32 [batch, stride] page indices (key j of sequence b is row
+    j % page_size of page page_table[b, j // page_size])."""
+    if kv_pages.dim() != 3 or int(kv_pages.shape[2]) != DQK:
+        raise ValueError("kv_pages must be [num_pages, page_size, 576]")
+    if page_table.dim() != 2 or not page_table.is_contiguous() or str(page_table.dtype) != "torch.int32":
+        raise ValueError("page_table must be a contiguous [batch, stride] int32 tensor")
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else (
+            workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0)
+    _check(lib().mla_decode_run_paged(plan.handle, _ptr(q), _ptr(kv_pages), int(kv_pages.shape[0]),
+                                      int(kv_pages.shape[1]), _ptr(page_table),
+                                      int(page_table.shape[1]), float(sm_scale), float(kv_scale),
+                                      _ptr(o), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+                                      _stream(stream)))
 
 
 def mla_decode_reduce(plan: Plan, workspace, o, lse, stream=None):

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmla_decode.so")
-SOURCES = ["api.cpp", "plan.cpp", "kernels.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "kernels_paged.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
@@ -28,11 +28,26 @@ def compile_flags():
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, *compile_flags(), "-shared", "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    """Compile every source to an object in parallel (the two kernel files are
+    the long ones), then link the shared library."""
+    import tempfile
+    with tempfile.TemporaryDirectory(prefix="mla_build_") as tmpdir:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src + ".o")
+            cmd = [HIPCC, *compile_flags(), "-c", "-o", obj, os.path.join(CSRC, src)]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            objs.append(obj)
+            procs.append((cmd, subprocess.Popen(cmd)))
+        for cmd, p in procs:
+            if p.wait() != 0:
+                raise subprocess.CalledProcessError(p.returncode, cmd)
+        tmp = LIB + f".tmp{os.getpid()}"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB
 

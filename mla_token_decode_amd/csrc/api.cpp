@@ -2,6 +2,7 @@
 // launches.  See include/mla_decode.h for the contract of each call.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -12,7 +13,8 @@
 
 namespace mla {
 const char* last_error();
-hipError_t launch_main(const MainArgs& a, bool fp8, int nrt, hipStream_t stream);
+hipError_t launch_main_contiguous(const MainArgs& a, bool fp8, int nrt, hipStream_t stream);
+hipError_t launch_main_paged(const MainArgs& a, bool fp8, int nrt, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
@@ -151,9 +153,14 @@ mla_status mla_plan_info(const mla_plan* plan, int32_t* num_units, int32_t* num_
   return MLA_OK;
 }
 
-mla_status mla_decode_run(const mla_plan* plan, const void* q, const void* kv, float sm_scale,
-                          float kv_scale, void* o, float* lse, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+namespace {
+
+// Shared by the contiguous and the paged entry points: `kv` is the KV array or
+// the page pool; `page_table` is null for contiguous KV.
+mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const int32_t* page_table,
+                      int32_t pt_stride, int32_t page_shift, int32_t num_pages, float sm_scale,
+                      float kv_scale, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   if (!plan) {
     set_error("plan must be non-null");
     return MLA_ERR_INVALID_ARGUMENT;
@@ -204,19 +211,70 @@ mla_status mla_decode_run(const mla_plan* plan, const void* q, const void* kv, f
   const double log2e = 1.4426950408889634;
   a.scale_log2 = static_cast<float>(static_cast<double>(sm_scale) * (fp8 ? kv_scale : 1.0) * log2e);
   a.o_scale = fp8 ? kv_scale : 1.0f;
+  a.pt_stride = pt_stride;
+  a.page_shift = page_shift;
+  a.num_pages = num_pages;
   a.H = plan->H;
   for (const Launch& ln : plan->launches) {
     a.num_seqs = ln.seq_end - ln.seq_begin;
     a.num_units = ln.num_units;
     a.units_per_xcd = (ln.num_units + kNumXcd - 1) / kNumXcd;
+    // page-table rows of this launch's sequences (the kernel indexes them from 0)
+    a.page_table = page_table ? page_table + static_cast<int64_t>(ln.seq_begin) * pt_stride : nullptr;
     for (int b = ln.seq_begin; b < ln.seq_end; ++b) a.seqs[b - ln.seq_begin] = plan->seqs[b];
-    hipError_t e = launch_main(a, fp8, ln.nrt, static_cast<hipStream_t>(stream));
+    hipError_t e = page_table ? launch_main_paged(a, fp8, ln.nrt, static_cast<hipStream_t>(stream))
+                              : launch_main_contiguous(a, fp8, ln.nrt, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
       set_error("main kernel launch failed: %s", hipGetErrorString(e));
       return MLA_ERR_DEVICE;
     }
   }
   return MLA_OK;
+}
+
+}  // namespace
+
+mla_status mla_decode_run(const mla_plan* plan, const void* q, const void* kv, float sm_scale,
+                          float kv_scale, void* o, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return run_common(plan, q, kv, nullptr, 0, 0, 0, sm_scale, kv_scale, o, lse, workspace,
+                    workspace_bytes, stream);
+}
+
+mla_status mla_decode_run_paged(const mla_plan* plan, const void* q, const void* kv_pages,
+                                int32_t num_pages, int32_t page_size, const int32_t* page_table,
+                                int32_t page_table_stride, float sm_scale, float kv_scale, void* o,
+                                float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (!plan) {
+    set_error("plan must be non-null");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (page_size < MLA_MIN_PAGE_SIZE || page_size > MLA_MAX_PAGE_SIZE ||
+      (page_size & (page_size - 1)) != 0) {
+    set_error("page_size %d is not supported: pages hold a power of two from %d to %d keys",
+              page_size, MLA_MIN_PAGE_SIZE, MLA_MAX_PAGE_SIZE);
+    return MLA_ERR_UNSUPPORTED;
+  }
+  if (num_pages < 1) {
+    set_error("num_pages must be >= 1 (got %d)", num_pages);
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (!page_table || reinterpret_cast<uintptr_t>(page_table) % 4 != 0) {
+    set_error("page_table must be a non-null, 4-byte aligned device pointer");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  int64_t need = 1;
+  for (const SeqDesc& d : plan->seqs) need = std::max<int64_t>(need, (d.n + page_size - 1) / page_size);
+  if (page_table_stride < need) {
+    set_error("page_table_stride %d is smaller than the %lld pages of the longest sequence",
+              page_table_stride, static_cast<long long>(need));
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  return run_common(plan, q, kv_pages, page_table, page_table_stride, shift, num_pages, sm_scale,
+                    kv_scale, o, lse, workspace, workspace_bytes, stream);
 }
 
 mla_status mla_decode_reduce(const mla_plan* plan, const void* workspace, void* o, float* lse,

@@ -172,15 +172,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* kv_un
   return make_rsrc(kv_unit + (int64_t)t * kTK * RB, (uint32_t)(rows * RB));
 }
 
-// Issue the global load of piece M of compute tile `t` into a staging set.
-// The loads are inline assembly so that their completion is waited for
-// explicitly (wait_stage): the compiler's own counting drains every set in
-// flight at the loop head.
+// Issue the global load of piece M of a compute tile (descriptor r) into a
+// staging set.  The loads are inline assembly so that their completion is
+// waited for explicitly (wait_stage): the compiler's own counting drains every
+// set in flight at the loop head.
 template <bool FP8, int M>
-__device__ __forceinline__ void stage_load_piece(Stage<FP8>& st, const uint8_t* kv_unit, int t,
-                                                 int nkeys, int tid) {
+__device__ __forceinline__ void stage_load_piece(Stage<FP8>& st, __amdgpu_buffer_rsrc_t r, int tid) {
   constexpr int PB = FP8 ? 8 : 16;  // bytes per piece
-  const __amdgpu_buffer_rsrc_t r = tile_rsrc<FP8>(kv_unit, t, nkeys);
   const int off = tid * PB;
   const int soff = kThreads * PB * M;
   if constexpr (FP8)
@@ -192,12 +190,58 @@ __device__ __forceinline__ void stage_load_piece(Stage<FP8>& st, const uint8_t* 
 }
 
 template <bool FP8>
-__device__ __forceinline__ void stage_load(Stage<FP8>& st, const uint8_t* kv_unit, int t, int nkeys,
-                                           int tid) {
-  static_for<kPieces>([&](auto mc) {
-    stage_load_piece<FP8, decltype(mc)::value>(st, kv_unit, t, nkeys, tid);
-  });
+__device__ __forceinline__ void stage_load(Stage<FP8>& st, __amdgpu_buffer_rsrc_t r, int tid) {
+  static_for<kPieces>([&](auto mc) { stage_load_piece<FP8, decltype(mc)::value>(st, r, tid); });
 }
+
+// Where a unit's KV tiles live: one contiguous run of rows, or the pages of a
+// pool listed in a page table (pages hold 2^shift >= 32 keys and tiles start
+// at multiples of 32 keys, so a tile never crosses a page).
+template <bool FP8, bool PAGED>
+struct KvSource {
+  static constexpr int RB = Stage<FP8>::kGlobalRowBytes;
+  const uint8_t* base;    // contiguous: first row of the chunk; paged: the pool
+  const int32_t* pt_row;  // paged: the sequence's page-table row
+  int lo;                 // first key of the chunk (sequence-relative)
+  int nkeys, shift, last_idx;
+  unsigned max_page;
+
+  // Page-table entry of tile t (tiles past the end reuse the last entry).
+  __device__ __forceinline__ int page_idx(int t) const {
+    return min((lo + kTK * t) >> shift, last_idx);
+  }
+  // First pool row of a page-table entry's page (entries are clamped to the pool).
+  __device__ __forceinline__ int64_t page_row(int entry) const {
+    return (int64_t)min((unsigned)entry, max_page) << shift;
+  }
+  // Page row of tile t, waited for here (prologue only).
+  __device__ __forceinline__ int64_t page_row_now(int t) const {
+    int e;
+    asm volatile("s_load_dword %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+                 : "=s"(e) : "s"(pt_row), "s"(4 * page_idx(t)) : "memory");
+    return page_row(e);
+  }
+  // The tile barrier (LDS traffic drained, then s_barrier) with the page row of
+  // tile t fetched under the same wait.
+  __device__ __forceinline__ int64_t barrier_and_page_row(int t) const {
+    int e;
+    asm volatile("s_load_dword %0, %1, %2\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
+                 : "=s"(e) : "s"(pt_row), "s"(4 * page_idx(t)) : "memory");
+    return page_row(e);
+  }
+  // Descriptor of tile t (keys [lo + 32 t, lo + 32 t + 32) of the sequence):
+  // rows past the chunk read as zero, tiles past the end read nothing.
+  // `prow` is the page row of tile t (paged only).
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(int t, int64_t prow) const {
+    if constexpr (!PAGED) {
+      return tile_rsrc<FP8>(base, t, nkeys);
+    } else {
+      const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kTK, nkeys - t * kTK)));
+      const int64_t row = prow + ((lo + kTK * t) & ((1 << shift) - 1));
+      return make_rsrc(base + row * RB, (uint32_t)(rows * RB));
+    }
+  }
+};
 
 // Wait until at most N global loads issued after this set's are outstanding
 // (vector memory loads complete in order); the set's registers are tied to the
@@ -386,7 +430,9 @@ struct UnitSetup {
   int t, s, R, H, S, rowb0, RU, row0, tail0, hi_eff, part_row0;
   float scale_log2, o_scale;
   const uint16_t* q;
-  const uint8_t* kv_unit;  // first KV row of the unit's chunk
+  const uint8_t* kv_unit;  // contiguous KV: first row of the unit's chunk; paged: the pool
+  const int32_t* pt_row;   // paged KV: the sequence's page-table row (null: contiguous)
+  int page_shift, last_page_idx, num_pages;
   uint16_t* o;
   float* lse;
   float* part_lse;
@@ -429,8 +475,30 @@ __device__ __forceinline__ bool unit_setup(const MainArgs& args, UnitSetup& us) 
   us.uc.nkeys = us.hi_eff - us.uc.lo;              // may be <= 0 (chunk hidden from every row)
   us.uc.ntiles = us.uc.nkeys > 0 ? (us.uc.nkeys + kTK - 1) / kTK : 0;
   us.uc.min_lim = min(us.hi_eff - 1, vis_lo) - us.uc.lo;  // every row sees keys <= this
-  us.kv_unit = args.kv + ((int64_t)sd.kv_row0 + us.uc.lo) * Stage<FP8>::kGlobalRowBytes;
+  if (args.page_table == nullptr) {
+    us.pt_row = nullptr;
+    us.kv_unit = args.kv + ((int64_t)sd.kv_row0 + us.uc.lo) * Stage<FP8>::kGlobalRowBytes;
+  } else {
+    us.pt_row = args.page_table + (int64_t)b * args.pt_stride;
+    us.kv_unit = args.kv;
+    us.page_shift = args.page_shift;
+    us.last_page_idx = (sd.n - 1) >> args.page_shift;
+    us.num_pages = args.num_pages;
+  }
   return true;
+}
+
+template <bool FP8, bool PAGED>
+__device__ __forceinline__ KvSource<FP8, PAGED> kv_source(const UnitSetup& us) {
+  KvSource<FP8, PAGED> src;
+  src.base = us.kv_unit;
+  src.pt_row = us.pt_row;
+  src.lo = us.uc.lo;
+  src.nkeys = us.uc.nkeys;
+  src.shift = PAGED ? us.page_shift : 0;
+  src.last_idx = PAGED ? us.last_page_idx : 0;
+  src.max_page = PAGED ? (unsigned)(us.num_pages - 1) : 0u;
+  return src;
 }
 
 // One Q fragment (MFMA B operand) straight from memory into its register file.
@@ -677,24 +745,34 @@ __device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, f32x4 (&sfull)[2
 // A row group with no row of the unit only takes its share of the staging
 // (same loads, stores and barriers as unit_pipeline, no LDS reads, no MFMAs).
 // It is a separate loop, so its staged registers never meet the other's.
-template <bool FP8, int NRT>
+// Page rows of tiles 0 .. N-1 (paged KV; prologue).
+template <int N, bool FP8, bool PAGED>
+__device__ __forceinline__ void prologue_page_rows(const KvSource<FP8, PAGED>& src, int64_t (&pr)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) pr[k] = PAGED ? src.page_row_now(k) : 0;
+}
+
+template <bool FP8, int NRT, bool PAGED>
 __device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* lds, int tid) {
   constexpr int NS = stage_sets<FP8, NRT>();
   constexpr int kAhead = (NS - 1) * kPieces;
   const UnitCtx u = us.uc;
-  const uint8_t* kv = us.kv_unit;
+  const KvSource<FP8, PAGED> src = kv_source<FP8, PAGED>(us);
   if (u.ntiles <= 0) return;
+  int64_t pr[NS + 3];
+  prologue_page_rows(src, pr);
   Stage<FP8> st[NS];
 #pragma unroll
-  for (int k = 0; k < NS; ++k) stage_load<FP8>(st[k], kv, k, u.nkeys, tid);
+  for (int k = 0; k < NS; ++k) stage_load<FP8>(st[k], src.rsrc(k, pr[k]), tid);
   static_for<2>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     wait_stage<kAhead, FP8>(st[j % NS]);
     stage_store<FP8>(st[j % NS], lds + j * kTileBytes, tid);
-    stage_load<FP8>(st[j % NS], kv, j + NS, u.nkeys, tid);
+    stage_load<FP8>(st[j % NS], src.rsrc(j + NS, pr[j + NS]), tid);
   });
   lds_barrier();
   lds_barrier();  // the exchange of tile 0's scores
+  int64_t prow_next = pr[NS + 2];  // page row of the first tile the loop loads
   for (int base = 0; base < u.ntiles; base += NS) {
     static_for<NS>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
@@ -703,8 +781,11 @@ __device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* l
       if (t < u.ntiles) {
         wait_stage<kAhead, FP8>(st[ks]);
         stage_store<FP8>(st[ks], lds + ((t + 2) % kRing) * kTileBytes, tid);
-        stage_load<FP8>(st[ks], kv, t + 2 + NS, u.nkeys, tid);
-        lds_barrier();
+        stage_load<FP8>(st[ks], src.rsrc(t + 2 + NS, prow_next), tid);
+        if constexpr (PAGED)
+          prow_next = src.barrier_and_page_row(t + 3 + NS);
+        else
+          lds_barrier();
       }
     });
   }
@@ -717,7 +798,7 @@ __device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* l
 // past the end load nothing), so the staged registers never need a copy while
 // their loads are in flight (the compiler does not know that an
 // inline-assembly load completes later).
-template <bool FP8, int NRT, int DH>
+template <bool FP8, int NRT, int DH, bool PAGED>
 __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, float* xs,
                                               int wave, const FragBases& fb,
                                               const bf16x8 (&qf)[NRT][9], f32x4 (&oacc)[16][NRT],
@@ -728,20 +809,23 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
   constexpr int kXsWave = NRT * 2 * 256;      // floats of one wave's partial scores
   constexpr int DK = k_ahead<NRT, FP8>(), DV = v_ahead<NRT, FP8>();
   const UnitCtx u = us.uc;
-  const uint8_t* kv = us.kv_unit;
+  const KvSource<FP8, PAGED> src = kv_source<FP8, PAGED>(us);
   if (u.ntiles <= 0) return;
 
   // prologue: tiles 0 and 1 into their slots; tile k always travels in set k % NS
+  int64_t pr[NS + 3];
+  prologue_page_rows(src, pr);
   Stage<FP8> st[NS];
 #pragma unroll
-  for (int k = 0; k < NS; ++k) stage_load<FP8>(st[k], kv, k, u.nkeys, tid);
+  for (int k = 0; k < NS; ++k) stage_load<FP8>(st[k], src.rsrc(k, pr[k]), tid);
   static_for<2>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     wait_stage<kAhead, FP8>(st[j % NS]);
     stage_store<FP8>(st[j % NS], lds + j * kTileBytes, tid);
-    stage_load<FP8>(st[j % NS], kv, j + NS, u.nkeys, tid);
+    stage_load<FP8>(st[j % NS], src.rsrc(j + NS, pr[j + NS]), tid);
   });
   lds_barrier();
+  int64_t prow_next = pr[NS + 2];  // page row of the first tile the loop loads
 
   // full scores of tile 0
   f32x4 sacc[2][NRT], sfull[2][NRT];
@@ -785,6 +869,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         lds_u8* slot_s = lds + ((t + 2) % kRing) * kTileBytes;
         const int k0 = t * kTK;
         const bool edge = k0 + kTK - 1 > u.min_lim;
+        const __amdgpu_buffer_rsrc_t rs_next = src.rsrc(t + 2 + NS, prow_next);
         issue_v_head<DH, DV>(vr, slot_t, fb);
 
         // staging of tile t + 2: wait for its loads, LDS store, next loads
@@ -796,7 +881,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
           } else if constexpr (s < 1 + kPieces) {
             stage_store_piece<FP8, s - 1>(st[ks], slot_s, tid);
           } else {
-            stage_load_piece<FP8, s - 1 - kPieces>(st[ks], kv, t + 2 + NS, u.nkeys, tid);
+            stage_load_piece<FP8, s - 1 - kPieces>(st[ks], rs_next, tid);
           }
         };
 
@@ -833,7 +918,10 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
           if constexpr (!kStageWithScores) slices_at<kStageSlices, kPvMfma, i>(stage_slice);
         });
 
-        lds_barrier();
+        if constexpr (PAGED)
+          prow_next = src.barrier_and_page_row(t + 3 + NS);
+        else
+          lds_barrier();
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
@@ -845,7 +933,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads issued past the end
 }
 
-template <bool FP8, int NRT, int DH>
+template <bool FP8, int NRT, int DH, bool PAGED>
 __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* smem) {
   UnitSetup us;
   if (!unit_setup<FP8>(args, us)) return;
@@ -885,10 +973,10 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
     for (int rt = 0; rt < NRT; ++rt) zero_o(oacc[c][rt]);
 
   if (!wave_active) {
-    unit_staging_only<FP8, NRT>(us, lds, tid);
+    unit_staging_only<FP8, NRT, PAGED>(us, lds, tid);
     return;
   }
-  unit_pipeline<FP8, NRT, DH>(us, lds, xs, wave, fb, qf, oacc, m_run, l_run, lim, tid, g, lane);
+  unit_pipeline<FP8, NRT, DH, PAGED>(us, lds, xs, wave, fb, qf, oacc, m_run, l_run, lim, tid, g, lane);
   epilogue<NRT, DH>(us, grow0, l16, g, oacc, m_run, l_run);
 }
 
@@ -897,14 +985,19 @@ constexpr int main_lds_bytes() {
   return kRing * kTileBytes + 2 * kWaves * NRT * 2 * 1024;  // tile ring + 2 exchange buffers
 }
 
-template <bool FP8, int NRT>
+// One kernel per (KV dtype, row tiles per row group, KV layout): a kernel holds
+// a single pipeline, so that the register allocation of one layout never
+// constrains the other.
+template <bool FP8, int NRT, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_main(const MainArgs args) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[main_lds_bytes<NRT>()];
   if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1)
-    unit_body<FP8, NRT, 1>(args, smem);
+    unit_body<FP8, NRT, 1, PAGED>(args, smem);
   else
-    unit_body<FP8, NRT, 0>(args, smem);
+    unit_body<FP8, NRT, 0, PAGED>(args, smem);
 }
+
+#ifndef MLA_PAGED_KV  // the merges are built once, with the contiguous-KV kernels
 
 // Split-KV merge.  One 256-thread block per (split output row, 64 of the 512
 // value columns).  Thread (part p, column group cg) owns columns
@@ -1034,29 +1127,41 @@ __global__ __launch_bounds__(kRedThreads) void mla_merge_shards_kernel(const Mer
                cb == 0 && cg == 0);
 }
 
+#endif  // !MLA_PAGED_KV
+
 // ------------------------------------------------------------- launchers
 
-template <bool FP8>
+template <bool FP8, bool PAGED>
 static void launch_main_t(const MainArgs& a, int nrt, int grid, hipStream_t stream) {
   if (nrt <= 1)
-    hipLaunchKernelGGL((mla_decode_main<FP8, 1>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((mla_decode_main<FP8, 1, PAGED>), dim3(grid), dim3(kThreads), 0, stream, a);
   else if (nrt == 2)
-    hipLaunchKernelGGL((mla_decode_main<FP8, 2>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((mla_decode_main<FP8, 2, PAGED>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((mla_decode_main<FP8, 3>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((mla_decode_main<FP8, 3, PAGED>), dim3(grid), dim3(kThreads), 0, stream, a);
 }
 
-hipError_t launch_main(const MainArgs& a, bool fp8, int nrt, hipStream_t stream) {
+// This file is compiled twice: once for contiguous KV (with the merges) and
+// once, with MLA_PAGED_KV defined (kernels_paged.hip), for paged KV, so that
+// the two sets of main kernels build in parallel.
+#ifdef MLA_PAGED_KV
+hipError_t launch_main_paged(const MainArgs& a, bool fp8, int nrt, hipStream_t stream) {
+  constexpr bool kPaged = true;
+#else
+hipError_t launch_main_contiguous(const MainArgs& a, bool fp8, int nrt, hipStream_t stream) {
+  constexpr bool kPaged = false;
+#endif
   const int grid = ((a.num_units + kNumXcd - 1) / kNumXcd) * kNumXcd;
   if (grid == 0) return hipSuccess;
   if (nrt < 1 || nrt > 3) return hipErrorInvalidValue;
   if (fp8)
-    launch_main_t<true>(a, nrt, grid, stream);
+    launch_main_t<true, kPaged>(a, nrt, grid, stream);
   else
-    launch_main_t<false>(a, nrt, grid, stream);
+    launch_main_t<false, kPaged>(a, nrt, grid, stream);
   return hipGetLastError();
 }
 
+#ifndef MLA_PAGED_KV
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
   const int grid = (kDv / kRedCols) * a.num_rows;
   if (grid == 0) return hipSuccess;
@@ -1069,5 +1174,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(mla_merge_shards_kernel, dim3(grid), dim3(kRedThreads), 0, stream, a);
   return hipGetLastError();
 }
+
+#endif  // !MLA_PAGED_KV
 
 }  // namespace mla

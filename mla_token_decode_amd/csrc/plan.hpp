@@ -47,6 +47,10 @@ struct MainArgs {
   float* part_o;       // [total partial rows][512]
   float scale_log2;    // sm_scale * kv_scale * log2(e)
   float o_scale;       // kv_scale (fp8) or 1 (bf16)
+  const int32_t* page_table;  // paged KV: [batch][pt_stride] page indices; null: contiguous KV
+  int32_t pt_stride;
+  int32_t page_shift;  // page size = 2^page_shift keys (paged only)
+  int32_t num_pages;   // pages in the pool (entries are clamped to it)
   int32_t H;
   int32_t num_seqs;
   int32_t num_units;

@@ -23,12 +23,23 @@ STAGED_LOAD = re.compile(r"buffer_load_dwordx[24] (v\S+?),? v\d+, s\[\d+:\d+\], 
 
 
 def kernels(asm: str) -> dict:
-    """Main-kernel name -> list of its assembly lines."""
+    """Main-kernel name -> list of its assembly lines (the body and the
+    compiler's resource summary comments that follow it)."""
     out = {}
     for m in MAIN_KERNEL.finditer(asm):
         end = asm.find(".Lfunc_end", m.end())
-        out[m.group(1)] = asm[m.end():end].split("\n")
+        stats = asm.find("; Occupancy:", end)
+        out[m.group(1)] = asm[m.end():stats if stats >= 0 else end].split("\n")
     return out
+
+
+def scratch_bytes(lines) -> int:
+    """ScratchSize of the kernel's resource summary (private memory per lane)."""
+    for line in lines:
+        m = re.match(r"; ScratchSize: (\d+)", line.strip())
+        if m:
+            return int(m.group(1))
+    raise AssertionError("no ScratchSize line")
 
 
 def regs(tok: str) -> set:

@@ -169,3 +169,26 @@ def test_merge_shards_argument_checks():
         assert L.mla_merge_shards(rows, shards, fake, fake, fake, fake, None) == mb.MLA_ERR_INVALID_ARGUMENT
     assert L.mla_merge_shards(4, 2, None, fake, fake, fake, None) == mb.MLA_ERR_INVALID_ARGUMENT
     assert L.mla_merge_shards(4, 2, fake + 4, fake, fake, fake, None) == mb.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_paged_run_argument_checks():
+    """mla_decode_run_paged rejects page sizes that are not powers of two in
+    [32, 2^20] as unsupported, and an empty pool, a null or misaligned page
+    table or a stride shorter than the longest sequence as invalid, before
+    any device work."""
+    L = mb.lib()
+    p = plan(12, [8], [3000])
+    fake = 1 << 20  # aligned, never dereferenced
+
+    def call(num_pages=64, page=64, table=fake, stride=64):
+        return L.mla_decode_run_paged(p.handle, fake, fake, num_pages, page, table, stride, 0.04,
+                                      1.0, fake, fake, fake, 1 << 30, None)
+
+    for page in (0, -64, 1, 16, 48, 96, 1 << 21):
+        assert call(page=page) == mb.MLA_ERR_UNSUPPORTED, page
+    assert call(num_pages=0) == mb.MLA_ERR_INVALID_ARGUMENT
+    assert call(table=None) == mb.MLA_ERR_INVALID_ARGUMENT
+    assert call(table=fake + 2) == mb.MLA_ERR_INVALID_ARGUMENT
+    assert call(page=64, stride=46) == mb.MLA_ERR_INVALID_ARGUMENT  # 3000 keys need 47 pages
+    assert call(page=32, stride=93) == mb.MLA_ERR_INVALID_ARGUMENT  # ... or 94
+    assert "page" in mb.lib().mla_last_error().decode()

@@ -18,13 +18,27 @@ HIPCC = hipbuild.HIPCC
 def kernels(tmp_path_factory):
     if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "kernels.s"
-    src = os.path.join(hipbuild.CSRC, "kernels.hip")
-    subprocess.run([HIPCC, *hipbuild.compile_flags(), "-S", "--cuda-device-only", "-o", str(out), src],
-                   check=True)
-    ks = asm_scan.kernels(out.read_text())
-    assert len(ks) == 6, sorted(ks)  # {bf16, fp8} x {16, 32, 48 rows per row group}
+    tmp = tmp_path_factory.mktemp("asm")
+    procs = []
+    for name in ("kernels", "kernels_paged"):  # contiguous and paged KV, compiled in parallel
+        out = tmp / f"{name}.s"
+        src = os.path.join(hipbuild.CSRC, f"{name}.hip")
+        cmd = [HIPCC, *hipbuild.compile_flags(), "-S", "--cuda-device-only", "-o", str(out), src]
+        procs.append((out, subprocess.Popen(cmd)))
+    ks = {}
+    for out, p in procs:
+        assert p.wait() == 0
+        part = asm_scan.kernels(out.read_text())
+        assert len(part) == 6, sorted(part)  # {bf16, fp8} x {16, 32, 48 rows per row group}
+        ks.update(part)
+    assert len(ks) == 12, sorted(ks)
     return ks
+
+
+def test_main_kernels_use_no_scratch(kernels):
+    """Every main kernel keeps its pipeline in registers: no private segment."""
+    for name, lines in kernels.items():
+        assert asm_scan.scratch_bytes(lines) == 0, name
 
 
 def test_no_unpadded_mfma_hazards(kernels):
