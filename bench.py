@@ -78,8 +78,10 @@ class CacheFlush:
             self.buf.add_(1)
 
 
-def measure(inp, dev, steps, warmup, flush, **plan_opts):
-    """Cold-cache timing of run + reduce.  Returns a stats dict (microseconds)."""
+def measure(inp, dev, steps, warmup, flush, paged=None, **plan_opts):
+    """Cold-cache timing of run + reduce (mla_decode_run, or mla_decode_run_paged
+    when `paged` = (pool, page table) is given).  Returns a stats dict
+    (microseconds)."""
     import torch
     from mla_token_decode_amd import binding as mb
 
@@ -88,8 +90,15 @@ def measure(inp, dev, steps, warmup, flush, **plan_opts):
     o, lse, ws = mb.alloc_outputs(plan, q.device)
     stream = torch.cuda.current_stream()
 
+    def run():
+        if paged is None:
+            mb.mla_decode_run(plan, q, kv, inp.sm_scale, inp.kv_scale, o, lse, ws, ws.numel(), stream)
+        else:
+            mb.mla_decode_run_paged(plan, q, paged[0], paged[1], inp.sm_scale, inp.kv_scale, o, lse,
+                                    ws, ws.numel(), stream)
+
     def step():
-        mb.mla_decode_run(plan, q, kv, inp.sm_scale, inp.kv_scale, o, lse, ws, ws.numel(), stream)
+        run()
         mb.mla_decode_reduce(plan, ws, o, lse, stream)
 
     for _ in range(warmup):
@@ -112,7 +121,7 @@ def measure(inp, dev, steps, warmup, flush, **plan_opts):
     for k in range(steps):
         flush()
         ev[k][0].record(stream)
-        mb.mla_decode_run(plan, q, kv, inp.sm_scale, inp.kv_scale, o, lse, ws, ws.numel(), stream)
+        run()
         ev[k][1].record(stream)
         mb.mla_decode_reduce(plan, ws, o, lse, stream)
         ev[k][2].record(stream)
@@ -233,6 +242,17 @@ def main():
 
     per = {HEADLINE: head}
     if not args.quick:
+        # the headline workload from a paged cache: 64-key pages in a seeded random order
+        page = 64
+        npages = w.kv_len[0] // page
+        perm = np.random.default_rng(7).permutation(npages)  # pool slot of each logical page
+        pool = torch.empty((npages, page, dev[1].shape[1]), dtype=dev[1].dtype, device="cuda")
+        pool[torch.from_numpy(perm).cuda()] = dev[1].view(npages, page, -1)
+        table = torch.from_numpy(perm.astype(np.int32)).view(1, npages).cuda()
+        name = f"paged_{HEADLINE}_p{page}"
+        per[name] = measure(inp, dev, args.steps, args.warmup, flush, paged=(pool, table))
+        log(f"  {name}: {per[name]['us_per_call']:.1f} us")
+        del pool, table
         # q-flatness at ctx=1M, both dtypes (same KV per dtype, Q per q)
         kv_fp8 = inp.kv
         for fp8 in (True, False):
