@@ -41,6 +41,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -62,6 +63,20 @@ constexpr int kChunks = kRowBytes / 16;        // 72
 constexpr int kTileBytes = kTK * kRowBytes;    // 36864
 __device__ __forceinline__ int swz(int key) { return (key & 7) ^ ((key >> 3) & 1); }
 
+// fp8 KV tiles stay fp8 in LDS for the latent part (QK^T runs on fp8 MFMAs and
+// V is converted when read): 512-byte latent rows, then the 64 rope columns
+// of every key as bf16 (128-byte rows; the rope part of QK^T stays bf16).
+// Latent rows XOR their 16-byte chunk index with swz8(key): the 16 keys of a
+// K fragment read (keys 16 kt + m) and the 8 keys of a transposing V read
+// (keys 4 g + i and 16 + 4 g + i) all land in distinct 16-byte bank slots.
+constexpr int kLatBytes8 = 512;
+constexpr int kRopeOff8 = kTK * kLatBytes8;       // 16384
+constexpr int kTileBytes8 = kRopeOff8 + kTK * 128;  // 20480
+template <bool FP8>
+constexpr int tile_bytes() { return FP8 ? kTileBytes8 : kTileBytes; }
+__device__ __forceinline__ int swz8(int key) { return (key & 15) ^ ((key & 16) >> 1); }
+__device__ __forceinline__ int rope_swz(int key) { return (key >> 1) & 7; }
+
 // One staged KV tile per thread: 2304 pieces of the tile (16 B of bf16 or 8 B
 // of fp8, i.e. 8 elements each), piece li = tid + 256 m, m = 0..8.
 constexpr int kPieces = kTK * kChunks / kThreads;  // 9
@@ -77,7 +92,7 @@ struct Stage {
 // of each row-tile count allows; with 3 row tiles a bf16 set is 36 VGPRs and
 // one set, issued one iteration ahead of its LDS store, is what fits.
 template <bool FP8, int NRT>
-constexpr int stage_sets() { return FP8 ? 3 : (NRT == 3 ? 1 : 2); }
+constexpr int stage_sets() { return FP8 ? (NRT == 1 ? 3 : 2) : (NRT == 3 ? 1 : 2); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -176,11 +191,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* kv_un
 // staging set.  The loads are inline assembly so that their completion is
 // waited for explicitly (wait_stage): the compiler's own counting drains every
 // set in flight at the loop head.
+// fp8: pieces 0..7 are latent (key tid/64 + 4 M, bytes 8 (tid % 64) ..), piece 8
+// is rope (key tid/8, bytes 512 + 8 (tid % 8) ..).  bf16: piece M is the 16
+// bytes at 16 tid + 4096 M of the tile.
 template <bool FP8, int M>
 __device__ __forceinline__ void stage_load_piece(Stage<FP8>& st, __amdgpu_buffer_rsrc_t r, int tid) {
   constexpr int PB = FP8 ? 8 : 16;  // bytes per piece
-  const int off = tid * PB;
-  const int soff = kThreads * PB * M;
+  const int off = !FP8 ? tid * PB
+                  : M < 8 ? (tid >> 6) * kDqk + 8 * (tid & 63)
+                          : (tid >> 3) * kDqk + 512 + 8 * (tid & 7);
+  const int soff = !FP8 ? kThreads * PB * M : M < 8 ? 4 * kDqk * M : 0;
   if constexpr (FP8)
     asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen"
                  : "=&v"(st.p[M]) : "v"(off), "s"(r), "s"(soff) : "memory");
@@ -256,17 +276,25 @@ __device__ __forceinline__ void wait_stage(Stage<FP8>& st) {
                : "memory");
 }
 
-// Write piece M of a staged tile into an LDS slot (bf16 rows, swizzled chunks).
+// Write piece M of a staged tile into an LDS slot.  bf16: swizzled bf16 rows.
+// fp8: latent pieces as they are (key k0 + 4 M with k0 = tid / 64, whose
+// swizzle is k0 ^ f(M): the address is one XOR with a constant away from a
+// per-thread base), the rope piece converted to bf16.
 template <bool FP8, int M>
 __device__ __forceinline__ void stage_store_piece(const Stage<FP8>& st, lds_u8* slot, int tid) {
-  const int li = tid + kThreads * M;
-  const int key = li / kChunks, c = li % kChunks;
-  u32x4 v;
-  if constexpr (FP8)
-    v = fp8x8_to_bf16(st.p[M]);
-  else
-    v = st.p[M];
-  *(u32x4*)(slot + key * kRowBytes + 16 * (c ^ swz(key))) = v;
+  if constexpr (!FP8) {
+    const int li = tid + kThreads * M;
+    const int key = li / kChunks, c = li % kChunks;
+    *(u32x4*)(slot + key * kRowBytes + 16 * (c ^ swz(key))) = st.p[M];
+  } else if constexpr (M < 8) {
+    const int k0 = tid >> 6, c8 = tid & 63;
+    const int base = k0 * kLatBytes8 + 16 * ((c8 >> 1) ^ k0) + 8 * (c8 & 1);
+    constexpr int f = (4 * (M & 3)) ^ (8 * (M >> 2));  // swz8(k0 + 4 M) = k0 ^ f
+    *(u32x2*)(slot + ((base ^ (16 * f)) + 4 * kLatBytes8 * M)) = st.p[M];
+  } else {
+    const int key = tid >> 3, c = tid & 7;
+    *(u32x4*)(slot + kRopeOff8 + key * 128 + 16 * (c ^ rope_swz(key))) = fp8x8_to_bf16(st.p[M]);
+  }
 }
 
 template <bool FP8>
@@ -345,6 +373,64 @@ __device__ __forceinline__ bf16x8 finish_v(const VRaw& r) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// ---- fp8 tiles (latent fp8, rope bf16)
+//
+// K fragment of the fp8 MFMA (A operand of S^T = K Q^T, 16 x 16 x 128): lane
+// (g, m) holds key 16 kt + m, latent columns 128 b + 32 g .. +32 of block b,
+// read as two 16-byte chunks.  Rope fragment (bf16 MFMA): key 16 kt + m,
+// rope columns 32 DH + 8 g .. +8.  V^T fragment (8 keys x 1 column, one
+// transposing 8-bit read): lane (g, i) gets column 16 ct + i, element e is key
+// 4 g + e (e < 4) or 16 + 4 g + e - 4, as in the bf16 layout; in each 16-lane
+// group lane 2 j + h points at key j's columns 16 ct + 8 h .. +8 and lane i
+// receives byte i mod 8 of the lanes 2 j + i / 8.
+struct FragBases8 {
+  int k[2][2][2];  // [kt][block b of the wave's half][16-byte half s]
+  int kr[2];       // [kt] rope
+  int v;           // V: key row + 8 h + 16 swz8(key); column tile ct adds ^ (16 ct)
+};
+
+template <int DH>
+__device__ __forceinline__ FragBases8 frag_bases8(int l16, int g) {
+  FragBases8 fb;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = 16 * kt + l16;
+    const int sw = swz8(key);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        fb.k[kt][b][h] = key * kLatBytes8 + 256 * DH + 16 * ((8 * b + 2 * g + h) ^ sw);
+    fb.kr[kt] = kRopeOff8 + key * 128 + 16 * ((4 * DH + g) ^ rope_swz(key));
+  }
+  const int j = l16 >> 1, h = l16 & 1;
+  const int kv = 16 * (j >> 2) + 4 * g + (j & 3);
+  fb.v = kv * kLatBytes8 + 8 * h + 16 * swz8(kv);
+  return fb;
+}
+
+template <int KT, int B>
+__device__ __forceinline__ i32x8 read_k8(lds_u8* tile, const FragBases8& fb) {
+  const i32x4 a = *(const i32x4*)(tile + fb.k[KT][B][0]);
+  const i32x4 b = *(const i32x4*)(tile + fb.k[KT][B][1]);
+  return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+template <int KT>
+__device__ __forceinline__ bf16x8 read_kr(lds_u8* tile, const FragBases8& fb) {
+  return *(const bf16x8*)(tile + fb.kr[KT]);
+}
+
+// V^T fragment of column tile 16 DH + CT (fp8 codes; see wait_lds1).
+template <int DH, int CT>
+__device__ __forceinline__ void issue_v8(i32x2& r, lds_u8* vbase) {
+  lds_u8* a = (lds_u8*)((size_t)vbase ^ (size_t)(16 * CT));
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(256 * DH));
+}
+template <int N>
+__device__ __forceinline__ void wait_lds1(i32x2& a) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N) : "memory");
+}
 
 // MFMAs through inline assembly with explicit register files: the compiler's
 // own choice kept moving accumulators between register files every
@@ -370,6 +456,15 @@ __device__ __forceinline__ void mfma_s(f32x4& acc, const bf16x8& k, const bf16x8
 template <int NRT>
 constexpr bool q_in_agpr(int rt, int j) {
   return 64 * NRT + 4 * (rt * 9 + j + 1) <= 256;
+}
+// fp8 score MFMA, Q (fp8, per-row scaled) in VGPRs: it is computed by VALU
+// instructions, and a VALU-defined operand in AGPRs became a copy per MFMA.
+template <bool ZERO>
+__device__ __forceinline__ void mfma_s8(f32x4& acc, const i32x8& k, const i32x8& q) {
+  if constexpr (ZERO)
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "v"(q));
+  else
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "v"(q));
 }
 __device__ __forceinline__ void mfma_o(f32x4& acc, const bf16x8& v, const bf16x8& p) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
@@ -592,7 +687,7 @@ __device__ __forceinline__ void slices_at(F&& f) {
 template <int NRT, bool FP8>
 constexpr int k_ahead() { return NRT == 1 ? 4 : NRT == 2 ? 2 : 1; }
 template <int NRT, bool FP8>
-constexpr int v_ahead() { return NRT == 1 ? 7 : NRT == 2 ? 4 : (FP8 ? 2 : 1); }
+constexpr int v_ahead() { return NRT == 1 ? 7 : FP8 ? (NRT == 2 ? 6 : 3) : (NRT == 2 ? 4 : 1); }
 
 // Score phase: S^T partial (this wave's 288 columns) of one tile; K fragments
 // DK steps ahead; pre(i) runs before MFMA i and slice(i) after it.
@@ -660,8 +755,88 @@ __device__ __forceinline__ void pv_phase(lds_u8* tile, const FragBases& fb,
   });
 }
 
+// fp8 score phase: S^T partial of one tile from this wave's two 128-column
+// latent blocks (fp8 MFMAs, 2 NRT each) and its 32 rope columns (bf16 MFMAs,
+// accumulated last: at least one independent MFMA separates each from the fp8
+// MFMA that wrote its accumulator); pre(i) runs before MFMA i, slice(i) after.
+template <int NRT>
+struct QFrag8 {
+  i32x8 lat[NRT][2];  // fp8 codes of Q / s_row, latent block 2 DH + b
+  bf16x8 rope[NRT];   // bf16 of Q / s_row, rope columns 32 DH + 8 g .. +8 (AGPRs)
+};
+
+template <int NRT, int DH, typename P, typename W>
+__device__ __forceinline__ void score_phase8(lds_u8* tile, const FragBases8& fb, const QFrag8<NRT>& q8,
+                                             f32x4 (&sacc)[2][NRT], P&& pre, W&& slice) {
+  i32x8 kl[2][2];  // [block][kt]
+  bf16x8 kr[2];
+  kl[0][0] = read_k8<0, 0>(tile, fb);
+  kl[0][1] = read_k8<1, 0>(tile, fb);
+  static_for<3>([&](auto sc) {
+    constexpr int st = decltype(sc)::value;
+    if constexpr (st == 0) {
+      kl[1][0] = read_k8<0, 1>(tile, fb);
+      kl[1][1] = read_k8<1, 1>(tile, fb);
+    } else if constexpr (st == 1) {
+      kr[0] = read_kr<0>(tile, fb);
+      kr[1] = read_kr<1>(tile, fb);
+    }
+    static_for<2 * NRT>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int kt = i / NRT, rt = i % NRT;
+      pre(std::integral_constant<int, st * 2 * NRT + i>{});
+      if constexpr (st < 2)
+        mfma_s8<st == 0>(sacc[kt][rt], kl[st][kt], q8.lat[rt][st]);
+      else
+        mfma_s<false, true>(sacc[kt][rt], kr[kt], q8.rope[rt]);
+      slice(std::integral_constant<int, st * 2 * NRT + i>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  });
+}
+
+template <int DH, int DV>
+__device__ __forceinline__ void issue_v_head8(i32x2 (&vr)[DV + 1], lds_u8* vbase) {
+  static_for<DV>([&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    issue_v8<DH, c>(vr[c], vbase);
+  });
+}
+
+// fp8 PV phase: as pv_phase, with one 8-bit transposing read per V fragment,
+// converted to bf16 (exact).  The conversion of column tile c + 1 runs
+// between the MFMAs of column tile c, so the MFMAs never wait for it.
+template <int NRT, int DH, int DV, typename W>
+__device__ __forceinline__ void pv_phase8(lds_u8* vbase, const bf16x8 (&pf)[NRT],
+                                          f32x4 (&oacc)[16][NRT], i32x2 (&vr)[DV + 1], W&& slice) {
+  static_assert(DV >= 1 && DV < 16, "read-ahead depth");
+  auto cvt = [](const i32x2& r) {
+    return __builtin_bit_cast(bf16x8, fp8x8_to_bf16(__builtin_bit_cast(u32x2, r)));
+  };
+  bf16x8 vf[2];
+  wait_lds1<DV - 1>(vr[0]);  // reads 0 .. DV-1 were issued before the score phase
+  vf[0] = cvt(vr[0]);
+  asm volatile("s_nop 1" : "+v"(vf[0]) :: "memory");  // VALU writes (vf, P) before the MFMAs
+  static_for<16>([&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    if constexpr (c + DV < 16) issue_v8<DH, c + DV>(vr[(c + DV) % (DV + 1)], vbase);
+    if constexpr (c + 1 < 16) wait_lds1<(c + DV < 16) ? DV - 1 : 14 - c>(vr[(c + 1) % (DV + 1)]);
+    static_for<NRT>([&](auto rc) {
+      constexpr int rt = decltype(rc)::value;
+      mfma_o(oacc[c][rt], vf[c & 1], pf[rt]);
+      if constexpr (rt == 0 && c + 1 < 16) {
+        vf[(c + 1) & 1] = cvt(vr[(c + 1) % (DV + 1)]);
+        if constexpr (NRT < 3) asm volatile("s_nop 1" : "+v"(vf[(c + 1) & 1]) :: "memory");
+      }
+      slice(std::integral_constant<int, c * NRT + rt>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  });
+}
+
 // Online softmax of one tile (base 2) with a lazy per-row reference m_run:
-// P = 2^(c s - m_run) with c = sm_scale * kv_scale * log2(e) > 0; the first
+// P = 2^(c s - m_run) with c = sm_scale * kv_scale * log2(e) > 0 (fp8: times the
+// row's Q scale, c is per row); the first
 // tile that shows a row a key sets its reference, which moves only when a
 // tile maximum exceeds it by more than kLazyOctaves (then O and l are
 // rescaled: rare).  Whether any row of the wave needs that is decided from
@@ -685,8 +860,8 @@ template <int NRT, int PH>
 __device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, f32x4 (&sfull)[2][NRT],
                                               bf16x8 (&pf)[NRT], float (&m_run)[NRT],
                                               float (&l_run)[NRT], f32x4 (&oacc)[16][NRT],
-                                              const int (&lim)[NRT], int k0, bool edge, float c,
-                                              int g, lds_u8* spill) {
+                                              const int (&lim)[NRT], int k0, bool edge,
+                                              const float (&c)[NRT], int g, lds_u8* spill) {
   if constexpr (PH == 0) {  // keys past a row's causal limit (last tiles of a chunk only)
     w.jump = false;
     if (edge) {
@@ -705,13 +880,13 @@ __device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, f32x4 (&sfull)[2
     constexpr int rt = PH - 1;
     const f32x4 a = sfull[0][rt], b = sfull[1][rt];
     w.mx[rt] = max2(max3(a[0], a[1], a[2]), max3(a[3], b[0], max3(b[1], b[2], b[3])));
-    w.jump = w.jump || w.mx[rt] * c > m_run[rt] + kLazyOctaves;
+    w.jump = w.jump || w.mx[rt] * c[rt] > m_run[rt] + kLazyOctaves;
   } else if constexpr (PH == NRT + 1) {  // wave vote; rare: row maxima, references, rescale
     if (__builtin_amdgcn_ballot_w64(w.jump) != 0) {  // wave-uniform
       asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // O MFMAs retired
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
-        const float mx = wave_max_across_groups(w.mx[rt]) * c;
+        const float mx = wave_max_across_groups(w.mx[rt]) * c[rt];
         const bool first = m_run[rt] == -INFINITY;  // O and l are still 0
         const bool jump = !first && mx > m_run[rt] + kLazyOctaves;
         if (__builtin_amdgcn_ballot_w64(jump) != 0) {
@@ -731,8 +906,8 @@ __device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, f32x4 (&sfull)[2
     constexpr int j = PH - (NRT + 2);
     constexpr int rt = j / 4, kt = (j / 2) % 2, h = j % 2;
     // v_exp_f32: results below the fp32 normal range flush to 0
-    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sfull[kt][rt][2 * h], c, w.nmu[rt]));
-    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sfull[kt][rt][2 * h + 1], c, w.nmu[rt]));
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sfull[kt][rt][2 * h], c[rt], w.nmu[rt]));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sfull[kt][rt][2 * h + 1], c[rt], w.nmu[rt]));
     w.psum[rt] = (j % 4 == 0) ? p0 + p1 : w.psum[rt] + (p0 + p1);
     pf[rt][4 * kt + 2 * h] = (__bf16)p0;
     pf[rt][4 * kt + 2 * h + 1] = (__bf16)p1;
@@ -767,7 +942,7 @@ __device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* l
   static_for<2>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     wait_stage<kAhead, FP8>(st[j % NS]);
-    stage_store<FP8>(st[j % NS], lds + j * kTileBytes, tid);
+    stage_store<FP8>(st[j % NS], lds + j * tile_bytes<FP8>(), tid);
     stage_load<FP8>(st[j % NS], src.rsrc(j + NS, pr[j + NS]), tid);
   });
   lds_barrier();
@@ -780,7 +955,7 @@ __device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* l
       const int t = base + k;
       if (t < u.ntiles) {
         wait_stage<kAhead, FP8>(st[ks]);
-        stage_store<FP8>(st[ks], lds + ((t + 2) % kRing) * kTileBytes, tid);
+        stage_store<FP8>(st[ks], lds + ((t + 2) % kRing) * tile_bytes<FP8>(), tid);
         stage_load<FP8>(st[ks], src.rsrc(t + 2 + NS, prow_next), tid);
         if constexpr (PAGED)
           prow_next = src.barrier_and_page_row(t + 3 + NS);
@@ -798,16 +973,17 @@ __device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* l
 // past the end load nothing), so the staged registers never need a copy while
 // their loads are in flight (the compiler does not know that an
 // inline-assembly load completes later).
-template <bool FP8, int NRT, int DH, bool PAGED>
+template <bool FP8, int NRT, int DH, bool PAGED, typename FB, typename QT>
 __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, float* xs,
-                                              int wave, const FragBases& fb,
-                                              const bf16x8 (&qf)[NRT][9], f32x4 (&oacc)[16][NRT],
+                                              int wave, const FB& fb, const QT& qf,
+                                              const float (&c)[NRT], f32x4 (&oacc)[16][NRT],
                                               float (&m_run)[NRT], float (&l_run)[NRT],
                                               const int (&lim)[NRT], int tid, int g, int lane) {
   constexpr int NS = stage_sets<FP8, NRT>();
   constexpr int kAhead = (NS - 1) * kPieces;  // loads issued after a set's own
   constexpr int kXsWave = NRT * 2 * 256;      // floats of one wave's partial scores
   constexpr int DK = k_ahead<NRT, FP8>(), DV = v_ahead<NRT, FP8>();
+  constexpr int TB = tile_bytes<FP8>();
   const UnitCtx u = us.uc;
   const KvSource<FP8, PAGED> src = kv_source<FP8, PAGED>(us);
   if (u.ntiles <= 0) return;
@@ -821,15 +997,22 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
   static_for<2>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     wait_stage<kAhead, FP8>(st[j % NS]);
-    stage_store<FP8>(st[j % NS], lds + j * kTileBytes, tid);
+    stage_store<FP8>(st[j % NS], lds + j * TB, tid);
     stage_load<FP8>(st[j % NS], src.rsrc(j + NS, pr[j + NS]), tid);
   });
   lds_barrier();
   int64_t prow_next = pr[NS + 2];  // page row of the first tile the loop loads
 
-  // full scores of tile 0
   f32x4 sacc[2][NRT], sfull[2][NRT];
-  score_phase<NRT, DH, DK>(lds, fb, qf, sacc, [](auto) {}, [](auto) {});
+  auto scores = [&](lds_u8* tile, auto&& pre, auto&& slice) {
+    if constexpr (FP8)
+      score_phase8<NRT, DH>(tile, fb, qf, sacc, pre, slice);
+    else
+      score_phase<NRT, DH, DK>(tile, fb, qf, sacc, pre, slice);
+  };
+
+  // full scores of tile 0
+  scores(lds, [](auto) {}, [](auto) {});
   asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");  // score MFMAs retire before the reads
   {
     float* mine = xs + wave * kXsWave;
@@ -849,7 +1032,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         sfull[kt][rt] = *(const f32x4*)(peer + ((rt * 2 + kt) * 64 + lane) * 4);
   }
 
-  VRaw vr[DV + 1];
+  typename std::conditional<FP8, i32x2, VRaw>::type vr[DV + 1];
   bf16x8 pf[NRT];
   SoftTile<NRT> sw;
 #pragma unroll
@@ -864,13 +1047,19 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         float* mine = xs + (par * kWaves + wave) * kXsWave;
         const float* peer = xs + (par * kWaves + (wave ^ 1)) * kXsWave;
         lds_u8* spill = (lds_u8*)mine + lane * 16;  // free until the exchange write below
-        lds_u8* slot_t = lds + (t % kRing) * kTileBytes;
-        lds_u8* slot_n = lds + ((t + 1) % kRing) * kTileBytes;
-        lds_u8* slot_s = lds + ((t + 2) % kRing) * kTileBytes;
+        lds_u8* slot_t = lds + (t % kRing) * TB;
+        lds_u8* slot_n = lds + ((t + 1) % kRing) * TB;
+        lds_u8* slot_s = lds + ((t + 2) % kRing) * TB;
         const int k0 = t * kTK;
         const bool edge = k0 + kTK - 1 > u.min_lim;
         const __amdgpu_buffer_rsrc_t rs_next = src.rsrc(t + 2 + NS, prow_next);
-        issue_v_head<DH, DV>(vr, slot_t, fb);
+        lds_u8* vbase = nullptr;  // fp8: V reads of tile t (column tile ct adds ^ 16 ct)
+        if constexpr (FP8) {
+          vbase = slot_t + fb.v;
+          issue_v_head8<DH, DV>(vr, vbase);
+        } else {
+          issue_v_head<DH, DV>(vr, slot_t, fb);
+        }
 
         // staging of tile t + 2: wait for its loads, LDS store, next loads
         constexpr int kStageSlices = 1 + 2 * kPieces;
@@ -888,25 +1077,24 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         // scores of tile t + 1  ||  softmax of tile t (and the staging); before
         // the first MFMAs overwrite this wave's half of tile t's scores, it is
         // added to the partner's half read after the last barrier
-        constexpr int kScoreMfma = 18 * NRT;
+        constexpr int kScoreMfma = (FP8 ? 6 : 18) * NRT;
         constexpr int kAdd = 2 * NRT;  // MFMAs of the first step
         auto add_own = [&](auto ic) {
           constexpr int i = decltype(ic)::value;
           if constexpr (i < kAdd) sfull[i / NRT][i % NRT] += sacc[i / NRT][i % NRT];
         };
-        score_phase<NRT, DH, DK>(slot_n, fb, qf, sacc, add_own, [&](auto ic) {
+        scores(slot_n, add_own, [&](auto ic) {
           constexpr int i = decltype(ic)::value;  // slices start once tile t's scores are whole
           slices_at<soft_slices<NRT>(), kScoreMfma - kAdd + 1, i - kAdd + 1>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
-            softmax_slice<NRT, s>(sw, sfull, pf, m_run, l_run, oacc, lim, k0, edge, us.scale_log2,
-                                  g, spill);
+            softmax_slice<NRT, s>(sw, sfull, pf, m_run, l_run, oacc, lim, k0, edge, c, g, spill);
           });
           if constexpr (kStageWithScores) slices_at<kStageSlices, kScoreMfma, i>(stage_slice);
         });
 
         // O of tile t  ||  exchange write of tile t + 1 (and the staging)
         constexpr int kPvMfma = 16 * NRT;
-        pv_phase<NRT, DH, DV>(slot_t, fb, pf, oacc, vr, [&](auto ic) {
+        auto pv_slice = [&](auto ic) {
           constexpr int i = decltype(ic)::value;
           slices_at<NRT, kPvMfma, i>([&](auto sc) {  // partial scores of tile t + 1
             constexpr int s = decltype(sc)::value;
@@ -916,7 +1104,11 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
               *(f32x4*)(mine + ((s * 2 + kt) * 64 + lane) * 4) = sacc[kt][s];
           });
           if constexpr (!kStageWithScores) slices_at<kStageSlices, kPvMfma, i>(stage_slice);
-        });
+        };
+        if constexpr (FP8)
+          pv_phase8<NRT, DH, DV>(vbase, pf, oacc, vr, pv_slice);
+        else
+          pv_phase<NRT, DH, DV>(slot_t, fb, pf, oacc, vr, pv_slice);
 
         if constexpr (PAGED)
           prow_next = src.barrier_and_page_row(t + 3 + NS);
@@ -931,6 +1123,81 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
     });
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads issued past the end
+}
+
+// fp8 Q: per row, the latent columns are quantised to e4m3 with the scale
+// s = max |q latent| / 448 (round to nearest even; the row's scores then carry
+// the factor s, folded into the row's softmax constant c = c0 s), the rope
+// columns become bf16 of q / s.  The two waves of a pair hold halves of each
+// row and agree on s through LDS (one barrier, taken by every wave of the
+// workgroup).  Rows past the unit read row RU - 1 (their outputs are never
+// written).
+template <int NRT, int DH>
+__device__ __forceinline__ void load_q8(const UnitSetup& us, int grow0, int l16, int g, int wave,
+                                        float* xs, QFrag8<NRT>& q8, float (&c)[NRT]) {
+  u32x4 lat[NRT][2][4], rope[NRT];
+  float half_max[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int row = min(grow0 + 16 * rt + l16, us.RU - 1);
+    const uint16_t* qrow = us.q + ((int64_t)us.row0 + row) * kDqk;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        lat[rt][b][i] = *(const u32x4*)(qrow + 256 * DH + 128 * b + 32 * g + 8 * i);
+    rope[rt] = *(const u32x4*)(qrow + 512 + 32 * DH + 8 * g);
+  }
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    float m = 0.0f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const unsigned x = lat[rt][b][i][w];
+          m = fmaxf(m, fmaxf(fabsf(__builtin_bit_cast(float, x << 16)),
+                             fabsf(__builtin_bit_cast(float, x & 0xffff0000u))));
+        }
+    half_max[rt] = wave_max_across_groups(m);
+    if (g == 0) xs[(wave * NRT + rt) * 16 + l16] = half_max[rt];
+  }
+  lds_barrier();
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const float M = fmaxf(half_max[rt], xs[((wave ^ 1) * NRT + rt) * 16 + l16]);
+    const float inv = M > 0.0f ? 448.0f / M : 1.0f;
+    c[rt] = us.scale_log2 * (M > 0.0f ? M / 448.0f : 1.0f);
+    auto q = [&](unsigned bits) {  // bf16 bits -> q / s, within the e4m3 range
+      return fminf(fmaxf(__builtin_bit_cast(float, bits) * inv, -448.0f), 448.0f);
+    };
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {  // dword k: elements 4 k .. 4 k + 3 of the lane's 32
+        const unsigned x0 = lat[rt][b][k >> 1][2 * (k & 1)], x1 = lat[rt][b][k >> 1][2 * (k & 1) + 1];
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(q(x0 << 16), q(x0 & 0xffff0000u), 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(q(x1 << 16), q(x1 & 0xffff0000u), v, true);
+        q8.lat[rt][b][k] = v;
+      }
+    bf16x8 r;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const unsigned x = rope[rt][w];
+      r[2 * w] = (__bf16)(__builtin_bit_cast(float, x << 16) * inv);
+      r[2 * w + 1] = (__bf16)(__builtin_bit_cast(float, x & 0xffff0000u) * inv);
+    }
+    // the rope fragment moves to its AGPR home through LDS (a lane-private
+    // 16-byte slot in the second half of the 16 NRT KB exchange area, past the
+    // scale exchange), so no VGPR copy of it stays live
+    static_assert(8192 * NRT + kWaves * NRT * 64 * 16 <= 2 * kWaves * NRT * 2 * 1024, "exchange area");
+    lds_u8* slot = (lds_u8*)xs + 8192 * NRT + ((wave * NRT + rt) * 64 + (threadIdx.x & 63)) * 16;
+    *(bf16x8*)slot = r;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\tds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=a"(q8.rope[rt]) : "v"(slot) : "memory");
+  }
 }
 
 template <bool FP8, int NRT, int DH, bool PAGED>
@@ -951,38 +1218,49 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
     const int rv = row < us.RU ? row : us.RU - 1;
     lim[rt] = min(us.hi_eff - 1, us.tail0 + (us.rowb0 + rv) / us.H) - us.uc.lo;
   }
-  const FragBases fb = frag_bases(l16, g);
   lds_u8* lds = (lds_u8*)smem;
-  float* xs = (float*)(smem + kRing * kTileBytes);
+  float* xs = (float*)(smem + kRing * tile_bytes<FP8>());
 
-  // Rows past the unit hold zero Q (their outputs are never written); a row
-  // group with no row of the unit only stages (unit_staging_only).
-  bf16x8 qf[NRT][9];
-  load_q<NRT, DH>(us, grow0, l16, g, qf);
   // per-lane softmax state: lane owns unit row grow0 + 16 rt + l16
   float m_run[NRT], l_run[NRT];
   f32x4 oacc[16][NRT];
+  auto run = [&](const auto& fb, const auto& qf, const float (&c)[NRT]) {
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.0f;
+    for (int rt = 0; rt < NRT; ++rt) {
+      m_run[rt] = -INFINITY;
+      l_run[rt] = 0.0f;
+    }
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc)
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) zero_o(oacc[cc][rt]);
+    if (!wave_active) {  // a row group with no row of the unit only stages
+      unit_staging_only<FP8, NRT, PAGED>(us, lds, tid);
+      return;
+    }
+    unit_pipeline<FP8, NRT, DH, PAGED>(us, lds, xs, wave, fb, qf, c, oacc, m_run, l_run, lim, tid,
+                                       g, lane);
+    epilogue<NRT, DH>(us, grow0, l16, g, oacc, m_run, l_run);
+  };
+  if constexpr (FP8) {
+    QFrag8<NRT> q8;
+    float c[NRT];
+    load_q8<NRT, DH>(us, grow0, l16, g, wave, xs, q8, c);
+    run(frag_bases8<DH>(l16, g), q8, c);
+  } else {
+    // Rows past the unit hold zero Q (their outputs are never written).
+    bf16x8 qf[NRT][9];
+    load_q<NRT, DH>(us, grow0, l16, g, qf);
+    float c[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) c[rt] = us.scale_log2;
+    run(frag_bases(l16, g), qf, c);
   }
-#pragma unroll
-  for (int c = 0; c < 16; ++c)
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) zero_o(oacc[c][rt]);
-
-  if (!wave_active) {
-    unit_staging_only<FP8, NRT, PAGED>(us, lds, tid);
-    return;
-  }
-  unit_pipeline<FP8, NRT, DH, PAGED>(us, lds, xs, wave, fb, qf, oacc, m_run, l_run, lim, tid, g, lane);
-  epilogue<NRT, DH>(us, grow0, l16, g, oacc, m_run, l_run);
 }
 
-template <int NRT>
+template <bool FP8, int NRT>
 constexpr int main_lds_bytes() {
-  return kRing * kTileBytes + 2 * kWaves * NRT * 2 * 1024;  // tile ring + 2 exchange buffers
+  return kRing * tile_bytes<FP8>() + 2 * kWaves * NRT * 2 * 1024;  // tile ring + 2 exchange buffers
 }
 
 // One kernel per (KV dtype, row tiles per row group, KV layout): a kernel holds
@@ -990,7 +1268,7 @@ constexpr int main_lds_bytes() {
 // constrains the other.
 template <bool FP8, int NRT, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_main(const MainArgs args) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[main_lds_bytes<NRT>()];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[main_lds_bytes<FP8, NRT>()];
   if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1)
     unit_body<FP8, NRT, 1, PAGED>(args, smem);
   else
