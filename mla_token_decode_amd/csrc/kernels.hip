@@ -824,9 +824,21 @@ __device__ __forceinline__ void pv_phase8(lds_u8* vbase, const bf16x8 (&pf)[NRT]
     static_for<NRT>([&](auto rc) {
       constexpr int rt = decltype(rc)::value;
       mfma_o(oacc[c][rt], vf[c & 1], pf[rt]);
-      if constexpr (rt == 0 && c + 1 < 16) {
-        vf[(c + 1) & 1] = cvt(vr[(c + 1) % (DV + 1)]);
-        if constexpr (NRT < 3) asm volatile("s_nop 1" : "+v"(vf[(c + 1) & 1]) :: "memory");
+      if constexpr (c + 1 < 16) {
+        // the 4 conversions of column tile c + 1 spread over tile c's MFMAs
+        // (an MFMA hides about one); the last one is padded before its use
+        constexpr int lo = rt == 0 ? 0 : (NRT == 3 ? rt + 1 : 2 * rt);
+        constexpr int hi = rt + 1 == NRT ? 4 : (NRT == 3 ? rt + 2 : 2 * rt + 2);
+        const u32x2 w = __builtin_bit_cast(u32x2, vr[(c + 1) % (DV + 1)]);
+        u32x4 x = __builtin_bit_cast(u32x4, vf[(c + 1) & 1]);
+        static_for<4>([&](auto ec) {
+          constexpr int e = decltype(ec)::value;
+          if constexpr (e >= lo && e < hi)
+            x[e] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                                    w[e >> 1], 1.0f, (e & 1) != 0));
+        });
+        vf[(c + 1) & 1] = __builtin_bit_cast(bf16x8, x);
+        if constexpr (rt + 1 == NRT) asm volatile("s_nop 1" : "+v"(vf[(c + 1) & 1]) :: "memory");
       }
       slice(std::integral_constant<int, c * NRT + rt>{});
       __builtin_amdgcn_sched_barrier(0);
