@@ -1138,9 +1138,10 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
 }
 
 // fp8 Q: per row, the latent columns are quantised to e4m3 with the scale
-// s = max |q latent| / 448 (round to nearest even; the row's scores then carry
-// the factor s, folded into the row's softmax constant c = c0 s), the rope
-// columns become bf16 of q / s.  The two waves of a pair hold halves of each
+// s = max(max |q latent|, 2^-64 max |q rope|) / 448 (round to nearest even; the
+// row's scores then carry the factor s, folded into the row's softmax
+// constant c = c0 s), the rope columns become bf16 of q / s (the rope term of
+// the scale keeps q / s finite when the latent part is vanishingly small).  The two waves of a pair hold halves of each
 // row and agree on s through LDS (one barrier, taken by every wave of the
 // workgroup).  Rows past the unit read row RU - 1 (their outputs are never
 // written).
@@ -1173,6 +1174,14 @@ __device__ __forceinline__ void load_q8(const UnitSetup& us, int grow0, int l16,
           m = fmaxf(m, fmaxf(fabsf(__builtin_bit_cast(float, x << 16)),
                              fabsf(__builtin_bit_cast(float, x & 0xffff0000u))));
         }
+    float mr = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const unsigned x = rope[rt][w];
+      mr = fmaxf(mr, fmaxf(fabsf(__builtin_bit_cast(float, x << 16)),
+                           fabsf(__builtin_bit_cast(float, x & 0xffff0000u))));
+    }
+    m = fmaxf(m, mr * 0x1p-64f);
     half_max[rt] = wave_max_across_groups(m);
     if (g == 0) xs[(wave * NRT + rt) * 16 + l16] = half_max[rt];
   }

@@ -193,3 +193,28 @@ def test_workload_peaked_sampled_rows(name):
     do, dl, mo = gu.compare(o.reshape(-1, 512)[rows], lse.reshape(-1)[rows], ro, rl, inp.kv_fp8,
                             f"{name} peaked")
     assert mo > 5 * gu.TOL_O[inp.kv_fp8]  # the check is discriminating
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_query_rows_of_very_different_magnitudes(fp8):
+    """Query rows scaled by powers of two from 2^-16 to 2^4, all-zero rows, and
+    rows whose latent part is vanishingly small next to their rope part: the
+    fp8 path quantises Q per row, so each row's scale must follow its own
+    magnitude (and stay finite)."""
+    H, q_len, kv_len = 12, [8, 3], [2000, 700]
+    inp = gen.peaked_inputs(gen.random_inputs(H, q_len, kv_len, fp8, seed=29), beta=10.0, seed=6)
+    q = gen.f32_from_bf16_bits(inp.q_bits).astype(np.float32)
+    rows = q.shape[0] * H
+    qr = q.reshape(rows, gen.DQK)
+    k = np.arange(rows) % 21 - 16  # 2^-16 .. 2^4, exact in bf16
+    qr *= np.float32(2.0) ** k[:, None].astype(np.float32)
+    qr[5] = 0.0
+    qr[40] = 0.0
+    qr[17, :gen.DV] *= np.float32(2.0 ** -100)  # latent ~1e-31 next to an O(1) rope part
+    qr[63, :gen.DV] = 0.0                          # rope part only
+    inp = gen.Inputs(H, inp.q_len, inp.kv_len, gen.bf16_bits_from_f32(q), inp.kv, inp.kv_fp8,
+                     inp.kv_scale)
+    ro, rl = gu.oracle_full(inp)
+    for splits in (1, 4):
+        o, lse, plan = gu.run_gpu(inp, force_splits=splits)
+        gu.compare(o, lse, ro, rl, fp8, f"row magnitudes splits={splits}")
