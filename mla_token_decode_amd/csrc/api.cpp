@@ -206,7 +206,7 @@ mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const
   a.lse = lse;
   a.part_lse = plan->workspace_bytes ? static_cast<float*>(workspace) : nullptr;
   a.part_o = plan->workspace_bytes
-                 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->part_o_offset)
+                 ? reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + plan->part_o_offset)
                  : nullptr;
   const double log2e = 1.4426950408889634;
   a.scale_log2 = static_cast<float>(static_cast<double>(sm_scale) * (fp8 ? kv_scale : 1.0) * log2e);
@@ -297,23 +297,26 @@ mla_status mla_decode_reduce(const mla_plan* plan, const void* workspace, void* 
   ReduceArgs a;
   std::memset(&a, 0, sizeof a);
   a.part_lse = static_cast<const float*>(workspace);
-  a.part_o = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + plan->part_o_offset);
+  a.part_o =
+      reinterpret_cast<const uint16_t*>(static_cast<const char*>(workspace) + plan->part_o_offset);
   a.o = static_cast<uint16_t*>(o);
   a.lse = lse;
   a.H = plan->H;
   for (const Launch& ln : plan->launches) {
     if (ln.num_split_rows == 0) continue;
-    int ns = 0, rows = 0;
+    int ns = 0, rows = 0, smax = 0;
     for (int b = ln.seq_begin; b < ln.seq_end; ++b) {
       const SeqDesc& d = plan->seqs[b];
       if (d.S <= 1) continue;
       a.seqs[ns] = d;
       a.row0[ns] = rows;
       rows += d.T * d.R;
+      smax = d.S > smax ? d.S : smax;
       ++ns;
     }
     a.num_seqs = ns;
     a.num_rows = rows;
+    a.max_splits = smax;
     hipError_t e = launch_reduce(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
       set_error("reduce kernel launch failed: %s", hipGetErrorString(e));

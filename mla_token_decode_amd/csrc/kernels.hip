@@ -51,9 +51,11 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = 4;
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer: range-checked, zero on OOB
 // Softmax reference slack in log2 units: P = 2^(x - m_ref) may reach 2^60
-// (bf16 P and fp32 sums have the range); a larger jump moves the reference
-// and rescales O and l.
-constexpr float kLazyOctaves = 60.0f;
+// with bf16 P (bf16 P and fp32 sums have the range) and 2^8 with e4m3 P (fp8
+// KV: its largest finite value is 448); a larger jump moves the reference and
+// rescales O and l.
+template <bool FP8P>
+constexpr float lazy_octaves() { return FP8P ? 8.0f : 60.0f; }
 
 // LDS holds every KV tile as bf16 rows: 1152 bytes = 72 chunks of 16 B,
 // physical chunk = logical chunk XOR swz(key) inside aligned groups of 8
@@ -469,6 +471,11 @@ __device__ __forceinline__ void mfma_s8(f32x4& acc, const i32x8& k, const i32x8&
 __device__ __forceinline__ void mfma_o(f32x4& acc, const bf16x8& v, const bf16x8& p) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
 }
+// fp8 KV: O^T += V^T . P^T with V as the cache's e4m3 codes and P as e4m3;
+// both operands hold 8 keys per lane in the same order as the bf16 form.
+__device__ __forceinline__ void mfma_o8(f32x4& acc, const i32x2& v, const i32x2& p) {
+  asm volatile("v_mfma_f32_16x16x32_fp8_fp8 %0, %1, %2, %0" : "+a"(acc) : "v"(v), "v"(p));
+}
 // O = 0, defined in the AGPR file (an MFMA of zeros), so that no definition of
 // O lives in VGPRs.  The zero operand is written by VALU moves just before:
 // an MFMA must not read a VGPR within 2 wait states of its VALU write, and
@@ -531,7 +538,7 @@ struct UnitSetup {
   uint16_t* o;
   float* lse;
   float* part_lse;
-  float* part_o;
+  uint16_t* part_o;
 };
 
 template <bool FP8>
@@ -659,10 +666,15 @@ __device__ __forceinline__ void epilogue(const UnitSetup& us, int grow0,
       const bool empty = !(lt > 0.0f);
       const float inv = empty ? 0.0f : us.o_scale / lt;
       if (valid) {
-        float* pp = us.part_o + prow * kDv + 256 * DH + 4 * g;
+        uint16_t* pp = us.part_o + prow * kDv + 256 * DH + 4 * g;
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
-          *(f32x4*)(pp + 16 * c) = empty ? f32x4{0.f, 0.f, 0.f, 0.f} : oacc[c][rt] * inv;
+        for (int c = 0; c < 16; ++c) {
+          const f32x4 o4 = empty ? f32x4{0.f, 0.f, 0.f, 0.f} : oacc[c][rt] * inv;
+          uint2 pk;
+          pk.x = pack_bf16x2(o4[0], o4[1]);
+          pk.y = pack_bf16x2(o4[2], o4[3]);
+          *(uint2*)(pp + 16 * c) = pk;
+        }
         if (g == 0 && DH == 0)
           us.part_lse[prow] = empty ? -INFINITY : (m_run[rt] + log2f(lt)) * ln2;
       }
@@ -795,51 +807,40 @@ __device__ __forceinline__ void score_phase8(lds_u8* tile, const FragBases8& fb,
   });
 }
 
-template <int DH, int DV>
-__device__ __forceinline__ void issue_v_head8(i32x2 (&vr)[DV + 1], lds_u8* vbase) {
+template <int DH, int DV, int NSL>
+__device__ __forceinline__ void issue_v_head8(i32x2 (&vr)[NSL], lds_u8* vbase) {
   static_for<DV>([&](auto cc) {
     constexpr int c = decltype(cc)::value;
     issue_v8<DH, c>(vr[c], vbase);
   });
 }
 
-// fp8 PV phase: as pv_phase, with one 8-bit transposing read per V fragment,
-// converted to bf16 (exact).  The conversion of column tile c + 1 runs
-// between the MFMAs of column tile c, so the MFMAs never wait for it.
+// fp8 PV phase: as pv_phase, with one 8-bit transposing read per V fragment
+// feeding the fp8 MFMA directly (P is e4m3 too).  The read ring has DV + 2
+// slots, so a read never targets the registers of the column tile whose
+// MFMAs were issued just before it.
+template <int DV>
+constexpr int v8_slots() { return DV + 2; }
+
 template <int NRT, int DH, int DV, typename W>
-__device__ __forceinline__ void pv_phase8(lds_u8* vbase, const bf16x8 (&pf)[NRT],
-                                          f32x4 (&oacc)[16][NRT], i32x2 (&vr)[DV + 1], W&& slice) {
-  static_assert(DV >= 1 && DV < 16, "read-ahead depth");
-  auto cvt = [](const i32x2& r) {
-    return __builtin_bit_cast(bf16x8, fp8x8_to_bf16(__builtin_bit_cast(u32x2, r)));
-  };
-  bf16x8 vf[2];
-  wait_lds1<DV - 1>(vr[0]);  // reads 0 .. DV-1 were issued before the score phase
-  vf[0] = cvt(vr[0]);
-  asm volatile("s_nop 1" : "+v"(vf[0]) :: "memory");  // VALU writes (vf, P) before the MFMAs
+__device__ __forceinline__ void pv_phase8(lds_u8* vbase, const i32x2 (&pf)[NRT],
+                                          f32x4 (&oacc)[16][NRT], i32x2 (&vr)[v8_slots<DV>()],
+                                          W&& slice) {
+  static_assert(DV >= 1 && DV < 15, "read-ahead depth");
+  constexpr int NSL = v8_slots<DV>();
+  asm volatile("s_nop 1" ::: "memory");  // last VALU write of P before the first O MFMA
   static_for<16>([&](auto cc) {
     constexpr int c = decltype(cc)::value;
-    if constexpr (c + DV < 16) issue_v8<DH, c + DV>(vr[(c + DV) % (DV + 1)], vbase);
-    if constexpr (c + 1 < 16) wait_lds1<(c + DV < 16) ? DV - 1 : 14 - c>(vr[(c + 1) % (DV + 1)]);
+    constexpr int cur = c % NSL;
+    if constexpr (c + DV < 16) {  // reads 0 .. DV-1 were issued before the score phase
+      issue_v8<DH, c + DV>(vr[(c + DV) % NSL], vbase);
+      wait_lds1<DV>(vr[cur]);
+    } else {
+      wait_lds1<15 - c>(vr[cur]);
+    }
     static_for<NRT>([&](auto rc) {
       constexpr int rt = decltype(rc)::value;
-      mfma_o(oacc[c][rt], vf[c & 1], pf[rt]);
-      if constexpr (c + 1 < 16) {
-        // the 4 conversions of column tile c + 1 spread over tile c's MFMAs
-        // (an MFMA hides about one); the last one is padded before its use
-        constexpr int lo = rt == 0 ? 0 : (NRT == 3 ? rt + 1 : 2 * rt);
-        constexpr int hi = rt + 1 == NRT ? 4 : (NRT == 3 ? rt + 2 : 2 * rt + 2);
-        const u32x2 w = __builtin_bit_cast(u32x2, vr[(c + 1) % (DV + 1)]);
-        u32x4 x = __builtin_bit_cast(u32x4, vf[(c + 1) & 1]);
-        static_for<4>([&](auto ec) {
-          constexpr int e = decltype(ec)::value;
-          if constexpr (e >= lo && e < hi)
-            x[e] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
-                                                    w[e >> 1], 1.0f, (e & 1) != 0));
-        });
-        vf[(c + 1) & 1] = __builtin_bit_cast(bf16x8, x);
-        if constexpr (rt + 1 == NRT) asm volatile("s_nop 1" : "+v"(vf[(c + 1) & 1]) :: "memory");
-      }
+      mfma_o8(oacc[c][rt], vr[cur], pf[rt]);
       slice(std::integral_constant<int, c * NRT + rt>{});
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -850,7 +851,7 @@ __device__ __forceinline__ void pv_phase8(lds_u8* vbase, const bf16x8 (&pf)[NRT]
 // P = 2^(c s - m_run) with c = sm_scale * kv_scale * log2(e) > 0 (fp8: times the
 // row's Q scale, c is per row); the first
 // tile that shows a row a key sets its reference, which moves only when a
-// tile maximum exceeds it by more than kLazyOctaves (then O and l are
+// tile maximum exceeds it by more than lazy_octaves (then O and l are
 // rescaled: rare).  Whether any row of the wave needs that is decided from
 // each lane's own maximum over its 8 keys (a row's maximum exceeds a bound
 // exactly when one of its lanes' does), so the cross-lane row maximum is only
@@ -868,12 +869,14 @@ struct SoftTile {
   bool jump;
 };
 
-template <int NRT, int PH>
+template <int NRT, int PH, typename PT>
 __device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, f32x4 (&sfull)[2][NRT],
-                                              bf16x8 (&pf)[NRT], float (&m_run)[NRT],
+                                              PT (&pf)[NRT], float (&m_run)[NRT],
                                               float (&l_run)[NRT], f32x4 (&oacc)[16][NRT],
                                               const int (&lim)[NRT], int k0, bool edge,
                                               const float (&c)[NRT], int g, lds_u8* spill) {
+  constexpr bool kFp8P = std::is_same<PT, i32x2>::value;
+  constexpr float kLazy = lazy_octaves<kFp8P>();
   if constexpr (PH == 0) {  // keys past a row's causal limit (last tiles of a chunk only)
     w.jump = false;
     if (edge) {
@@ -892,7 +895,7 @@ __device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, f32x4 (&sfull)[2
     constexpr int rt = PH - 1;
     const f32x4 a = sfull[0][rt], b = sfull[1][rt];
     w.mx[rt] = max2(max3(a[0], a[1], a[2]), max3(a[3], b[0], max3(b[1], b[2], b[3])));
-    w.jump = w.jump || w.mx[rt] * c[rt] > m_run[rt] + kLazyOctaves;
+    w.jump = w.jump || w.mx[rt] * c[rt] > m_run[rt] + kLazy;
   } else if constexpr (PH == NRT + 1) {  // wave vote; rare: row maxima, references, rescale
     if (__builtin_amdgcn_ballot_w64(w.jump) != 0) {  // wave-uniform
       asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // O MFMAs retired
@@ -900,7 +903,7 @@ __device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, f32x4 (&sfull)[2
       for (int rt = 0; rt < NRT; ++rt) {
         const float mx = wave_max_across_groups(w.mx[rt]) * c[rt];
         const bool first = m_run[rt] == -INFINITY;  // O and l are still 0
-        const bool jump = !first && mx > m_run[rt] + kLazyOctaves;
+        const bool jump = !first && mx > m_run[rt] + kLazy;
         if (__builtin_amdgcn_ballot_w64(jump) != 0) {
           const float f = jump ? __builtin_amdgcn_exp2f(m_run[rt] - mx) : 1.0f;
           l_run[rt] *= f;
@@ -914,15 +917,19 @@ __device__ __forceinline__ void softmax_slice(SoftTile<NRT>& w, f32x4 (&sfull)[2
         asm volatile("" : "+v"(m_run[rt]), "+v"(w.nmu[rt]));
       }
     }
-  } else if constexpr (PH < 5 * NRT + 2) {  // P of 2 keys of one row tile: c s - m <= kLazyOctaves
+  } else if constexpr (PH < 5 * NRT + 2) {  // P of 2 keys of one row tile: c s - m <= kLazy
     constexpr int j = PH - (NRT + 2);
     constexpr int rt = j / 4, kt = (j / 2) % 2, h = j % 2;
     // v_exp_f32: results below the fp32 normal range flush to 0
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sfull[kt][rt][2 * h], c[rt], w.nmu[rt]));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sfull[kt][rt][2 * h + 1], c[rt], w.nmu[rt]));
     w.psum[rt] = (j % 4 == 0) ? p0 + p1 : w.psum[rt] + (p0 + p1);
-    pf[rt][4 * kt + 2 * h] = (__bf16)p0;
-    pf[rt][4 * kt + 2 * h + 1] = (__bf16)p1;
+    if constexpr (kFp8P)  // keys 16 kt + 4 g + 2 h, +1 -> bytes 2 h, 2 h + 1 of dword kt
+      pf[rt][kt] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pf[rt][kt], h != 0);
+    else {
+      pf[rt][4 * kt + 2 * h] = (__bf16)p0;
+      pf[rt][4 * kt + 2 * h + 1] = (__bf16)p1;
+    }
   } else {
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) l_run[rt] += w.psum[rt];
@@ -1044,8 +1051,8 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         sfull[kt][rt] = *(const f32x4*)(peer + ((rt * 2 + kt) * 64 + lane) * 4);
   }
 
-  typename std::conditional<FP8, i32x2, VRaw>::type vr[DV + 1];
-  bf16x8 pf[NRT];
+  typename std::conditional<FP8, i32x2, VRaw>::type vr[FP8 ? v8_slots<DV>() : DV + 1];
+  typename std::conditional<FP8, i32x2, bf16x8>::type pf[NRT];  // P^T: e4m3 with fp8 KV
   SoftTile<NRT> sw;
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) sw.nmu[rt] = 0.0f;  // references not set yet (m_run = -inf)
@@ -1317,6 +1324,12 @@ __device__ __forceinline__ float wave_max64(float v) {
   return v;
 }
 
+// 4 bf16 (two dwords, element 0 in the low half of the first) -> fp32, exact.
+__device__ __forceinline__ f32x4 bf16x4_to_f32(uint2 pk) {
+  return f32x4{__builtin_bit_cast(float, pk.x << 16), __builtin_bit_cast(float, pk.x & 0xffff0000u),
+               __builtin_bit_cast(float, pk.y << 16), __builtin_bit_cast(float, pk.y & 0xffff0000u)};
+}
+
 __device__ __forceinline__ float merge_weight(float ls, float M) {
   return ls == -INFINITY ? 0.0f : __expf(ls - M);
 }
@@ -1367,11 +1380,11 @@ __global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_kernel(const Re
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float W = 0.0f;
-  const float* po = args.part_o + kRedCols * cb + 4 * cg;
+  const uint16_t* po = args.part_o + kRedCols * cb + 4 * cg;
 #pragma unroll 8
   for (int s = part; s < S; s += kRedParts) {
     const int64_t prow = pbase + (int64_t)s * R;
-    const f32x4 v = *(const f32x4*)(po + prow * kDv);
+    const f32x4 v = bf16x4_to_f32(*(const uint2*)(po + prow * kDv));
     const float w = merge_weight(args.part_lse[prow], M);
     W += w;
     acc += w * v;
@@ -1383,6 +1396,60 @@ __global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_kernel(const Re
   const int64_t orow = (int64_t)sd.q_row0 + (int64_t)t * R + r;
   merge_finish(red_acc, red_w, cg, M, args.o + orow * kDv + kRedCols * cb, args.lse + orow,
                cb == 0 && cg == 0);
+}
+
+// Split-KV merge for launches whose sequences have few chunks (S <= 16, e.g.
+// many tiles of short sequences): the wide layout above would leave most of
+// its 16 parts idle and launch 8 blocks per row.  Here one thread owns 4
+// columns of one row (128 threads per row, 2 rows per block) and folds the
+// row's S chunks itself in ascending order, its loads in flight together.
+constexpr int kRedSmallMaxS = 16;
+
+__global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_small_kernel(const ReduceArgs args) {
+  constexpr int kThreadsPerRow = kDv / 4;
+  const int gr = blockIdx.x * (kRedThreads / kThreadsPerRow) + threadIdx.x / kThreadsPerRow;
+  if (gr >= args.num_rows) return;
+  int b = 0;
+  while (b + 1 < args.num_seqs && args.row0[b + 1] <= gr) ++b;
+  const SeqDesc& sd = args.seqs[b];
+  const int local = gr - args.row0[b];
+  const int R = sd.R;
+  const int t = local / R;
+  const int r = local % R;
+  const int S = sd.S;
+  const int64_t pbase = (int64_t)sd.part_row0 + (int64_t)t * S * R + r;
+  const int cg = threadIdx.x % kThreadsPerRow;
+
+  float ls[kRedSmallMaxS];
+  f32x4 v[kRedSmallMaxS];
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kRedSmallMaxS; ++s) {
+    if (s < S) {
+      const int64_t prow = pbase + (int64_t)s * R;
+      ls[s] = args.part_lse[prow];
+      v[s] = bf16x4_to_f32(*(const uint2*)(args.part_o + prow * kDv + 4 * cg));
+      M = fmaxf(M, ls[s]);
+    }
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float W = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kRedSmallMaxS; ++s) {
+    if (s < S) {
+      const float w = merge_weight(ls[s], M);
+      W += w;
+      acc += w * v[s];
+    }
+  }
+  const bool empty = !(W > 0.0f);  // no chunk shows this row a key
+  const float inv = empty ? 0.0f : 1.0f / W;
+  const int64_t orow = (int64_t)sd.q_row0 + (int64_t)t * R + r;
+  uint2 pk;
+  pk.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  pk.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *(uint2*)(args.o + orow * kDv + 4 * cg) = pk;
+  if (cg == 0) args.lse[orow] = empty ? -INFINITY : M + __logf(W);
 }
 
 // Combination of per-shard results (bf16 O, fp32 LSE) with the layout and the
@@ -1411,9 +1478,7 @@ __global__ __launch_bounds__(kRedThreads) void mla_merge_shards_kernel(const Mer
   for (int s = part; s < W; s += kRedParts) {
     const float ls = args.lse_shards[s * rows + row];
     if (ls == -INFINITY) continue;  // a shard that shows the row no key: its O is not read
-    const uint2 pk = *(const uint2*)(po + (s * rows + row) * kDv);
-    const f32x4 v = {__builtin_bit_cast(float, pk.x << 16), __builtin_bit_cast(float, pk.x & 0xffff0000u),
-                     __builtin_bit_cast(float, pk.y << 16), __builtin_bit_cast(float, pk.y & 0xffff0000u)};
+    const f32x4 v = bf16x4_to_f32(*(const uint2*)(po + (s * rows + row) * kDv));
     const float w = __expf(ls - M);
     Wsum += w;
     acc += w * v;
@@ -1462,9 +1527,15 @@ hipError_t launch_main_contiguous(const MainArgs& a, bool fp8, int nrt, hipStrea
 
 #ifndef MLA_PAGED_KV
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
-  const int grid = (kDv / kRedCols) * a.num_rows;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_decode_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, stream, a);
+  if (a.num_rows == 0) return hipSuccess;
+  if (a.max_splits <= kRedSmallMaxS) {
+    constexpr int kRowsPerBlock = kRedThreads / (kDv / 4);
+    const int grid = (a.num_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL(mla_decode_reduce_small_kernel, dim3(grid), dim3(kRedThreads), 0, stream, a);
+  } else {
+    const int grid = (kDv / kRedCols) * a.num_rows;
+    hipLaunchKernelGGL(mla_decode_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -72,7 +72,7 @@ double plan_cost(const std::vector<int32_t>& q_len, const std::vector<int32_t>& 
     const int32_t NRB = (R + kMaxUnitRows - 1) / kMaxUnitRows;
     const int64_t S = (n + L - 1) / L;
     units += static_cast<int64_t>(T) * NRB * S;
-    const double part = S > 1 ? static_cast<double>(R) * 2.0 * (kDv * 4 + 4) : 0.0;
+    const double part = S > 1 ? static_cast<double>(R) * 2.0 * (kDv * 2 + 4) : 0.0;
     const double unit = static_cast<double>(std::min<int64_t>(L, n)) * row_bytes + part + 65536.0;
     longest = std::max(longest, unit);
   }
@@ -241,7 +241,7 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
   if (part_row > 0) {
     const size_t lse_bytes = static_cast<size_t>(part_row) * sizeof(float);
     plan->part_o_offset = (lse_bytes + 255) / 256 * 256;
-    plan->workspace_bytes = plan->part_o_offset + static_cast<size_t>(part_row) * kDv * sizeof(float);
+    plan->workspace_bytes = plan->part_o_offset + static_cast<size_t>(part_row) * kDv * sizeof(uint16_t);
   } else {
     plan->part_o_offset = 0;
     plan->workspace_bytes = 0;

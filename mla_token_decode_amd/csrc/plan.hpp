@@ -44,7 +44,7 @@ struct MainArgs {
   uint16_t* o;
   float* lse;
   float* part_lse;     // [total partial rows]
-  float* part_o;       // [total partial rows][512]
+  uint16_t* part_o;    // [total partial rows][512] bf16 (normalised partial O)
   float scale_log2;    // sm_scale * kv_scale * log2(e)
   float o_scale;       // kv_scale (fp8) or 1 (bf16)
   const int32_t* page_table;  // paged KV: [batch][pt_stride] page indices; null: contiguous KV
@@ -60,13 +60,13 @@ struct MainArgs {
 
 struct ReduceArgs {
   const float* part_lse;
-  const float* part_o;
+  const uint16_t* part_o;
   uint16_t* o;
   float* lse;
   int32_t H;
   int32_t num_seqs;
   int32_t num_rows;    // split rows covered by this launch
-  int32_t pad_;
+  int32_t max_splits;  // largest S among the launch's sequences (picks the merge layout)
   SeqDesc seqs[kMaxSeqPerLaunch];
   int32_t row0[kMaxSeqPerLaunch];  // first reduce row of each sequence in this launch
 };
