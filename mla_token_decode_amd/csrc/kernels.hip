@@ -517,9 +517,12 @@ __device__ __forceinline__ void scale_o(f32x4& acc, float f, lds_u8* spill) {
 // contents, discarded).
 
 constexpr int kRing = 3;
-// Where the staging of tile t + 2 runs: between the score MFMAs (which carry
-// only the 7 softmax slices) rather than between the PV MFMAs.
-constexpr bool kStageWithScores = true;
+// Where the staging of tile t + 2 runs: bf16 KV between the score MFMAs
+// (its PV phase already carries two transposing reads per column tile); fp8
+// KV between the PV MFMAs (48 of them with one read per column tile and no
+// VALU work, against 6 NRT score MFMAs that carry the softmax).
+template <bool FP8>
+constexpr bool stage_with_scores() { return !FP8; }
 
 struct UnitCtx {
   int lo, nkeys, ntiles, min_lim;
@@ -699,7 +702,7 @@ __device__ __forceinline__ void slices_at(F&& f) {
 template <int NRT, bool FP8>
 constexpr int k_ahead() { return NRT == 1 ? 4 : NRT == 2 ? 2 : 1; }
 template <int NRT, bool FP8>
-constexpr int v_ahead() { return NRT == 1 ? 7 : FP8 ? (NRT == 2 ? 6 : 3) : (NRT == 2 ? 4 : 1); }
+constexpr int v_ahead() { return NRT == 1 ? 7 : FP8 ? (NRT == 2 ? 6 : 2) : (NRT == 2 ? 4 : 1); }
 
 // Score phase: S^T partial (this wave's 288 columns) of one tile; K fragments
 // DK steps ahead; pre(i) runs before MFMA i and slice(i) after it.
@@ -1108,7 +1111,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
             constexpr int s = decltype(sc)::value;
             softmax_slice<NRT, s>(sw, sfull, pf, m_run, l_run, oacc, lim, k0, edge, c, g, spill);
           });
-          if constexpr (kStageWithScores) slices_at<kStageSlices, kScoreMfma, i>(stage_slice);
+          if constexpr (stage_with_scores<FP8>()) slices_at<kStageSlices, kScoreMfma, i>(stage_slice);
         });
 
         // O of tile t  ||  exchange write of tile t + 1 (and the staging)
@@ -1122,7 +1125,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
             for (int kt = 0; kt < 2; ++kt)
               *(f32x4*)(mine + ((s * 2 + kt) * 64 + lane) * 4) = sacc[kt][s];
           });
-          if constexpr (!kStageWithScores) slices_at<kStageSlices, kPvMfma, i>(stage_slice);
+          if constexpr (!stage_with_scores<FP8>()) slices_at<kStageSlices, kPvMfma, i>(stage_slice);
         };
         if constexpr (FP8)
           pv_phase8<NRT, DH, DV>(vbase, pf, oacc, vr, pv_slice);
