@@ -1,6 +1,6 @@
 // MLA speculative-verify decode kernels for gfx950 (MI355X, CDNA4).
 //
-// Main kernel: one workgroup (4 waves, 256 threads) per work unit = up to 64
+// Main kernel: one workgroup (4 waves, 256 threads) per work unit = up to 96
 // rows of one folded tile (F verify tokens x H heads, contiguous in Q) and one
 // split-KV chunk of its sequence.  The chunk is streamed once from HBM and
 // shared by all rows of the unit -- the fold_sq idea of "[Kimi-K3] Allow DSPARK
@@ -8,24 +8,27 @@
 // paragraph "Why".  Split chunks write normalised partials that the reduce
 // kernel merges (same PR, section "GPU timeline").
 //
-// Loader: every thread keeps two (bf16) or three (fp8) 32-key KV tiles in
-// flight in registers (inline-assembly buffer loads with explicit vmcnt
-// waits), then writes each tile into a two-slot LDS ring in the bf16 row
-// layout; fp8-e4m3 rows are converted to bf16 there, once per element
-// (exact), so one compute loop serves both cache formats.  The per-tensor fp8
-// scale is folded into the logit scale and the O epilogue.
+// Loader: every thread keeps one to three 32-key KV tiles in flight in
+// registers (inline-assembly buffer loads with explicit vmcnt waits), then
+// writes each tile into a three-slot LDS ring: bf16 KV as bf16 rows; fp8-e4m3
+// KV with the 512 latent columns kept as e4m3 codes and the 64 rope columns
+// converted (exactly) to bf16.  The per-tensor fp8 scale is folded into the
+// logit scale and the O epilogue.
 //
 // Work split inside a workgroup: wave w = (row group rg = w / 2, half
-// dh = w % 2).  A row group is up to 32 rows (NRT 16-row MFMA tiles); the
+// dh = w % 2).  A row group is up to 48 rows (NRT 16-row MFMA tiles); the
 // wave pair splits the 576 score columns and the 512 value columns in halves:
-//   S^T[key][row] partial = K[:, 288dh:+288] . Q^T   (bf16 MFMA 16x16x32;
-//                  A = K from LDS, B = the wave's Q half held in AGPRs)
+//   S^T[key][row] partial = K[:, 288dh:+288] . Q^T   (bf16 KV: bf16 MFMA
+//                  16x16x32; fp8 KV: fp8 MFMA 16x16x128 on the latent part
+//                  with Q quantised per row, bf16 MFMA on the rope part;
+//                  A = K from LDS, B = the wave's Q half in registers)
 //   the pair sums its two partials through LDS (fp32 a+b == b+a, so both
 //   waves hold bitwise-identical scores, reference, P and row sums)
 //   online softmax: a lane holds 4 keys of ONE row; per-lane running state;
-//                  the base-2 reference moves only for jumps > 60 octaves
+//                  the base-2 reference moves only for large jumps
 //   O^T[256dh + col][row] += V^T . P^T  (A = V^T fragments read with the
-//                  gfx950 transposing LDS loads, B = P in VGPRs, O in AGPRs)
+//                  gfx950 transposing LDS loads, B = P in VGPRs, O in AGPRs;
+//                  bf16 P and V with bf16 KV, e4m3 P and V with fp8 KV)
 #include <hip/hip_runtime.h>
 
 #include <cmath>
