@@ -464,10 +464,14 @@ constexpr bool q_in_agpr(int rt, int j) {
 }
 // fp8 score MFMA, Q (fp8, per-row scaled) in VGPRs: it is computed by VALU
 // instructions, and a VALU-defined operand in AGPRs became a copy per MFMA.
-template <bool ZERO>
+template <bool ZERO, bool QA = false>
 __device__ __forceinline__ void mfma_s8(f32x4& acc, const i32x8& k, const i32x8& q) {
-  if constexpr (ZERO)
+  if constexpr (ZERO && QA)
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "a"(q));
+  else if constexpr (ZERO)
     asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "v"(q));
+  else if constexpr (QA)
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "a"(q));
   else
     asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "v"(q));
 }
@@ -505,7 +509,7 @@ __device__ __forceinline__ void scale_o(f32x4& acc, float f, lds_u8* spill) {
 
 // ---------------------------------------------------------- main kernel
 //
-// Per workgroup: a ring of kRing LDS tile slots and, per tile, one barrier.
+// Per workgroup: a ring of 3 LDS tile slots and, per tile, one barrier.
 // Iteration t of a unit (tile t's full scores are already in registers):
 //   score phase   S^T MFMAs of tile t+1 (K from its slot), interleaved one by
 //                 one with the softmax of tile t (VALU work runs while the
@@ -519,7 +523,12 @@ __device__ __forceinline__ void scale_o(f32x4& acc, float f, lds_u8* spill) {
 // The last iteration computes the scores of a tile past the end (stale slot
 // contents, discarded).
 
-constexpr int kRing = 3;
+// The fp8 kernel of 48-row row groups splits each tile's keys between the two
+// waves of a pair (unit_pipeline8k below) and keeps four tiles in the ring.
+template <bool FP8, int NRT>
+constexpr bool key_split() { return FP8 && NRT == 3; }
+template <bool FP8, int NRT>
+constexpr int ring_slots() { return key_split<FP8, NRT>() ? 4 : 3; }
 // Where the staging of tile t + 2 runs: bf16 KV between the score MFMAs
 // (its PV phase already carries two transposing reads per column tile); fp8
 // KV between the PV MFMAs (48 of them with one read per column tile and no
@@ -637,7 +646,9 @@ __device__ __forceinline__ void load_q(const UnitSetup& us, int grow0, int l16, 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int NRT, int DH>
+// l_run: per-lane partial row sums (summed across the lane groups here), or
+// with TOTAL the rows' whole sums already.
+template <int NRT, int DH, bool TOTAL = false>
 __device__ __forceinline__ void epilogue(const UnitSetup& us, int grow0,
                                          int l16, int g, f32x4 (&oacc)[16][NRT],
                                          const float (&m_run)[NRT], const float (&l_run)[NRT]) {
@@ -645,7 +656,7 @@ __device__ __forceinline__ void epilogue(const UnitSetup& us, int grow0,
   const float ln2 = 0.69314718055994530942f;
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
-    const float lt = wave_sum_across_groups(l_run[rt]);
+    const float lt = TOTAL ? l_run[rt] : wave_sum_across_groups(l_run[rt]);
     const int row = grow0 + 16 * rt + l16;
     const bool valid = row < us.RU;
     if (us.S == 1) {
@@ -980,7 +991,7 @@ __device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* l
       const int t = base + k;
       if (t < u.ntiles) {
         wait_stage<kAhead, FP8>(st[ks]);
-        stage_store<FP8>(st[ks], lds + ((t + 2) % kRing) * tile_bytes<FP8>(), tid);
+        stage_store<FP8>(st[ks], lds + ((t + 2) % ring_slots<FP8, NRT>()) * tile_bytes<FP8>(), tid);
         stage_load<FP8>(st[ks], src.rsrc(t + 2 + NS, prow_next), tid);
         if constexpr (PAGED)
           prow_next = src.barrier_and_page_row(t + 3 + NS);
@@ -1072,9 +1083,10 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         float* mine = xs + (par * kWaves + wave) * kXsWave;
         const float* peer = xs + (par * kWaves + (wave ^ 1)) * kXsWave;
         lds_u8* spill = (lds_u8*)mine + lane * 16;  // free until the exchange write below
-        lds_u8* slot_t = lds + (t % kRing) * TB;
-        lds_u8* slot_n = lds + ((t + 1) % kRing) * TB;
-        lds_u8* slot_s = lds + ((t + 2) % kRing) * TB;
+        constexpr int RING = ring_slots<FP8, NRT>();
+        lds_u8* slot_t = lds + (t % RING) * TB;
+        lds_u8* slot_n = lds + ((t + 1) % RING) * TB;
+        lds_u8* slot_s = lds + ((t + 2) % RING) * TB;
         const int k0 = t * kTK;
         const bool edge = k0 + kTK - 1 > u.min_lim;
         const __amdgpu_buffer_rsrc_t rs_next = src.rsrc(t + 2 + NS, prow_next);
@@ -1234,6 +1246,457 @@ __device__ __forceinline__ void load_q8(const UnitSetup& us, int grow0, int l16,
   }
 }
 
+// ------------------------------------------------ fp8 KV, 48-row row groups
+//
+// The two waves of a pair split each tile's 32 keys instead of the score
+// columns: wave dh computes the full 576-column scores of keys 16 dh .. +15,
+// so no fp32 score exchange is needed and each wave forms the softmax of its
+// own 16 keys only.  Per row tile and lane the pair exchanges one lane maximum
+// (both waves then take the same reference decisions) and one dword of e4m3
+// P (the partner's half of the PV operand: byte e of lane group g is key
+// 4 g + e of the kt = 0 half for e < 4 and of the kt = 1 half otherwise).
+// The PV of tile t runs in iteration t + 1, after the barrier that publishes
+// the partner's P(t); a four-slot ring keeps tile t's V meanwhile.  A
+// reference move found by the softmax of tile t rescales O after the PV of
+// tile t - 1, whose P was formed against the old reference (the deferred O
+// rescale of the r52 kernel in "bench(cake_mla_varq_dcp_decode): drop the
+// package README and add a query-pattern benchmark option" (flashinfer PR
+// #5588), embedded follow-up, section "Summary").
+
+// K fragments of the wave's own 16 keys at full depth: latent block b (fp8
+// MFMA A operand, columns 128 b + 32 g .. +32 as two 16-byte chunks) and rope
+// half h (bf16 MFMA, rope columns 32 h + 8 g .. +8); V as FragBases8.
+struct FragBases8K {
+  int k[4][2];
+  int kr[2];
+  int v;
+};
+
+template <int DH>
+__device__ __forceinline__ FragBases8K frag_bases8k(int l16, int g) {
+  FragBases8K fb;
+  const int key = 16 * DH + l16;
+  const int sw = swz8(key);
+  // the swizzle touches the low 4 bits of the chunk index only, so blocks 2
+  // and 3 sit 256 bytes past blocks 0 and 1 (an immediate offset)
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      fb.k[b][h] = key * kLatBytes8 + 16 * ((8 * b + 2 * g + h) ^ sw);
+      fb.k[b + 2][h] = fb.k[b][h] + 256;
+    }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) fb.kr[h] = kRopeOff8 + key * 128 + 16 * ((4 * h + g) ^ rope_swz(key));
+  const int j = l16 >> 1, h = l16 & 1;
+  const int kv = 16 * (j >> 2) + 4 * g + (j & 3);
+  fb.v = kv * kLatBytes8 + 8 * h + 16 * swz8(kv);
+  return fb;
+}
+
+template <int B>
+__device__ __forceinline__ i32x8 read_k8k(lds_u8* tile, const FragBases8K& fb) {
+  const i32x4 a = *(const i32x4*)(tile + fb.k[B][0]);
+  const i32x4 b = *(const i32x4*)(tile + fb.k[B][1]);
+  return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+template <int H>
+__device__ __forceinline__ bf16x8 read_kr8k(lds_u8* tile, const FragBases8K& fb) {
+  return *(const bf16x8*)(tile + fb.kr[H]);
+}
+
+// Latent blocks 0..2 in VGPRs, block 3 in AGPRs (with the 192 AGPRs of O and
+// the rope fragments, what the register files hold).
+template <int NRT>
+struct QFrag8K {
+  i32x8 lat[NRT][4];    // e4m3 codes of Q / s_row, latent block b (b = 3: AGPRs)
+  bf16x8 rope[NRT][2];  // bf16 of Q / s_row, rope columns 32 h + 8 g .. +8 (AGPRs)
+};
+template <int B>
+constexpr bool lat_in_agpr() { return B == 3; }
+
+// LDS records of the key-split pipeline inside the exchange area (16 bytes
+// per lane): lane maxima [2 parities][waves][64], e4m3 P [2][waves][64], the
+// row sums at the end [waves][64], a per-wave spill slot for the O rescale,
+// and (set-up only) the lane-private slots that move the rope Q fragments to
+// their AGPR home.
+constexpr int kXmOff = 0;
+constexpr int kXpOff = 2 * kWaves * 64 * 16;
+constexpr int kXlOff = kXpOff + 2 * kWaves * 64 * 16;
+constexpr int kSpillOff = kXlOff + kWaves * 64 * 16;
+constexpr int kRopeSlotOff = kSpillOff + kWaves * 64 * 16;
+
+// fp8 Q at full depth: each wave quantises its rows itself (the same scale
+// rule as load_q8, from the whole row: both waves of a pair reach the same
+// scale), one row tile at a time.
+template <int NRT>
+__device__ __forceinline__ void load_q8k(const UnitSetup& us, int grow0, int l16, int g, int wave,
+                                         float* xs, QFrag8K<NRT>& q8, float (&c)[NRT]) {
+  static_assert(kRopeSlotOff + kWaves * NRT * 2 * 64 * 16 <= 2 * kWaves * NRT * 2 * 1024,
+                "exchange area");
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int row = min(grow0 + 16 * rt + l16, us.RU - 1);
+    const uint16_t* qrow = us.q + ((int64_t)us.row0 + row) * kDqk;
+    u32x4 lat[4][4], rope[2];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lat[b][i] = *(const u32x4*)(qrow + 128 * b + 32 * g + 8 * i);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) rope[h] = *(const u32x4*)(qrow + 512 + 32 * h + 8 * g);
+    auto amax2 = [](float m, unsigned x) {
+      return fmaxf(m, fmaxf(fabsf(__builtin_bit_cast(float, x << 16)),
+                            fabsf(__builtin_bit_cast(float, x & 0xffff0000u))));
+    };
+    float m = 0.0f, mr = 0.0f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) m = amax2(m, lat[b][i][w]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) mr = amax2(mr, rope[h][w]);
+    const float M = wave_max_across_groups(fmaxf(m, mr * 0x1p-64f));
+    const float inv = M > 0.0f ? 448.0f / M : 1.0f;
+    c[rt] = us.scale_log2 * (M > 0.0f ? M / 448.0f : 1.0f);
+    auto q = [&](unsigned bits) {  // bf16 bits -> q / s, within the e4m3 range
+      return fminf(fmaxf(__builtin_bit_cast(float, bits) * inv, -448.0f), 448.0f);
+    };
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {  // dword k: elements 4 k .. 4 k + 3 of the lane's 32
+        const unsigned x0 = lat[b][k >> 1][2 * (k & 1)], x1 = lat[b][k >> 1][2 * (k & 1) + 1];
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(q(x0 << 16), q(x0 & 0xffff0000u), 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(q(x1 << 16), q(x1 & 0xffff0000u), v, true);
+        q8.lat[rt][b][k] = v;
+      }
+    // block 3 moves to the AGPR file once, here (an empty statement whose
+    // output lives in AGPRs; the MFMAs read it from there)
+    asm volatile("" : "=a"(q8.lat[rt][3]) : "0"(q8.lat[rt][3]));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 r;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const unsigned x = rope[h][w];
+        r[2 * w] = (__bf16)(__builtin_bit_cast(float, x << 16) * inv);
+        r[2 * w + 1] = (__bf16)(__builtin_bit_cast(float, x & 0xffff0000u) * inv);
+      }
+      lds_u8* slot = (lds_u8*)xs + kRopeSlotOff + (((wave * NRT + rt) * 2 + h) * 64 + lane) * 16;
+      *(bf16x8*)slot = r;
+      asm volatile("s_waitcnt lgkmcnt(0)\n\tds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                   : "=a"(q8.rope[rt][h]) : "v"(slot) : "memory");
+    }
+    // one row tile at a time: the scheduler would otherwise issue every row
+    // tile's loads first and run out of registers
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Score phase of the key-split path: S^T of the wave's 16 keys, per row tile
+// 4 fp8 MFMAs (latent blocks) then 2 bf16 MFMAs (rope halves), row tiles
+// innermost so that NRT - 1 independent MFMAs separate each pair on one
+// accumulator; pre(i) runs before MFMA i and slice(i) after it.
+template <int NRT, typename P, typename W>
+__device__ __forceinline__ void score_phase8k(lds_u8* tile, const FragBases8K& fb,
+                                              const QFrag8K<NRT>& q8, f32x4 (&sacc)[NRT], P&& pre,
+                                              W&& slice) {
+  static_assert(NRT >= 2, "dependent MFMAs need an independent one between them");
+  i32x8 kl[3];  // latent block b in kl[b % 3]: a block is read two steps ahead
+  bf16x8 kr[2];
+  kl[0] = read_k8k<0>(tile, fb);
+  kl[1] = read_k8k<1>(tile, fb);
+  static_for<6>([&](auto sc) {
+    constexpr int st = decltype(sc)::value;
+    if constexpr (st == 0) {
+      kl[2] = read_k8k<2>(tile, fb);
+    } else if constexpr (st == 1) {
+      kl[0] = read_k8k<3>(tile, fb);  // block 0's MFMAs were issued in step 0
+    } else if constexpr (st == 2) {
+      kr[0] = read_kr8k<0>(tile, fb);
+      kr[1] = read_kr8k<1>(tile, fb);
+    }
+    static_for<NRT>([&](auto rc) {
+      constexpr int rt = decltype(rc)::value;
+      constexpr int i = st * NRT + rt;
+      pre(std::integral_constant<int, i>{});
+      if constexpr (st < 4)
+        mfma_s8<st == 0, lat_in_agpr<st>()>(sacc[rt], kl[st % 3], q8.lat[rt][st]);
+      else
+        mfma_s<false, true>(sacc[rt], kr[st - 4], q8.rope[rt][st - 4]);
+      slice(std::integral_constant<int, i>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  });
+}
+
+// Softmax of one tile in the key-split path, by slices: 0 combines the lane
+// maxima of both halves and checks them against the references; 1 is the
+// wave vote (rare: row maxima, references, l rescale, the O rescale left
+// pending); then P of 2 keys of one row tile per slice; the last adds the row
+// sums and publishes this wave's P.
+template <int NRT>
+constexpr int soft_slices_k() { return 2 * NRT + 3; }
+
+template <int NRT>
+struct SoftTileK {
+  float mxc[NRT], nmu[NRT], psum[NRT], pend[NRT];
+  bool jump, pending;
+};
+
+template <int NRT, int PH>
+__device__ __forceinline__ void softmax_slice_k(SoftTileK<NRT>& w, const f32x4 (&sfull)[NRT],
+                                                const float (&own_mx)[NRT], const f32x4& peer_mx,
+                                                int (&pnew)[NRT], float (&m_run)[NRT],
+                                                float (&l_run)[NRT], const float (&c)[NRT],
+                                                i32x4* p_out) {
+  constexpr float kLazy = lazy_octaves<true>();
+  if constexpr (PH == 0) {
+    w.jump = false;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      w.mxc[rt] = max2(own_mx[rt], peer_mx[rt]);
+      w.jump = w.jump || w.mxc[rt] * c[rt] > m_run[rt] + kLazy;
+    }
+  } else if constexpr (PH == 1) {
+    w.pending = false;
+    if (__builtin_amdgcn_ballot_w64(w.jump) != 0) {  // wave-uniform
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const float mx = wave_max_across_groups(w.mxc[rt]) * c[rt];
+        const bool first = m_run[rt] == -INFINITY;  // O and l are still 0
+        const bool jump = !first && mx > m_run[rt] + kLazy;
+        const float f = jump ? __builtin_amdgcn_exp2f(m_run[rt] - mx) : 1.0f;
+        l_run[rt] *= f;
+        w.pend[rt] = f;
+        w.pending = w.pending || __builtin_amdgcn_ballot_w64(jump) != 0;
+        m_run[rt] = (first && mx > -INFINITY) || jump ? mx : m_run[rt];
+        w.nmu[rt] = m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
+        asm volatile("" : "+v"(m_run[rt]), "+v"(w.nmu[rt]));
+      }
+    }
+  } else if constexpr (PH < 2 + 2 * NRT) {  // P of keys 4 g + 2 h, +1: bytes 2 h, 2 h + 1
+    constexpr int j = PH - 2;
+    constexpr int rt = j / 2, h = j % 2;
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sfull[rt][2 * h], c[rt], w.nmu[rt]));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sfull[rt][2 * h + 1], c[rt], w.nmu[rt]));
+    w.psum[rt] = h == 0 ? p0 + p1 : w.psum[rt] + (p0 + p1);
+    pnew[rt] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pnew[rt], h != 0);
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) l_run[rt] += w.psum[rt];
+    i32x4 rec = {0, 0, 0, 0};
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) rec[rt] = pnew[rt];
+    *p_out = rec;
+  }
+}
+
+// The whole KV chunk of a unit in the key-split path (see above).  Same
+// staging, barriers and tile-loop unrolling as unit_pipeline; the exchange
+// records replace the score exchange.
+template <int NRT, int DH, bool PAGED>
+__device__ __forceinline__ void unit_pipeline8k(const UnitSetup& us, lds_u8* lds, float* xs,
+                                                int wave, const FragBases8K& fb,
+                                                const QFrag8K<NRT>& qf, const float (&c)[NRT],
+                                                f32x4 (&oacc)[16][NRT], float (&m_run)[NRT],
+                                                float (&l_run)[NRT], const int (&lim)[NRT], int tid,
+                                                int g, int lane) {
+  constexpr bool FP8 = true;
+  static_assert(NRT == 3, "exchange records hold one dword per row tile, at most 3");
+  constexpr int NS = stage_sets<FP8, NRT>();
+  constexpr int kAhead = (NS - 1) * kPieces;
+  constexpr int DV = v_ahead<NRT, FP8>();
+  constexpr int TB = tile_bytes<FP8>();
+  constexpr int RING = ring_slots<FP8, NRT>();
+  static_assert(RING == 4, "tile t - 1 (V), t, t + 1 (K) and t + 2 (staged) are live together");
+  const UnitCtx u = us.uc;
+  const KvSource<FP8, PAGED> src = kv_source<FP8, PAGED>(us);
+  auto zero_all_o = [&] {
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc)
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) zero_o(oacc[cc][rt]);
+  };
+  if (u.ntiles <= 0) {
+    zero_all_o();
+    return;
+  }
+  unsigned char* xb = (unsigned char*)xs;
+  auto xm_at = [&](int par, int w) { return (f32x4*)(xb + kXmOff + (par * kWaves + w) * 1024) + lane; };
+  auto xp_at = [&](int par, int w) { return (i32x4*)(xb + kXpOff + (par * kWaves + w) * 1024) + lane; };
+  lds_u8* spill = (lds_u8*)(xb + kSpillOff + wave * 1024 + lane * 16);
+
+  // prologue: tiles 0 and 1 into their slots; tile k always travels in set k % NS
+  int64_t pr[NS + 3];
+  prologue_page_rows(src, pr);
+  Stage<FP8> st[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) stage_load<FP8>(st[k], src.rsrc(k, pr[k]), tid);
+  static_for<2>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    wait_stage<kAhead, FP8>(st[j % NS]);
+    stage_store<FP8>(st[j % NS], lds + j * TB, tid);
+    stage_load<FP8>(st[j % NS], src.rsrc(j + NS, pr[j + NS]), tid);
+  });
+  lds_barrier();
+  int64_t prow_next = pr[NS + 2];  // page row of the first tile the loop loads
+
+  // scores of tile t in sc[t % 2] (the loop is unrolled by NS = 2, so the
+  // score MFMAs of tile t + 1 and the softmax of tile t use fixed registers)
+  static_assert(NS % 2 == 0, "tile parity must be static");
+  f32x4 sc[2][NRT];
+  float own_mx[NRT];
+  // scores of tile t1 in sc[t1 % 2]: causal mask (last tiles of a chunk), lane
+  // maxima, published for the partner
+  auto lane_max = [&](auto parc, int t1) {
+    constexpr int par = decltype(parc)::value;
+    f32x4 (&sacc)[NRT] = sc[par];
+    const int k0 = t1 * kTK;
+    if (k0 + kTK - 1 > u.min_lim) {
+      asm volatile("" ::: "memory");  // keep this a branch: interior tiles skip it
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + 16 * DH + 4 * g + i;
+          sacc[rt][i] = key <= lim[rt] ? sacc[rt][i] : -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+      own_mx[rt] = max2(max2(sacc[rt][0], sacc[rt][1]), max2(sacc[rt][2], sacc[rt][3]));
+    *xm_at(t1 & 1, wave) = f32x4{own_mx[0], own_mx[1], own_mx[2], 0.0f};
+  };
+
+  score_phase8k<NRT>(lds, fb, qf, sc[0], [](auto) {}, [](auto) {});
+  asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");  // score MFMAs retire before the reads
+  lane_max(std::integral_constant<int, 0>{}, 0);
+  lds_barrier();
+  f32x4 peer_mx = *xm_at(0, wave ^ 1);
+  i32x4 peer_p = {0, 0, 0, 0};
+
+  zero_all_o();  // here rather than before the prologue: fewer values live across it
+  i32x2 vr[v8_slots<DV>()];
+  i32x2 pf[NRT];
+  int pnew[NRT];
+  SoftTileK<NRT> sw;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    pf[rt] = i32x2{0, 0};  // P of "tile -1": the first PV adds nothing
+    pnew[rt] = 0;
+    sw.nmu[rt] = 0.0f;  // references not set yet (m_run = -inf)
+  }
+  for (int base = 0; base < u.ntiles; base += NS) {
+    static_for<NS>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int ks = (k + 2) % NS;  // staging set of tile t + 2
+      const int t = base + k;
+      if (t < u.ntiles) {
+        // V of tile t - 1 (tile 0's slot at t = 0, where P is 0)
+        lds_u8* vbase = lds + ((t == 0 ? 0 : t - 1) % RING) * TB + fb.v;
+        lds_u8* slot_n = lds + ((t + 1) % RING) * TB;
+        lds_u8* slot_s = lds + ((t + 2) % RING) * TB;
+        const __amdgpu_buffer_rsrc_t rs_next = src.rsrc(t + 2 + NS, prow_next);
+        issue_v_head8<DH, DV>(vr, vbase);
+
+        constexpr int kStageSlices = 1 + 2 * kPieces;
+        auto stage_slice = [&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          if constexpr (s == 0) {
+            wait_stage<kAhead, FP8>(st[ks]);
+          } else if constexpr (s < 1 + kPieces) {
+            stage_store_piece<FP8, s - 1>(st[ks], slot_s, tid);
+          } else {
+            stage_load_piece<FP8, s - 1 - kPieces>(st[ks], rs_next, tid);
+          }
+        };
+
+        // scores of tile t + 1 (into sc[(k + 1) % 2]) || softmax of tile t (sc[k])
+        constexpr int kScoreMfma = 6 * NRT;
+        i32x4* p_out = xp_at(t & 1, wave);
+        score_phase8k<NRT>(slot_n, fb, qf, sc[(k + 1) % 2], [](auto) {}, [&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          slices_at<soft_slices_k<NRT>(), kScoreMfma, i>([&](auto slc) {
+            constexpr int s = decltype(slc)::value;
+            softmax_slice_k<NRT, s>(sw, sc[k], own_mx, peer_mx, pnew, m_run, l_run, c, p_out);
+          });
+        });
+
+        // the partner's half of P(t - 1) joins the PV operand (VALU writes: at
+        // least 2 wait states before the first MFMA reads them)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) pf[rt][1 - DH] = peer_p[rt];
+        asm volatile("s_nop 1" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]));
+
+        // O of tile t - 1  ||  lane maxima of tile t + 1, staging of tile t + 2
+        constexpr int kPvMfma = 16 * NRT;
+        auto pv_slice = [&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          if constexpr (i == 2) {
+            asm volatile("s_nop 15" ::: "memory");  // the score MFMAs have retired
+            lane_max(std::integral_constant<int, (k + 1) % 2>{}, t + 1);
+          }
+          slices_at<kStageSlices, kPvMfma, i>(stage_slice);
+        };
+        pv_phase8<NRT, DH, DV>(vbase, pf, oacc, vr, pv_slice);
+
+        if (sw.pending) {  // rare, wave-uniform: a reference moved at tile t
+          asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // O MFMAs retired
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt)
+            if (__builtin_amdgcn_ballot_w64(sw.pend[rt] != 1.0f) != 0) {
+#pragma unroll
+              for (int cc = 0; cc < 16; ++cc) scale_o(oacc[cc][rt], sw.pend[rt], spill);
+            }
+        }
+
+        if constexpr (PAGED)
+          prow_next = src.barrier_and_page_row(t + 3 + NS);
+        else
+          lds_barrier();
+        // published by the barrier: the partner's P(t) and lane maxima of tile t + 1
+        peer_p = *xp_at(t & 1, wave ^ 1);
+        peer_mx = *xm_at((t + 1) & 1, wave ^ 1);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) pf[rt][DH] = pnew[rt];
+      }
+    });
+  }
+  // PV of the last tile
+  {
+    lds_u8* vbase = lds + ((u.ntiles - 1) % RING) * TB + fb.v;
+    issue_v_head8<DH, DV>(vr, vbase);
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) pf[rt][1 - DH] = peer_p[rt];
+    asm volatile("s_nop 1" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]));
+    pv_phase8<NRT, DH, DV>(vbase, pf, oacc, vr, [](auto) {});
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads issued past the end
+}
+
+// Row sums of the key-split path: each wave of a pair summed its own keys;
+// both waves add the two totals (in either order: the same fp32 result).
+template <int NRT>
+__device__ __forceinline__ void total_row_sums(float* xs, int wave, float (&l_run)[NRT]) {
+  const int lane = threadIdx.x & 63;
+  unsigned char* xb = (unsigned char*)xs;
+  f32x4 own = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) own[rt] = wave_sum_across_groups(l_run[rt]);
+  *((f32x4*)(xb + kXlOff + wave * 1024) + lane) = own;
+  lds_barrier();
+  const f32x4 peer = *((const f32x4*)(xb + kXlOff + (wave ^ 1) * 1024) + lane);
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) l_run[rt] = own[rt] + peer[rt];
+}
+
 template <bool FP8, int NRT, int DH, bool PAGED>
 __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* smem) {
   UnitSetup us;
@@ -1253,7 +1716,7 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
     lim[rt] = min(us.hi_eff - 1, us.tail0 + (us.rowb0 + rv) / us.H) - us.uc.lo;
   }
   lds_u8* lds = (lds_u8*)smem;
-  float* xs = (float*)(smem + kRing * tile_bytes<FP8>());
+  float* xs = (float*)(smem + ring_slots<FP8, NRT>() * tile_bytes<FP8>());
 
   // per-lane softmax state: lane owns unit row grow0 + 16 rt + l16
   float m_run[NRT], l_run[NRT];
@@ -1264,19 +1727,34 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
       m_run[rt] = -INFINITY;
       l_run[rt] = 0.0f;
     }
+    if constexpr (!key_split<FP8, NRT>()) {  // the key-split pipeline zeroes O itself
 #pragma unroll
-    for (int cc = 0; cc < 16; ++cc)
+      for (int cc = 0; cc < 16; ++cc)
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) zero_o(oacc[cc][rt]);
+        for (int rt = 0; rt < NRT; ++rt) zero_o(oacc[cc][rt]);
+    }
     if (!wave_active) {  // a row group with no row of the unit only stages
       unit_staging_only<FP8, NRT, PAGED>(us, lds, tid);
+      if constexpr (key_split<FP8, NRT>()) lds_barrier();  // the other pair's row-sum exchange
       return;
     }
-    unit_pipeline<FP8, NRT, DH, PAGED>(us, lds, xs, wave, fb, qf, c, oacc, m_run, l_run, lim, tid,
-                                       g, lane);
-    epilogue<NRT, DH>(us, grow0, l16, g, oacc, m_run, l_run);
+    if constexpr (key_split<FP8, NRT>()) {
+      unit_pipeline8k<NRT, DH, PAGED>(us, lds, xs, wave, fb, qf, c, oacc, m_run, l_run, lim, tid,
+                                      g, lane);
+      total_row_sums<NRT>(xs, wave, l_run);
+      epilogue<NRT, DH, true>(us, grow0, l16, g, oacc, m_run, l_run);
+    } else {
+      unit_pipeline<FP8, NRT, DH, PAGED>(us, lds, xs, wave, fb, qf, c, oacc, m_run, l_run, lim, tid,
+                                         g, lane);
+      epilogue<NRT, DH>(us, grow0, l16, g, oacc, m_run, l_run);
+    }
   };
-  if constexpr (FP8) {
+  if constexpr (key_split<FP8, NRT>()) {
+    QFrag8K<NRT> q8;
+    float c[NRT];
+    load_q8k<NRT>(us, grow0, l16, g, wave, xs, q8, c);
+    run(frag_bases8k<DH>(l16, g), q8, c);
+  } else if constexpr (FP8) {
     QFrag8<NRT> q8;
     float c[NRT];
     load_q8<NRT, DH>(us, grow0, l16, g, wave, xs, q8, c);
@@ -1294,7 +1772,8 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
 
 template <bool FP8, int NRT>
 constexpr int main_lds_bytes() {
-  return kRing * tile_bytes<FP8>() + 2 * kWaves * NRT * 2 * 1024;  // tile ring + 2 exchange buffers
+  // tile ring + 2 exchange buffers
+  return ring_slots<FP8, NRT>() * tile_bytes<FP8>() + 2 * kWaves * NRT * 2 * 1024;
 }
 
 // One kernel per (KV dtype, row tiles per row group, KV layout): a kernel holds

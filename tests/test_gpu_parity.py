@@ -74,6 +74,10 @@ def test_planted_probe(fp8):
 
 @pytest.mark.parametrize("fp8", [False, True])
 def test_folded_equals_unfolded(fp8):
+    """Folding changes which rows share a tile, not a row's arithmetic: O and
+    LSE match the unfolded run bitwise, except that with fp8 KV the 96-row
+    tiles split each KV tile's keys between two waves, so a row's sum of P
+    adds its two halves last (LSE within 2 fp32 ulps; O within 1 bf16 ulp)."""
     inp = gen.peaked_inputs(gen.random_inputs(12, [8, 4], [1000, 333], fp8, seed=5), beta=10.0)
     for splits in (1, 4):
         o1, l1, p1 = gu.run_gpu(inp, force_splits=splits)
@@ -82,7 +86,11 @@ def test_folded_equals_unfolded(fp8):
         same = np.array_equal(o1, o2) and np.array_equal(l1, l2)
         gu.log(f"folded vs unfolded splits={splits}: bitwise={same} "
                f"max|dO|={np.abs(o1 - o2).max():.3e} max|dLSE|={np.abs(l1 - l2).max():.3e}")
-        assert same
+        if not fp8:
+            assert same
+        else:
+            assert np.all(np.abs(o1 - o2) <= 2.0 ** -7 * np.abs(o2))
+            assert np.all(np.abs(l1 - l2) <= 2 * np.spacing(np.abs(l2).astype(np.float32)))
 
 
 def test_split_counts_agree():
