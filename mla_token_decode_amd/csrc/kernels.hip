@@ -523,12 +523,17 @@ __device__ __forceinline__ void scale_o(f32x4& acc, float f, lds_u8* spill) {
 // The last iteration computes the scores of a tile past the end (stale slot
 // contents, discarded).
 
-// The fp8 kernel of 48-row row groups splits each tile's keys between the two
-// waves of a pair (unit_pipeline8k below) and keeps four tiles in the ring.
+// The fp8 kernels of 32- and 48-row row groups split each tile's keys between
+// the two waves of a pair (unit_pipeline8k below) and keep four tiles in the
+// ring.
 template <bool FP8, int NRT>
-constexpr bool key_split() { return FP8 && NRT == 3; }
+constexpr bool key_split() { return FP8 && NRT >= 2; }
 template <bool FP8, int NRT>
 constexpr int ring_slots() { return key_split<FP8, NRT>() ? 4 : 3; }
+// Bytes of the exchange area after the ring: two buffers of partial scores
+// (16 NRT KB), or the key-split records and Q set-up slots (48 KB).
+template <bool FP8, int NRT>
+constexpr int exchange_bytes() { return key_split<FP8, NRT>() ? 49152 : 2 * kWaves * NRT * 2 * 1024; }
 // Where the staging of tile t + 2 runs: bf16 KV between the score MFMAs
 // (its PV phase already carries two transposing reads per column tile); fp8
 // KV between the PV MFMAs (48 of them with one read per column tile and no
@@ -1332,7 +1337,7 @@ constexpr int kRopeSlotOff = kSpillOff + kWaves * 64 * 16;
 template <int NRT>
 __device__ __forceinline__ void load_q8k(const UnitSetup& us, int grow0, int l16, int g, int wave,
                                          float* xs, QFrag8K<NRT>& q8, float (&c)[NRT]) {
-  static_assert(kRopeSlotOff + kWaves * NRT * 2 * 64 * 16 <= 2 * kWaves * NRT * 2 * 1024,
+  static_assert(kRopeSlotOff + kWaves * NRT * 2 * 64 * 16 <= exchange_bytes<true, NRT>(),
                 "exchange area");
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -1498,6 +1503,16 @@ __device__ __forceinline__ void softmax_slice_k(SoftTileK<NRT>& w, const f32x4 (
   }
 }
 
+// 2 wait states between the VALU writes of the PV operand P and the first
+// MFMA that reads it (the asm consumes and redefines P, so it stays between).
+template <int NRT>
+__device__ __forceinline__ void pad_p_writes(i32x2 (&pf)[NRT]) {
+  if constexpr (NRT == 2)
+    asm volatile("s_nop 1" : "+v"(pf[0]), "+v"(pf[1]));
+  else
+    asm volatile("s_nop 1" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]));
+}
+
 // The whole KV chunk of a unit in the key-split path (see above).  Same
 // staging, barriers and tile-loop unrolling as unit_pipeline; the exchange
 // records replace the score exchange.
@@ -1509,7 +1524,7 @@ __device__ __forceinline__ void unit_pipeline8k(const UnitSetup& us, lds_u8* lds
                                                 float (&l_run)[NRT], const int (&lim)[NRT], int tid,
                                                 int g, int lane) {
   constexpr bool FP8 = true;
-  static_assert(NRT == 3, "exchange records hold one dword per row tile, at most 3");
+  static_assert(NRT >= 2 && NRT <= 3, "exchange records hold one dword per row tile, at most 3");
   constexpr int NS = stage_sets<FP8, NRT>();
   constexpr int kAhead = (NS - 1) * kPieces;
   constexpr int DV = v_ahead<NRT, FP8>();
@@ -1572,7 +1587,10 @@ __device__ __forceinline__ void unit_pipeline8k(const UnitSetup& us, lds_u8* lds
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
       own_mx[rt] = max2(max2(sacc[rt][0], sacc[rt][1]), max2(sacc[rt][2], sacc[rt][3]));
-    *xm_at(t1 & 1, wave) = f32x4{own_mx[0], own_mx[1], own_mx[2], 0.0f};
+    f32x4 rec = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) rec[rt] = own_mx[rt];
+    *xm_at(t1 & 1, wave) = rec;
   };
 
   score_phase8k<NRT>(lds, fb, qf, sc[0], [](auto) {}, [](auto) {});
@@ -1633,7 +1651,7 @@ __device__ __forceinline__ void unit_pipeline8k(const UnitSetup& us, lds_u8* lds
         // least 2 wait states before the first MFMA reads them)
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) pf[rt][1 - DH] = peer_p[rt];
-        asm volatile("s_nop 1" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]));
+        pad_p_writes(pf);
 
         // O of tile t - 1  ||  lane maxima of tile t + 1, staging of tile t + 2
         constexpr int kPvMfma = 16 * NRT;
@@ -1675,7 +1693,7 @@ __device__ __forceinline__ void unit_pipeline8k(const UnitSetup& us, lds_u8* lds
     issue_v_head8<DH, DV>(vr, vbase);
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) pf[rt][1 - DH] = peer_p[rt];
-    asm volatile("s_nop 1" : "+v"(pf[0]), "+v"(pf[1]), "+v"(pf[2]));
+    pad_p_writes(pf);
     pv_phase8<NRT, DH, DV>(vbase, pf, oacc, vr, [](auto) {});
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads issued past the end
@@ -1773,7 +1791,7 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
 template <bool FP8, int NRT>
 constexpr int main_lds_bytes() {
   // tile ring + 2 exchange buffers
-  return ring_slots<FP8, NRT>() * tile_bytes<FP8>() + 2 * kWaves * NRT * 2 * 1024;
+  return ring_slots<FP8, NRT>() * tile_bytes<FP8>() + exchange_bytes<FP8, NRT>();
 }
 
 // One kernel per (KV dtype, row tiles per row group, KV layout): a kernel holds
