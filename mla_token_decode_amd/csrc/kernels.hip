@@ -721,7 +721,7 @@ __device__ __forceinline__ void slices_at(F&& f) {
 template <int NRT, bool FP8>
 constexpr int k_ahead() { return NRT == 1 ? 4 : NRT == 2 ? 2 : 1; }
 template <int NRT, bool FP8>
-constexpr int v_ahead() { return NRT == 1 ? 7 : FP8 ? (NRT == 2 ? 6 : 2) : (NRT == 2 ? 4 : 1); }
+constexpr int v_ahead() { return NRT == 1 ? 7 : FP8 ? (NRT == 2 ? 6 : 2) : (NRT == 2 ? 4 : 2); }
 
 // Score phase: S^T partial (this wave's 288 columns) of one tile; K fragments
 // DK steps ahead; pre(i) runs before MFMA i and slice(i) after it.

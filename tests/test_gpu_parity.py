@@ -179,6 +179,24 @@ def test_large_logit_jumps_move_the_reference(fp8):
         gu.compare(o, lse, ro, rl, fp8, f"escalating splits={splits} units={plan.num_units}")
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_reference_moves_in_96_row_tiles(fp8):
+    """Reference moves in the 96-row tiles of H=12, q=8 (with fp8 KV the
+    key-split pipeline: a move found at tile t rescales O after the PV of
+    tile t - 1): jumps on either half of a tile's keys, on the first and the
+    last tile, and at chunk boundaries."""
+    H, q_len, kv_len = 12, [8], [1500]
+    targets = [(0, 7, 0, [3, 17, 40, 1499]),     # keys of both halves of tiles 0 and 1; last key
+               (0, 0, 11, [15, 16, 700]),        # the two halves of tile 0
+               (0, 4, 5, [31, 32, 33, 1200]),    # last key of tile 0, first keys of tile 1
+               (0, 6, 9, [63, 64, 1024])]        # chunk boundaries of 64-key chunks
+    inp = gen.escalating_inputs(H, q_len, kv_len, targets, fp8=fp8, seed=29)
+    ro, rl = gu.oracle_full(inp)
+    for splits in (1, 5, 24):
+        o, lse, plan = gu.run_gpu(inp, force_splits=splits)
+        gu.compare(o, lse, ro, rl, fp8, f"96-row escalating splits={splits} units={plan.num_units}")
+
+
 def test_poisoned_workspace_is_never_read_unwritten():
     inp = gen.random_inputs(12, [8, 2], [3000, 77], False, seed=13)
     ro, rl = gu.oracle_full(inp)
