@@ -1596,9 +1596,12 @@ __device__ __forceinline__ void unit_pipeline8k(const UnitSetup& us, lds_u8* lds
   score_phase8k<NRT>(lds, fb, qf, sc[0], [](auto) {}, [](auto) {});
   asm volatile("s_nop 15\n\ts_nop 7" ::: "memory");  // score MFMAs retire before the reads
   lane_max(std::integral_constant<int, 0>{}, 0);
+  *xp_at(1, wave) = i32x4{0, 0, 0, 0};  // P of "tile -1", read by the partner at t = 0
   lds_barrier();
-  f32x4 peer_mx = *xm_at(0, wave ^ 1);
-  i32x4 peer_p = {0, 0, 0, 0};
+  // the partner's records, read at the start of each iteration's score phase
+  // (after its K reads are issued, so no iteration starts with a wait on them)
+  f32x4 peer_mx;
+  i32x4 peer_p;
 
   zero_all_o();  // here rather than before the prologue: fewer values live across it
   i32x2 vr[v8_slots<DV>()];
@@ -1639,7 +1642,13 @@ __device__ __forceinline__ void unit_pipeline8k(const UnitSetup& us, lds_u8* lds
         // scores of tile t + 1 (into sc[(k + 1) % 2]) || softmax of tile t (sc[k])
         constexpr int kScoreMfma = 6 * NRT;
         i32x4* p_out = xp_at(t & 1, wave);
-        score_phase8k<NRT>(slot_n, fb, qf, sc[(k + 1) % 2], [](auto) {}, [&](auto ic) {
+        auto read_peer = [&](auto ic) {
+          if constexpr (decltype(ic)::value == 0) {
+            peer_p = *xp_at((t + 1) & 1, wave ^ 1);  // P(t - 1)
+            peer_mx = *xm_at(t & 1, wave ^ 1);       // lane maxima of tile t
+          }
+        };
+        score_phase8k<NRT>(slot_n, fb, qf, sc[(k + 1) % 2], read_peer, [&](auto ic) {
           constexpr int i = decltype(ic)::value;
           slices_at<soft_slices_k<NRT>(), kScoreMfma, i>([&](auto slc) {
             constexpr int s = decltype(slc)::value;
@@ -1679,9 +1688,6 @@ __device__ __forceinline__ void unit_pipeline8k(const UnitSetup& us, lds_u8* lds
           prow_next = src.barrier_and_page_row(t + 3 + NS);
         else
           lds_barrier();
-        // published by the barrier: the partner's P(t) and lane maxima of tile t + 1
-        peer_p = *xp_at(t & 1, wave ^ 1);
-        peer_mx = *xm_at((t + 1) & 1, wave ^ 1);
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) pf[rt][DH] = pnew[rt];
       }
@@ -1691,6 +1697,7 @@ __device__ __forceinline__ void unit_pipeline8k(const UnitSetup& us, lds_u8* lds
   {
     lds_u8* vbase = lds + ((u.ntiles - 1) % RING) * TB + fb.v;
     issue_v_head8<DH, DV>(vr, vbase);
+    peer_p = *xp_at((u.ntiles - 1) & 1, wave ^ 1);
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) pf[rt][1 - DH] = peer_p[rt];
     pad_p_writes(pf);
