@@ -10,14 +10,16 @@
 //
 // Loader: every thread keeps one to three 32-key KV tiles in flight in
 // registers (inline-assembly buffer loads with explicit vmcnt waits), then
-// writes each tile into a three-slot LDS ring: bf16 KV as bf16 rows; fp8-e4m3
+// writes each tile into an LDS ring of three slots (four for the fp8
+// key-split kernels below): bf16 KV as bf16 rows; fp8-e4m3
 // KV with the 512 latent columns kept as e4m3 codes and the 64 rope columns
 // converted (exactly) to bf16.  The per-tensor fp8 scale is folded into the
 // logit scale and the O epilogue.
 //
 // Work split inside a workgroup: wave w = (row group rg = w / 2, half
 // dh = w % 2).  A row group is up to 48 rows (NRT 16-row MFMA tiles); the
-// wave pair splits the 576 score columns and the 512 value columns in halves:
+// wave pair splits the 512 value columns in halves and, except in the fp8
+// key-split kernels (unit_pipeline8k), the 576 score columns too:
 //   S^T[key][row] partial = K[:, 288dh:+288] . Q^T   (bf16 KV: bf16 MFMA
 //                  16x16x32; fp8 KV: fp8 MFMA 16x16x128 on the latent part
 //                  with Q quantised per row, bf16 MFMA on the rope part;
