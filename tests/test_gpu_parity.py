@@ -31,6 +31,12 @@ SMALL_CASES = [
     (128, [2], [64], False),
     (12, [1, 2, 3, 4, 8], [33, 64, 65, 500, 8], False),
     (96, [1, 2, 3, 4], [100, 40, 9, 4], True),
+    # fp8 KV at every row-group width of the key-split kernels: 128-row tiles
+    # cut into 64-row units, 70- and 96-row tiles, kv_len == q_len
+    (128, [1], [130], True),
+    (64, [2], [65], True),
+    (7, [20], [90], True),
+    (6, [16], [16], True),
 ]
 
 
