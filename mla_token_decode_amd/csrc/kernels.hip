@@ -62,6 +62,12 @@ constexpr unsigned kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer: range-checked,
 template <bool FP8P>
 constexpr float lazy_octaves() { return FP8P ? 8.0f : 60.0f; }
 
+// fp8 Q: a row's largest |q| maps to the e4m3 maximum 448.  The fp32
+// rounding of 448 / M and of q * (448 / M) can put a value up to 2 ulps above
+// 448; the gfx950 conversion rounds to nearest before it saturates (inputs up
+// to 463 give 448, checked on the MI355X), so no clamp is needed.
+constexpr float kQ8Top = 448.0f;
+
 // LDS holds every KV tile as bf16 rows: 1152 bytes = 72 chunks of 16 B,
 // physical chunk = logical chunk XOR swz(key) inside aligned groups of 8
 // chunks, so the 16 keys an MFMA operand read touches hit distinct bank slots.
@@ -1221,10 +1227,11 @@ __device__ __forceinline__ void load_q8(const UnitSetup& us, int grow0, int l16,
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const float M = fmaxf(half_max[rt], xs[((wave ^ 1) * NRT + rt) * 16 + l16]);
-    const float inv = M > 0.0f ? 448.0f / M : 1.0f;
-    c[rt] = us.scale_log2 * (M > 0.0f ? M / 448.0f : 1.0f);
-    auto q = [&](unsigned bits) {  // bf16 bits -> q / s, within the e4m3 range
-      return fminf(fmaxf(__builtin_bit_cast(float, bits) * inv, -448.0f), 448.0f);
+    // 1 / s with s = M / 448 (no clamp needed: see kQ8Top)
+    const float inv = M > 0.0f ? kQ8Top / M : 1.0f;
+    c[rt] = us.scale_log2 * (M > 0.0f ? M / kQ8Top : 1.0f);
+    auto q = [&](unsigned bits) {  // bf16 bits -> q / s, inside the e4m3 range
+      return __builtin_bit_cast(float, bits) * inv;
     };
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -1369,10 +1376,11 @@ __device__ __forceinline__ void load_q8k(const UnitSetup& us, int grow0, int l16
 #pragma unroll
       for (int w = 0; w < 4; ++w) mr = amax2(mr, rope[h][w]);
     const float M = wave_max_across_groups(fmaxf(m, mr * 0x1p-64f));
-    const float inv = M > 0.0f ? 448.0f / M : 1.0f;
-    c[rt] = us.scale_log2 * (M > 0.0f ? M / 448.0f : 1.0f);
-    auto q = [&](unsigned bits) {  // bf16 bits -> q / s, within the e4m3 range
-      return fminf(fmaxf(__builtin_bit_cast(float, bits) * inv, -448.0f), 448.0f);
+    // 1 / s with s = M / 448 (no clamp needed: see kQ8Top)
+    const float inv = M > 0.0f ? kQ8Top / M : 1.0f;
+    c[rt] = us.scale_log2 * (M > 0.0f ? M / kQ8Top : 1.0f);
+    auto q = [&](unsigned bits) {  // bf16 bits -> q / s, inside the e4m3 range
+      return __builtin_bit_cast(float, bits) * inv;
     };
 #pragma unroll
     for (int b = 0; b < 4; ++b)
