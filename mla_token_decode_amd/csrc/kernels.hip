@@ -1331,87 +1331,117 @@ constexpr bool lat_in_agpr() { return B == 3; }
 
 // LDS records of the key-split pipeline inside the exchange area (16 bytes
 // per lane): lane maxima [2 parities][waves][64], e4m3 P [2][waves][64], the
-// row sums at the end [waves][64], a per-wave spill slot for the O rescale,
-// and (set-up only) the lane-private slots that move the rope Q fragments to
-// their AGPR home.
+// row sums at the end [waves][64] and a per-wave spill slot for the O rescale.
 constexpr int kXmOff = 0;
 constexpr int kXpOff = 2 * kWaves * 64 * 16;
 constexpr int kXlOff = kXpOff + 2 * kWaves * 64 * 16;
 constexpr int kSpillOff = kXlOff + kWaves * 64 * 16;
-constexpr int kRopeSlotOff = kSpillOff + kWaves * 64 * 16;
+static_assert(kSpillOff + kWaves * 64 * 16 <= 49152, "key-split records fit the exchange area");
 
-// fp8 Q at full depth: each wave quantises its rows itself (the same scale
-// rule as load_q8, from the whole row: both waves of a pair reach the same
-// scale), one row tile at a time.
-template <int NRT>
+// fp8 Q at full depth, quantised once per pair: wave dh quantises latent
+// blocks 2 dh, 2 dh + 1 and rope half dh of its rows (the scale rule of
+// load_q8, from the whole row: the pair first exchanges its half maxima) and
+// the two halves are swapped through LDS.  The exchange lives in the tile
+// ring, which no wave writes before the pipeline's prologue; the last barrier
+// here keeps the staging of tiles 0 and 1 behind every wave's reads.
+constexpr int kQxMaxBytes = 4096;  // half maxima [waves][NRT][64] fp32
+constexpr int kQxRec = 80;         // per lane and row tile: 2 latent blocks + rope half
+
+template <int NRT, int DH>
 __device__ __forceinline__ void load_q8k(const UnitSetup& us, int grow0, int l16, int g, int wave,
-                                         float* xs, QFrag8K<NRT>& q8, float (&c)[NRT]) {
-  static_assert(kRopeSlotOff + kWaves * NRT * 2 * 64 * 16 <= exchange_bytes<true, NRT>(),
-                "exchange area");
+                                         lds_u8* ring, QFrag8K<NRT>& q8, float (&c)[NRT]) {
+  static_assert(kWaves * NRT * 64 * 4 <= kQxMaxBytes, "half maxima");
+  static_assert(kQxMaxBytes + kWaves * NRT * 64 * kQxRec <= 4 * kTileBytes8, "Q exchange in the ring");
   const int lane = threadIdx.x & 63;
+  typedef __attribute__((address_space(3))) float lds_f32;
+  lds_f32* xmax = (lds_f32*)ring;
+  auto rec = [&](int w, int rt) { return ring + kQxMaxBytes + ((w * NRT + rt) * 64 + lane) * kQxRec; };
+  u32x4 lat[NRT][2][4], rope[NRT];
+  float hm[NRT];
+  auto amax2 = [](float m, unsigned x) {
+    return fmaxf(m, fmaxf(fabsf(__builtin_bit_cast(float, x << 16)),
+                          fabsf(__builtin_bit_cast(float, x & 0xffff0000u))));
+  };
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const int row = min(grow0 + 16 * rt + l16, us.RU - 1);
     const uint16_t* qrow = us.q + ((int64_t)us.row0 + row) * kDqk;
-    u32x4 lat[4][4], rope[2];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lat[b][i] = *(const u32x4*)(qrow + 128 * b + 32 * g + 8 * i);
+      for (int i = 0; i < 4; ++i)
+        lat[rt][bb][i] = *(const u32x4*)(qrow + 128 * (2 * DH + bb) + 32 * g + 8 * i);
+    rope[rt] = *(const u32x4*)(qrow + 512 + 32 * DH + 8 * g);
+  }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) rope[h] = *(const u32x4*)(qrow + 512 + 32 * h + 8 * g);
-    auto amax2 = [](float m, unsigned x) {
-      return fmaxf(m, fmaxf(fabsf(__builtin_bit_cast(float, x << 16)),
-                            fabsf(__builtin_bit_cast(float, x & 0xffff0000u))));
-    };
+  for (int rt = 0; rt < NRT; ++rt) {
     float m = 0.0f, mr = 0.0f;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) m = amax2(m, lat[b][i][w]);
+        for (int w = 0; w < 4; ++w) m = amax2(m, lat[rt][bb][i][w]);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int w = 0; w < 4; ++w) mr = amax2(mr, rope[rt][w]);
+    hm[rt] = wave_max_across_groups(fmaxf(m, mr * 0x1p-64f));
+    xmax[(wave * NRT + rt) * 64 + lane] = hm[rt];
+  }
+  lds_barrier();
 #pragma unroll
-      for (int w = 0; w < 4; ++w) mr = amax2(mr, rope[h][w]);
-    const float M = wave_max_across_groups(fmaxf(m, mr * 0x1p-64f));
+  for (int rt = 0; rt < NRT; ++rt) {
+    const float M = fmaxf(hm[rt], xmax[((wave ^ 1) * NRT + rt) * 64 + lane]);
     // 1 / s with s = M / 448 (no clamp needed: see kQ8Top)
     const float inv = M > 0.0f ? kQ8Top / M : 1.0f;
     c[rt] = us.scale_log2 * (M > 0.0f ? M / kQ8Top : 1.0f);
     auto q = [&](unsigned bits) {  // bf16 bits -> q / s, inside the e4m3 range
       return __builtin_bit_cast(float, bits) * inv;
     };
+    lds_u8* mine = rec(wave, rt);
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int bb = 0; bb < 2; ++bb) {
+      i32x8 v8;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {  // dword k: elements 4 k .. 4 k + 3 of the lane's 32
-        const unsigned x0 = lat[b][k >> 1][2 * (k & 1)], x1 = lat[b][k >> 1][2 * (k & 1) + 1];
+        const unsigned x0 = lat[rt][bb][k >> 1][2 * (k & 1)];
+        const unsigned x1 = lat[rt][bb][k >> 1][2 * (k & 1) + 1];
         int v = __builtin_amdgcn_cvt_pk_fp8_f32(q(x0 << 16), q(x0 & 0xffff0000u), 0, false);
         v = __builtin_amdgcn_cvt_pk_fp8_f32(q(x1 << 16), q(x1 & 0xffff0000u), v, true);
-        q8.lat[rt][b][k] = v;
+        v8[k] = v;
       }
+      q8.lat[rt][2 * DH + bb] = v8;
+      *(i32x4*)(mine + 32 * bb) = i32x4{v8[0], v8[1], v8[2], v8[3]};
+      *(i32x4*)(mine + 32 * bb + 16) = i32x4{v8[4], v8[5], v8[6], v8[7]};
+    }
+    bf16x8 r;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const unsigned x = rope[rt][w];
+      r[2 * w] = (__bf16)(__builtin_bit_cast(float, x << 16) * inv);
+      r[2 * w + 1] = (__bf16)(__builtin_bit_cast(float, x & 0xffff0000u) * inv);
+    }
+    *(bf16x8*)(mine + 64) = r;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    lds_u8* peer = rec(wave ^ 1, rt);
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const i32x4 a = *(const i32x4*)(peer + 32 * bb);
+      const i32x4 b = *(const i32x4*)(peer + 32 * bb + 16);
+      q8.lat[rt][2 * (1 - DH) + bb] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
     // block 3 moves to the AGPR file once, here (an empty statement whose
     // output lives in AGPRs; the MFMAs read it from there)
     asm volatile("" : "=a"(q8.lat[rt][3]) : "0"(q8.lat[rt][3]));
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 r;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const unsigned x = rope[h][w];
-        r[2 * w] = (__bf16)(__builtin_bit_cast(float, x << 16) * inv);
-        r[2 * w + 1] = (__bf16)(__builtin_bit_cast(float, x & 0xffff0000u) * inv);
-      }
-      lds_u8* slot = (lds_u8*)xs + kRopeSlotOff + (((wave * NRT + rt) * 2 + h) * 64 + lane) * 16;
-      *(bf16x8*)slot = r;
-      asm volatile("s_waitcnt lgkmcnt(0)\n\tds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-                   : "=a"(q8.rope[rt][h]) : "v"(slot) : "memory");
-    }
-    // one row tile at a time: the scheduler would otherwise issue every row
-    // tile's loads first and run out of registers
-    __builtin_amdgcn_sched_barrier(0);
+    // both rope halves go straight from LDS to their AGPR home
+    asm volatile("ds_read_b128 %0, %1 offset:64\n\ts_waitcnt lgkmcnt(0)"
+                 : "=a"(q8.rope[rt][DH]) : "v"(rec(wave, rt)) : "memory");
+    asm volatile("ds_read_b128 %0, %1 offset:64\n\ts_waitcnt lgkmcnt(0)"
+                 : "=a"(q8.rope[rt][1 - DH]) : "v"(peer) : "memory");
   }
+  lds_barrier();  // every wave's reads are done before the ring takes tiles
 }
 
 // Score phase of the key-split path: S^T of the wave's 16 keys, per row tile
@@ -1787,7 +1817,7 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
   if constexpr (key_split<FP8, NRT>()) {
     QFrag8K<NRT> q8;
     float c[NRT];
-    load_q8k<NRT>(us, grow0, l16, g, wave, xs, q8, c);
+    load_q8k<NRT, DH>(us, grow0, l16, g, wave, lds, q8, c);
     run(frag_bases8k<DH>(l16, g), q8, c);
   } else if constexpr (FP8) {
     QFrag8<NRT> q8;
