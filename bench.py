@@ -15,8 +15,11 @@ second set of steps with one more event between the two kernels.
 Prints ONE JSON line.  The headline workload is fp8-e4m3 KV, bf16 Q, batch 1,
 H=12, q=8, ctx=1048576; `value` is its median us per call.  `per_workload`
 adds the other workloads and the q-flatness sweep (ctx=1048576, q=1,2,4,8,
-bf16 and fp8).  `cpu_baseline` times the fp64 oracle on a bounded sample of
-the headline workload's rows on the host cores.
+bf16 and fp8), each with the GPU clocks the driver reported around its
+timing.  `cpu_baseline` times the fp64 oracle on the host cores after all GPU
+timing: the headline workload in full (every output row), and each other
+workload on a stated sample of rows (`per_config`), plus single-thread runs of
+the two smallest workloads.
 """
 from __future__ import annotations
 
@@ -37,13 +40,47 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 METRIC = "µs/call + KV-read HBM GB/s (% roofline), H=12 q=8 ctx=1M bf16/fp8"
 HEADLINE = "h12_1m_fp8"
-PAGES_FP8_1M_US = 168.2  # B300, cute-dsl fold_sq, H=12 q=8 ctx~1M fp8 (context, other hardware)
+# The pages' own figure for this shape (B300, cute-dsl fold_sq, H=12 q=8 ctx~1M
+# fp8, median us/call): context on other hardware, not a baseline of this run.
+PAGES_FP8_1M_US_B300 = 168.2
 KERNEL_SOURCE = os.path.join(ROOT, "mla_token_decode_amd", "csrc", "kernels.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mla_decode_main_fp8_h12_q8_1m_hbm_traffic.txt")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def read_clocks():
+    """SCLK / MCLK of GPU 0 as the driver reports them right now (rocm-smi,
+    best effort: None with the reason when unavailable)."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        data = json.loads(r.stdout[r.stdout.index("{"):])
+        card = next(iter(data.values()))
+        out = {}
+        for key, val in card.items():
+            m = re.search(r"(\d+)\s*Mhz", str(val), re.I)
+            for name in ("sclk", "mclk", "fclk", "socclk"):
+                if key.lower().startswith(name) and m:
+                    out[name + "_mhz"] = int(m.group(1))
+        return out or {"error": "no clock fields in rocm-smi output"}
+    except Exception as e:  # noqa: BLE001 -- a missing tool must not stop the bench
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def to_device(inp):
@@ -78,10 +115,24 @@ class CacheFlush:
             self.buf.add_(1)
 
 
-def measure(inp, dev, steps, warmup, flush, paged=None, **plan_opts):
+def settle(flush, ms):
+    """Untimed: keep the GPU busy with cache-flush reads for `ms` milliseconds
+    so that its clocks leave any idle state (input generation on the host
+    leaves the GPU idle for seconds) before the warm-up calls."""
+    import torch
+    if ms <= 0:
+        return
+    t_end = time.perf_counter() + ms * 1e-3
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            flush()
+        torch.cuda.synchronize()
+
+
+def measure(inp, dev, steps, warmup, flush, paged=None, settle_ms=0, **plan_opts):
     """Cold-cache timing of run + reduce (mla_decode_run, or mla_decode_run_paged
     when `paged` = (pool, page table) is given).  Returns a stats dict
-    (microseconds)."""
+    (microseconds) with the clocks the driver reported before and after."""
     import torch
     from mla_token_decode_amd import binding as mb
 
@@ -101,10 +152,12 @@ def measure(inp, dev, steps, warmup, flush, paged=None, **plan_opts):
         run()
         mb.mla_decode_reduce(plan, ws, o, lse, stream)
 
+    settle(flush, settle_ms)
     for _ in range(warmup):
         flush()
         step()
     torch.cuda.synchronize()
+    clocks_before = read_clocks()
     # the call: events only around run + reduce
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     t0 = time.perf_counter()
@@ -144,6 +197,8 @@ def measure(inp, dev, steps, warmup, flush, paged=None, **plan_opts):
         "split_tiles": plan.num_split_tiles,
         "fold_tiles_splits_L": list(plan.query(0)),
         "wall_s": wall,
+        "clocks_before": clocks_before,
+        "clocks_after": read_clocks(),
     }
 
 
@@ -182,22 +237,58 @@ def flops(inp):
     return total
 
 
-def cpu_baseline(inp, rows_sample):
+def oracle_time(inp, rows_sample, threads=None, seed=123):
+    """Wall time of the fp64 oracle on `rows_sample` output rows (all rows when
+    the sample covers them), scaled to the whole call.  Returns a dict."""
     import oracle
     total_rows = int(inp.q_len.sum()) * inp.H
-    rng = np.random.default_rng(123)
-    rows = np.sort(rng.choice(total_rows, size=min(rows_sample, total_rows), replace=False))
-    t0 = time.perf_counter()
-    oracle.mla_decode_rows(inp.q_bits, inp.kv, inp.q_len, inp.kv_len, inp.H, rows,
-                           kv_is_fp8=inp.kv_fp8, kv_scale=inp.kv_scale, sm_scale=inp.sm_scale)
-    dt = time.perf_counter() - t0
+    if rows_sample >= total_rows:
+        rows = np.arange(total_rows, dtype=np.int64)
+    else:
+        rng = np.random.default_rng(seed)
+        rows = np.sort(rng.choice(total_rows, size=rows_sample, replace=False))
+    if threads is not None:
+        oracle.set_num_threads(threads)
+    try:
+        used = oracle.num_threads()
+        t0 = time.perf_counter()
+        oracle.mla_decode_rows(inp.q_bits, inp.kv, inp.q_len, inp.kv_len, inp.H, rows,
+                               kv_is_fp8=inp.kv_fp8, kv_scale=inp.kv_scale, sm_scale=inp.sm_scale)
+        dt = time.perf_counter() - t0
+    finally:
+        if threads is not None:
+            oracle.set_num_threads(len(os.sched_getaffinity(0)))
+    return {"us_per_call": dt / len(rows) * total_rows * 1e6, "threads": used,
+            "rows_timed": int(len(rows)), "rows_total": total_rows, "timed_s": round(dt, 3)}
+
+
+# Rows of each workload the oracle is timed on (about 10-30 s of host work in
+# total at 16 threads): the headline in full; the others sampled.
+ORACLE_ROWS = {"h12_1m_fp8": 96, "small": 24, "h12_131k": 96, "h96_125k": 96, "ragged": 320}
+ORACLE_ROWS_1T = {"small": 24, "h12_131k": 12}
+
+
+def cpu_baseline(head_inp, other_inps):
+    import oracle
+    oracle.set_num_threads(len(os.sched_getaffinity(0)))
+    head = oracle_time(head_inp, ORACLE_ROWS[HEADLINE])
+    per = {HEADLINE: head}
+    for name, inp in other_inps.items():
+        per[name] = oracle_time(inp, ORACLE_ROWS.get(name, 96))
+        log(f"  oracle {name}: {per[name]}")
+        if name in ORACLE_ROWS_1T:
+            per[name + "_1thread"] = oracle_time(inp, ORACLE_ROWS_1T[name], threads=1)
+            log(f"  oracle {name} (1 thread): {per[name + '_1thread']}")
     return {
-        "value": dt / len(rows) * total_rows * 1e6,
+        "value": round(head["us_per_call"], 1),
         "unit": "µs/call",
-        "cores": oracle.num_threads(),
+        "cores": head["threads"],
         "kind": "oracle",
-        "sample": f"{len(rows)} of {total_rows} output rows of the headline workload, "
-                  f"fp64, timed {dt:.2f} s, scaled to all rows",
+        "sample": f"all {head['rows_total']} output rows of the headline workload "
+                  f"(fp64, OpenMP over rows, {head['threads']} threads), timed "
+                  f"{head['timed_s']:.2f} s; other workloads on the row samples in per_config",
+        "cpu_model": cpu_model(),
+        "per_config": per,
     }
 
 
@@ -205,10 +296,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=50,
-                    help="untimed calls per workload (the GPU clocks settle over ~50)")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed calls per workload")
+    ap.add_argument("--settle-ms", type=int, default=300,
+                    help="untimed cache-flush reads before each workload's warm-up, so the "
+                         "GPU clocks leave the idle state of the host-side input generation")
     ap.add_argument("--quick", action="store_true", help="headline workload only")
-    ap.add_argument("--cpu-rows", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     args = ap.parse_args()
@@ -227,20 +319,34 @@ def main():
     # FETCH_SIZE / WRITE_SIZE counter summaries are calibrated against
     flush.buf.add_(1)
     torch.cuda.synchronize()
+    # measured read-stream ceiling: torch.sum over the 1 GiB buffer, timed
+    settle(flush, args.settle_ms)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+    for k in range(10):
+        evs[k].record()
+        flush()
+    evs[10].record()
+    torch.cuda.synchronize()
+    stream_us = np.median([evs[k].elapsed_time(evs[k + 1]) for k in range(10)]) * 1e3
+    read_stream_gbps = flush.buf.numel() * 4 / (stream_us * 1e-6) / 1e9
+    log(f"read stream (torch.sum over 1 GiB): {read_stream_gbps:.0f} GB/s")
 
+    meas = dict(steps=args.steps, warmup=args.warmup, flush=flush, settle_ms=args.settle_ms)
     log(f"generating {HEADLINE}")
     w = gen.workload(HEADLINE)
     inp = gen.gen_workload_inputs(w)
     dev = to_device(inp)
     log("timing headline")
-    head = measure(inp, dev, args.steps, args.warmup, flush)
+    head = measure(inp, dev, **meas)
     log(f"  {head}")
     dirty = None
     if not args.quick:
-        dirty = measure(inp, dev, args.steps, args.warmup, CacheFlush("write"))["us_per_call"]
+        dirty = measure(inp, dev, args.steps, args.warmup, CacheFlush("write"),
+                        settle_ms=args.settle_ms)["us_per_call"]
         log(f"  after a dirtying flush: {dirty:.1f} us")
 
     per = {HEADLINE: head}
+    others = {}
     if not args.quick:
         # the headline workload from a paged cache: 64-key pages in a seeded random order
         page = 64
@@ -250,7 +356,7 @@ def main():
         pool[torch.from_numpy(perm).cuda()] = dev[1].view(npages, page, -1)
         table = torch.from_numpy(perm.astype(np.int32)).view(1, npages).cuda()
         name = f"paged_{HEADLINE}_p{page}"
-        per[name] = measure(inp, dev, args.steps, args.warmup, flush, paged=(pool, table))
+        per[name] = measure(inp, dev, paged=(pool, table), **meas)
         log(f"  {name}: {per[name]['us_per_call']:.1f} us")
         del pool, table
         # q-flatness at ctx=1M, both dtypes (same KV per dtype, Q per q)
@@ -268,25 +374,30 @@ def main():
                                  fp8, scale)
                 qd = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).cuda()
                 name = f"flat_{'fp8' if fp8 else 'bf16'}_q{q}_1m"
-                per[name] = measure(sub, (qd, kv_dev), args.steps, args.warmup, flush)
+                per[name] = measure(sub, (qd, kv_dev), **meas)
                 log(f"  {name}: {per[name]['us_per_call']:.1f} us")
             del kv_dev
+        for fp8 in ("fp8", "bf16"):
+            q1, q8 = per[f"flat_{fp8}_q1_1m"]["us_per_call"], per[f"flat_{fp8}_q8_1m"]["us_per_call"]
+            per[f"flat_{fp8}_q8_over_q1"] = round(q8 / q1, 3)
         for name in ("small", "h12_131k", "h96_125k", "ragged"):
             log(f"generating {name}")
             winp = gen.gen_workload_inputs(gen.workload(name))
             wdev = to_device(winp)
-            st = measure(winp, wdev, args.steps, args.warmup, flush)
+            st = measure(winp, wdev, **meas)
             st["tflops"] = flops(winp) / (st["us_per_call"] * 1e-6) / 1e12
             st["frac_bf16_mfma_peak"] = st["tflops"] / BF16_MFMA_PEAK_TFLOPS
+            st["main_tflops"] = flops(winp) / (st["main_us_mean"] * 1e-6) / 1e12
             per[name] = st
             log(f"  {name}: {st['us_per_call']:.1f} us")
-            del wdev, winp
+            others[name] = winp
+            del wdev
             torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline")
-        cpu = cpu_baseline(inp, args.cpu_rows)
+        cpu = cpu_baseline(inp, others)
     traffic = measured_traffic()
 
     main_us = head["main_us_mean"]
@@ -301,15 +412,23 @@ def main():
         "ms_per_step": round(head["us_per_call"] / 1e3, 4),
         "higher_is_better": False,
         "scaling": "weak",
-        "vs_baseline": round(head["us_per_call"] / PAGES_FP8_1M_US, 3),
-        "dtype": "bf16",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
         "data": "synthetic (seeded N(0,1)*0.1, fp8-e4m3 KV with per-tensor scale)",
         "config": {"workload": HEADLINE, "description": w.description, "batch": 1, "H": 12,
                    "q": 8, "ctx": 1048576, "kv_dtype": "fp8_e4m3", "q_dtype": "bf16",
+                   "arithmetic": "QK^T latent part: e4m3 x e4m3 MFMA (Q quantised per row); "
+                                 "QK^T rope part: bf16 MFMA; PV: e4m3 P x e4m3 V MFMA; fp32 "
+                                 "accumulation, softmax and merge; bf16 split partials",
                    "kv_gbps": round(head["kv_gbps"], 1),
                    "frac_hbm_roofline": round(head["frac_hbm_peak"], 4),
                    "timing": "cold cache (1 GiB read between steps: no KV and no dirty lines "
                              "left in L2 / Infinity Cache), HIP events, median",
+                   "settle_ms": args.settle_ms,
+                   "clocks": {"before": head["clocks_before"], "after": head["clocks_after"]},
+                   "read_stream_gbps": round(read_stream_gbps, 1),
+                   "frac_of_read_stream": round(head["kv_gbps"] / read_stream_gbps, 4),
+                   "context_pages_b300_us": PAGES_FP8_1M_US_B300,
                    "us_per_call_after_dirty_flush": round(dirty, 2) if dirty else None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -322,8 +441,9 @@ def main():
                      "kernel_us_mean": round(main_us, 2),
                      "kernel_source_sha256": kernel_source_sha256()},
         "cpu_baseline": cpu,
-        "per_workload": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
-                             for kk, vv in v.items()} for k, v in per.items()},
+        "per_workload": {k: ({kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                              for kk, vv in v.items()} if isinstance(v, dict) else v)
+                         for k, v in per.items()},
     }
     print(json.dumps(line), flush=True)
 

@@ -191,11 +191,51 @@ def mla_decode_plan(num_heads, q_len, kv_len, kv_fp8=False, **opts) -> Plan:
     return Plan(num_heads, q_len, kv_len, kv_fp8, **opts)
 
 
+def _check_tensor(t, name, dtypes, min_numel):
+    """Validate a device buffer passed as a torch tensor before its pointer
+    reaches the library: the kernels address buffers from the plan's sizes, so
+    a short, strided, host or wrongly typed tensor would be read or written out
+    of bounds on the device.  Raw integer pointers are passed through as they
+    are (the caller vouches for them)."""
+    if t is None or isinstance(t, int):
+        return
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a device (cuda) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if str(t.dtype).replace("torch.", "") not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements; the plan needs at least {min_numel}")
+
+
+def _check_run_args(plan: Plan, q, kv, o, lse, workspace, workspace_bytes, kv_rows):
+    rows = sum(plan.q_len) * plan.num_heads
+    _check_tensor(q, "q", ("bfloat16",), rows * DQK)
+    if q is not None and not isinstance(q, int) and q.numel() != rows * DQK:
+        raise ValueError(f"q must hold sum(q_len) * H * 576 = {rows * DQK} elements")
+    _check_tensor(kv, "kv", ("uint8", "float8_e4m3fn") if plan.kv_fp8 else ("bfloat16",),
+                  kv_rows * DQK)
+    _check_tensor(o, "o", ("bfloat16",), rows * DV)
+    _check_tensor(lse, "lse", ("float32",), rows)
+    if workspace is not None and not isinstance(workspace, int):
+        _check_tensor(workspace, "workspace", ("uint8", "int8", "float32", "bfloat16", "int32"), 0)
+        if workspace.numel() * workspace.element_size() < int(workspace_bytes):
+            raise ValueError("workspace_bytes exceeds the workspace tensor")
+
+
+def _workspace_bytes(workspace, workspace_bytes):
+    if workspace_bytes is not None:
+        return int(workspace_bytes)
+    if workspace is None or isinstance(workspace, int):
+        return 0
+    return workspace.numel() * workspace.element_size()
+
+
 def mla_decode_run(plan: Plan, q, kv, sm_scale: float, kv_scale: float, o, lse, workspace=None,
                    workspace_bytes=None, stream=None):
-    if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None else (
-            workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0)
+    workspace_bytes = _workspace_bytes(workspace, workspace_bytes)
+    _check_run_args(plan, q, kv, o, lse, workspace, workspace_bytes, sum(plan.kv_len))
     _check(lib().mla_decode_run(plan.handle, _ptr(q), _ptr(kv), float(sm_scale), float(kv_scale),
                                 _ptr(o), _ptr(lse), _ptr(workspace), int(workspace_bytes),
                                 _stream(stream)))
@@ -210,9 +250,13 @@ def mla_decode_run_paged(plan: Plan, q, kv_pages, page_table, sm_scale: float, k
         raise ValueError("kv_pages must be [num_pages, page_size, 576]")
     if page_table.dim() != 2 or not page_table.is_contiguous() or str(page_table.dtype) != "torch.int32":
         raise ValueError("page_table must be a contiguous [batch, stride] int32 tensor")
-    if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None else (
-            workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0)
+    if int(page_table.shape[0]) < len(plan.q_len):
+        raise ValueError("page_table needs one row per sequence of the plan")
+    if not page_table.is_cuda:
+        raise ValueError("page_table must be a device (cuda) tensor")
+    workspace_bytes = _workspace_bytes(workspace, workspace_bytes)
+    _check_run_args(plan, q, kv_pages, o, lse, workspace, workspace_bytes,
+                    int(kv_pages.shape[0]) * int(kv_pages.shape[1]))
     _check(lib().mla_decode_run_paged(plan.handle, _ptr(q), _ptr(kv_pages), int(kv_pages.shape[0]),
                                       int(kv_pages.shape[1]), _ptr(page_table),
                                       int(page_table.shape[1]), float(sm_scale), float(kv_scale),
@@ -221,6 +265,13 @@ def mla_decode_run_paged(plan: Plan, q, kv_pages, page_table, sm_scale: float, k
 
 
 def mla_decode_reduce(plan: Plan, workspace, o, lse, stream=None):
+    rows = sum(plan.q_len) * plan.num_heads
+    _check_tensor(o, "o", ("bfloat16",), rows * DV)
+    _check_tensor(lse, "lse", ("float32",), rows)
+    if workspace is not None and not isinstance(workspace, int):
+        _check_tensor(workspace, "workspace", ("uint8", "int8", "float32", "bfloat16", "int32"), 0)
+        if workspace.numel() * workspace.element_size() < plan.workspace_bytes:
+            raise ValueError(f"workspace is smaller than the planned {plan.workspace_bytes} bytes")
     _check(lib().mla_decode_reduce(plan.handle, _ptr(workspace), _ptr(o), _ptr(lse),
                                    _stream(stream)))
 
@@ -234,6 +285,10 @@ def mla_merge_shards(o_shards, lse_shards, o, lse, stream=None):
         raise ValueError("o_shards must be [W, rows, 512] and lse_shards [W, rows]")
     if int(o.numel()) != num_rows * DV or int(lse.numel()) != num_rows:
         raise ValueError("o must hold rows x 512 values and lse rows values")
+    _check_tensor(o_shards, "o_shards", ("bfloat16",), num_shards * num_rows * DV)
+    _check_tensor(lse_shards, "lse_shards", ("float32",), num_shards * num_rows)
+    _check_tensor(o, "o", ("bfloat16",), num_rows * DV)
+    _check_tensor(lse, "lse", ("float32",), num_rows)
     _check(lib().mla_merge_shards(num_rows, num_shards, _ptr(o_shards), _ptr(lse_shards), _ptr(o),
                                   _ptr(lse), _stream(stream)))
 

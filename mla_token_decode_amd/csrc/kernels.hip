@@ -65,8 +65,18 @@ constexpr float lazy_octaves() { return FP8P ? 8.0f : 60.0f; }
 // fp8 Q: a row's largest |q| maps to the e4m3 maximum 448.  The fp32
 // rounding of 448 / M and of q * (448 / M) can put a value up to 2 ulps above
 // 448; the gfx950 conversion rounds to nearest before it saturates (inputs up
-// to 463 give 448, checked on the MI355X), so no clamp is needed.
+// to 463 give 448, checked on the MI355X), so no clamp is needed there.
 constexpr float kQ8Top = 448.0f;
+
+// 1 / s for a row whose largest |q| (the scale rule's M) is M, s = M / 448.
+// Below 2^-100 (a zero row, or values near the bottom of the fp32 range, where
+// 448 / M would overflow to +inf and turn the row into NaN) 1 / s stays at
+// 448 * 2^100: q / s is then finite and far inside the e4m3 range, and the
+// row's scores (all below 2^-100 in size) give a near-uniform softmax.  The
+// row's softmax constant is scale_log2 / inv_s in both cases.
+__device__ __forceinline__ float q8_inv_scale(float M) {
+  return M > 0x1p-100f ? kQ8Top / M : kQ8Top * 0x1p100f;
+}
 
 // LDS holds every KV tile as bf16 rows: 1152 bytes = 72 chunks of 16 B,
 // physical chunk = logical chunk XOR swz(key) inside aligned groups of 8
@@ -1227,9 +1237,8 @@ __device__ __forceinline__ void load_q8(const UnitSetup& us, int grow0, int l16,
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const float M = fmaxf(half_max[rt], xs[((wave ^ 1) * NRT + rt) * 16 + l16]);
-    // 1 / s with s = M / 448 (no clamp needed: see kQ8Top)
-    const float inv = M > 0.0f ? kQ8Top / M : 1.0f;
-    c[rt] = us.scale_log2 * (M > 0.0f ? M / kQ8Top : 1.0f);
+    const float inv = q8_inv_scale(M);
+    c[rt] = us.scale_log2 / inv;
     auto q = [&](unsigned bits) {  // bf16 bits -> q / s, inside the e4m3 range
       return __builtin_bit_cast(float, bits) * inv;
     };
@@ -1391,9 +1400,8 @@ __device__ __forceinline__ void load_q8k(const UnitSetup& us, int grow0, int l16
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const float M = fmaxf(hm[rt], xmax[((wave ^ 1) * NRT + rt) * 64 + lane]);
-    // 1 / s with s = M / 448 (no clamp needed: see kQ8Top)
-    const float inv = M > 0.0f ? kQ8Top / M : 1.0f;
-    c[rt] = us.scale_log2 * (M > 0.0f ? M / kQ8Top : 1.0f);
+    const float inv = q8_inv_scale(M);
+    c[rt] = us.scale_log2 / inv;
     auto q = [&](unsigned bits) {  // bf16 bits -> q / s, inside the e4m3 range
       return __builtin_bit_cast(float, bits) * inv;
     };

@@ -76,6 +76,8 @@ def _load():
         lib.oracle_mla_partial.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         _lib = lib
         return lib
 
@@ -190,3 +192,8 @@ def mla_partial(q_bits, kv, q_len, kv_len, H, b, i, h, lo, hi, *, kv_is_fp8=Fals
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the following oracle calls (timing only)."""
+    _load().oracle_set_num_threads(int(n))

@@ -394,3 +394,13 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Thread count for the following calls (timing runs: a single-thread run
+ * beside the all-core one).  n < 1 is ignored. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

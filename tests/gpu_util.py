@@ -69,27 +69,25 @@ def compare(o, lse, ro, rl, fp8, what=""):
     do = float(np.max(np.abs(o - ro)))
     dl = float(np.max(np.abs(lse - rl)))
     mo = float(np.max(np.abs(ro)))
-    log(f"  {what}: max|dO|={do:.3e} (max|O_ref|={mo:.3e}) max|dLSE|={dl:.3e}")
+    rel = do / mo if mo > 0 else float("inf")
+    log(f"  {what}: max|dO|={do:.3e} (max|O_ref|={mo:.3e}, ratio {rel:.3e}) max|dLSE|={dl:.3e}")
     assert do <= TOL_O[fp8], f"{what}: max|dO| {do} > {TOL_O[fp8]}"
     assert dl <= TOL_LSE, f"{what}: max|dLSE| {dl} > {TOL_LSE}"
     return do, dl, mo
 
 
 def sample_rows(inp, count, seed=0):
-    """Row indices (token * H + head) covering first/last tokens of every
-    sequence plus seeded random rows."""
+    """Row indices (token * H + head): for every token of every sequence the
+    first, a middle and the last head (so every sequence, every folded tile
+    and every tile of a wide-head workload is compared), then seeded random
+    rows until `count` rows are chosen (never fewer than the per-token rows)."""
     H = inp.H
-    q_off = np.concatenate([[0], np.cumsum(inp.q_len)])
+    total = int(np.sum(inp.q_len)) * H
     rows = set()
-    for b in range(inp.batch):
-        first = int(q_off[b]) * H
-        last = (int(q_off[b + 1]) - 1) * H
-        rows.update([first, first + H - 1, last, last + H - 1])
-        if len(rows) >= count:
-            break
+    for tok in range(int(np.sum(inp.q_len))):
+        rows.update([tok * H, tok * H + H // 2, tok * H + H - 1])
     rng = np.random.default_rng([seed, 11])
-    total = int(q_off[-1]) * H
-    count = min(count, total)
+    count = min(max(count, len(rows)), total)
     while len(rows) < count:
         rows.add(int(rng.integers(0, total)))
     return np.array(sorted(rows), dtype=np.int64)

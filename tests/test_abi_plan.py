@@ -192,3 +192,20 @@ def test_paged_run_argument_checks():
     assert call(page=64, stride=46) == mb.MLA_ERR_INVALID_ARGUMENT  # 3000 keys need 47 pages
     assert call(page=32, stride=93) == mb.MLA_ERR_INVALID_ARGUMENT  # ... or 94
     assert "page" in mb.lib().mla_last_error().decode()
+
+
+def test_binding_rejects_host_tensors_before_the_library_call():
+    """The binding checks torch tensors against the plan before their pointers
+    reach the kernels: a host tensor is refused with ValueError (the
+    device-side size, dtype and contiguity checks are in the GPU suite)."""
+    import torch
+    p = plan(12, [2], [100], force_splits=2)
+    q = torch.zeros((2, 12, mb.DQK), dtype=torch.bfloat16)
+    kv = torch.zeros((100, mb.DQK), dtype=torch.bfloat16)
+    o = torch.zeros((2, 12, mb.DV), dtype=torch.bfloat16)
+    lse = torch.zeros((2, 12), dtype=torch.float32)
+    ws = torch.zeros((p.workspace_bytes,), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device"):
+        mb.mla_decode_run(p, q, kv, 0.04, 1.0, o, lse, ws, stream=0)
+    with pytest.raises(ValueError, match="device"):
+        mb.mla_decode_reduce(p, ws, o, lse, stream=0)

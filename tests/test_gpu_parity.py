@@ -244,6 +244,13 @@ def test_identical_keys_give_the_value_row():
     assert np.abs(lse - rl).max() <= 1e-3
 
 
+def _check_covers_every_sequence(inp, rows):
+    q_off = np.concatenate([[0], np.cumsum(inp.q_len)]) * inp.H
+    for b in range(inp.batch):
+        assert np.any((rows >= q_off[b]) & (rows < q_off[b + 1])), f"sequence {b} not sampled"
+        assert q_off[b] in rows and q_off[b + 1] - 1 in rows
+
+
 @pytest.mark.parametrize("name", gen.WORKLOADS)
 def test_workload_sampled_rows(name):
     gu.log(f"workload {name}")
@@ -253,20 +260,26 @@ def test_workload_sampled_rows(name):
            f"fold/tiles/splits/L of seq0={plan.query(0)}")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     rows = gu.sample_rows(inp, 24 if name != "small" else 48)
+    _check_covers_every_sequence(inp, rows)
+    gu.log(f"  {len(rows)} rows compared")
     ro, rl = gu.oracle_rows(inp, rows)
     gu.compare(o.reshape(-1, 512)[rows], lse.reshape(-1)[rows], ro, rl, inp.kv_fp8, name)
 
 
-@pytest.mark.parametrize("name", ["h12_131k", "h96_125k", "h12_1m_fp8"])
+@pytest.mark.parametrize("name", ["h12_131k", "h96_125k", "h12_1m_fp8", "ragged"])
 def test_workload_peaked_sampled_rows(name):
     gu.log(f"peaked workload {name}")
     inp = gen.peaked_inputs(gu.workload_inputs(name), beta=10.0, seed=1)
     o, lse, _ = gu.run_gpu(inp)
     rows = gu.sample_rows(inp, 16, seed=2)
+    _check_covers_every_sequence(inp, rows)
     ro, rl = gu.oracle_rows(inp, rows)
     do, dl, mo = gu.compare(o.reshape(-1, 512)[rows], lse.reshape(-1)[rows], ro, rl, inp.kv_fp8,
                             f"{name} peaked")
     assert mo > 5 * gu.TOL_O[inp.kv_fp8]  # the check is discriminating
+    # every sampled row is discriminating, not only the largest one
+    per_row = np.abs(ro).max(axis=1)
+    assert np.all(per_row > gu.TOL_O[inp.kv_fp8]), f"rows with small |O|: {np.sum(per_row <= gu.TOL_O[inp.kv_fp8])}"
 
 
 @pytest.mark.parametrize("fp8", [False, True])
@@ -286,9 +299,55 @@ def test_query_rows_of_very_different_magnitudes(fp8):
     qr[40] = 0.0
     qr[17, :gen.DV] *= np.float32(2.0 ** -100)  # latent ~1e-31 next to an O(1) rope part
     qr[63, :gen.DV] = 0.0                          # rope part only
+    # rows whose largest |q| is below 448 / FLT_MAX: 448 / max|q| overflows fp32,
+    # so the per-row fp8 scale must be bounded (bf16 subnormals and zeros)
+    qr[70] *= np.float32(2.0 ** -130)
+    qr[71] *= np.float32(2.0 ** -140)
+    qr[72, :gen.DV] = np.float32(2.0 ** -133)      # one subnormal step, latent part only
+    qr[72, gen.DV:] = 0.0
+    # rows whose entries, scaled so that the largest maps to 448, sit just
+    # under e4m3 rounding midpoints of several binades (and the largest a hair
+    # below the top code, so q * 448 / max|q| rounds across it)
+    mids = np.array([0.5 * (a + b) for a, b in [(256, 288), (112, 120), (28, 30), (3.5, 3.75),
+                                                 (0.4375, 0.46875), (2 ** -7, 1.5 * 2 ** -7)]])
+    vals = (mids * (1 - 2 ** -7) / 448.0).astype(np.float32)
+    for r, scale in ((73, 1.0), (74, 3.0), (75, 2.0 ** -20)):
+        row = np.resize(vals, gen.DQK).astype(np.float32) * np.float32(scale)
+        row[::7] *= -1
+        row[5] = np.float32(scale * (1 - 2 ** -9))
+        qr[r] = row
     inp = gen.Inputs(H, inp.q_len, inp.kv_len, gen.bf16_bits_from_f32(q), inp.kv, inp.kv_fp8,
                      inp.kv_scale)
     ro, rl = gu.oracle_full(inp)
     for splits in (1, 4):
         o, lse, plan = gu.run_gpu(inp, force_splits=splits)
         gu.compare(o, lse, ro, rl, fp8, f"row magnitudes splits={splits}")
+
+
+def test_binding_rejects_tensors_that_do_not_match_the_plan():
+    """Short, strided or wrongly typed device tensors are refused by the
+    binding (ValueError) before any kernel is launched."""
+    import torch
+    from mla_token_decode_amd import binding as mb
+    inp = gen.random_inputs(12, [4], [300], False, seed=31)
+    plan = mb.Plan(12, inp.q_len, inp.kv_len, False, force_splits=2)
+    q, kv = gu.to_device(inp)
+    o, lse, ws = mb.alloc_outputs(plan, q.device)
+    bad = [
+        dict(kv=kv[:299]),                                   # fewer KV rows than the plan
+        dict(q=q[:3]),                                       # fewer Q rows
+        dict(o=o.view(-1)[: o.numel() - 512]),               # short O
+        dict(lse=lse.view(-1)[:-1]),                         # short LSE
+        dict(kv=kv.view(torch.int16)),                       # wrong dtype
+        dict(q=q.transpose(1, 2).contiguous().transpose(1, 2)),  # strided
+        dict(lse=lse.to(torch.float64)),
+    ]
+    for c in bad:
+        kw = dict(q=q, kv=kv, o=o, lse=lse)
+        kw.update(c)
+        with pytest.raises(ValueError):
+            mb.mla_decode_run(plan, kw["q"], kw["kv"], inp.sm_scale, 1.0, kw["o"], kw["lse"], ws)
+    fp8 = gen.random_inputs(12, [4], [300], True, seed=31)
+    p8 = mb.Plan(12, fp8.q_len, fp8.kv_len, True)
+    with pytest.raises(ValueError):  # bf16 KV given to an fp8 plan
+        mb.mla_decode_run(p8, q, kv, inp.sm_scale, 0.01, o, lse, ws)
