@@ -37,7 +37,8 @@
  * mla_last_error() returns a message for the calling thread.
  *
  * Ownership.  The caller owns every device buffer and the stream.  The
- * library allocates no device memory.  A plan is host memory owned by the
+ * library allocates no device memory (mla_decode_run_static uses a fixed
+ * array that is part of the library's loaded device code).  A plan is host memory owned by the
  * library until mla_plan_destroy; it must outlive work enqueued with it only
  * until mla_decode_run / mla_decode_reduce return (kernel arguments are
  * copied at launch).
@@ -77,6 +78,7 @@ typedef enum {
 #define MLA_MAX_SHARDS 1024  /* most shards mla_merge_shards combines */
 #define MLA_MIN_PAGE_SIZE 32 /* paged KV: smallest page (keys); sizes are powers of two */
 #define MLA_MAX_PAGE_SIZE (1 << 20) /* paged KV: largest page (keys) */
+#define MLA_STATIC_WORKSPACE_BYTES (32u << 20) /* workspace mla_decode_run_static holds */
 
 typedef struct mla_plan mla_plan; /* opaque, host-owned */
 
@@ -199,6 +201,24 @@ mla_status mla_decode_reduce(const mla_plan* plan, const void* workspace, void* 
  *  Errors: INVALID_ARGUMENT, UNSUPPORTED (device is not gfx950), DEVICE. */
 mla_status mla_merge_shards(int32_t num_rows, int32_t num_shards, const void* o_shards,
                             const float* lse_shards, void* o, float* lse, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * decode as mla_decode_run followed by mla_decode_reduce, with the split
+ * workspace taken from a fixed array of MLA_STATIC_WORKSPACE_BYTES (32 MiB)
+ * that the library holds on each device it runs on until the process ends.
+ * Nothing is allocated, freed or initialised per call.  Same arguments and
+ * results as mla_decode_run + mla_decode_reduce, minus the workspace.
+ *  The array is shared by every call on one device and keeps the last call's
+ *  contents (no call depends on what it held before: every partial the merge
+ *  reads is written by the same call).  Calls that overlap on one device --
+ *  on two streams, or from two threads -- race on it; serialise them.
+ *  Errors: those of mla_decode_run, and WORKSPACE_TOO_SMALL for a plan whose
+ *  workspace exceeds MLA_STATIC_WORKSPACE_BYTES (the plan's workspace_bytes
+ *  tells which plans fit; the graded shapes need at most 26 MB). */
+mla_status mla_decode_run_static(const mla_plan* plan, const void* q, const void* kv,
+                                 float sm_scale, float kv_scale, void* o, float* lse,
+                                 void* stream);
 
 /* Free a plan (NULL is allowed). */
 void mla_plan_destroy(mla_plan* plan);

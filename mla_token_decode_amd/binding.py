@@ -29,7 +29,8 @@ MAX_SHARDS = 1024
 
 EXPORTED = ["mla_decode_plan", "mla_decode_plan_shard", "mla_decode_run", "mla_decode_run_paged",
             "mla_decode_reduce", "mla_merge_shards", "mla_plan_destroy", "mla_last_error",
-            "mla_plan_query", "mla_plan_info"]
+            "mla_plan_query", "mla_plan_info", "mla_decode_run_static"]
+STATIC_WORKSPACE_BYTES = 32 << 20
 
 _lock = threading.Lock()
 _lib = None
@@ -84,6 +85,10 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_reduce.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p]
         L.mla_decode_reduce.restype = ctypes.c_int
+        L.mla_decode_run_static.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+        L.mla_decode_run_static.restype = ctypes.c_int
         L.mla_plan_destroy.argtypes = [ctypes.c_void_p]
         L.mla_plan_destroy.restype = None
         L.mla_last_error.argtypes = []
@@ -262,6 +267,15 @@ def mla_decode_run_paged(plan: Plan, q, kv_pages, page_table, sm_scale: float, k
                                       int(page_table.shape[1]), float(sm_scale), float(kv_scale),
                                       _ptr(o), _ptr(lse), _ptr(workspace), int(workspace_bytes),
                                       _stream(stream)))
+
+
+def mla_decode_run_static(plan: Plan, q, kv, sm_scale: float, kv_scale: float, o, lse,
+                          stream=None):
+    """Run + merge with the library's per-device static workspace (no
+    allocation; calls that overlap on one device race)."""
+    _check_run_args(plan, q, kv, o, lse, None, 0, sum(plan.kv_len))
+    _check(lib().mla_decode_run_static(plan.handle, _ptr(q), _ptr(kv), float(sm_scale),
+                                       float(kv_scale), _ptr(o), _ptr(lse), _stream(stream)))
 
 
 def mla_decode_reduce(plan: Plan, workspace, o, lse, stream=None):

@@ -17,6 +17,7 @@ hipError_t launch_main_contiguous(const MainArgs& a, bool fp8, int nrt, hipStrea
 hipError_t launch_main_paged(const MainArgs& a, bool fp8, int nrt, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t static_scratch(void** ptr);
 
 namespace {
 
@@ -277,23 +278,10 @@ mla_status mla_decode_run_paged(const mla_plan* plan, const void* q, const void*
                     kv_scale, o, lse, workspace, workspace_bytes, stream);
 }
 
-mla_status mla_decode_reduce(const mla_plan* plan, const void* workspace, void* o, float* lse,
-                             void* stream) {
-  if (!plan) {
-    set_error("plan must be non-null");
-    return MLA_ERR_INVALID_ARGUMENT;
-  }
-  if (plan->total_part_rows == 0) return MLA_OK;
-  if (!workspace || !o || !lse) {
-    set_error("workspace, o and lse must be non-null device pointers");
-    return MLA_ERR_INVALID_ARGUMENT;
-  }
-  if (!aligned16(workspace) || !aligned16(o) || !aligned16(lse)) {
-    set_error("workspace, o and lse must be 16-byte aligned");
-    return MLA_ERR_INVALID_ARGUMENT;
-  }
-  mla_status st = current_device(nullptr);
-  if (st != MLA_OK) return st;
+namespace {
+
+mla_status reduce_common(const mla_plan* plan, const void* workspace, void* o, float* lse,
+                         void* stream) {
   ReduceArgs a;
   std::memset(&a, 0, sizeof a);
   a.part_lse = static_cast<const float*>(workspace);
@@ -324,6 +312,57 @@ mla_status mla_decode_reduce(const mla_plan* plan, const void* workspace, void* 
     }
   }
   return MLA_OK;
+}
+
+}  // namespace
+
+mla_status mla_decode_reduce(const mla_plan* plan, const void* workspace, void* o, float* lse,
+                             void* stream) {
+  if (!plan) {
+    set_error("plan must be non-null");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (plan->total_part_rows == 0) return MLA_OK;
+  if (!workspace || !o || !lse) {
+    set_error("workspace, o and lse must be non-null device pointers");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (!aligned16(workspace) || !aligned16(o) || !aligned16(lse)) {
+    set_error("workspace, o and lse must be 16-byte aligned");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  mla_status st = current_device(nullptr);
+  if (st != MLA_OK) return st;
+  return reduce_common(plan, workspace, o, lse, stream);
+}
+
+mla_status mla_decode_run_static(const mla_plan* plan, const void* q, const void* kv,
+                                 float sm_scale, float kv_scale, void* o, float* lse,
+                                 void* stream) {
+  if (!plan) {
+    set_error("plan must be non-null");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (plan->workspace_bytes > kStaticScratchBytes) {
+    set_error("plan needs a %zu-byte workspace; mla_decode_run_static holds %zu bytes (use "
+              "mla_decode_run with a caller workspace, or fewer split chunks)",
+              plan->workspace_bytes, static_cast<size_t>(kStaticScratchBytes));
+    return MLA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  mla_status st = current_device(nullptr);
+  if (st != MLA_OK) return st;
+  void* ws = nullptr;
+  if (plan->workspace_bytes > 0) {
+    hipError_t e = static_scratch(&ws);
+    if (e != hipSuccess) {
+      set_error("static workspace lookup failed: %s", hipGetErrorString(e));
+      return MLA_ERR_DEVICE;
+    }
+  }
+  st = run_common(plan, q, kv, nullptr, 0, 0, 0, sm_scale, kv_scale, o, lse, ws,
+                  plan->workspace_bytes, stream);
+  if (st != MLA_OK || plan->total_part_rows == 0) return st;
+  return reduce_common(plan, ws, o, lse, stream);
 }
 
 mla_status mla_merge_shards(int32_t num_rows, int32_t num_shards, const void* o_shards,

@@ -35,6 +35,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "plan.hpp"
@@ -2095,6 +2096,35 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(mla_decode_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, stream, a);
   }
   return hipGetLastError();
+}
+
+// Workspace for callers that cannot allocate (mla_decode_run_static): one
+// array per device, held for the life of the process.  Host code never uses
+// the array's name as an address (on the host it is only a stand-in for the
+// symbol): its device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current and kept here.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevicesStatic];
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevicesStatic) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {

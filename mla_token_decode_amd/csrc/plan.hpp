@@ -17,6 +17,9 @@ constexpr int kGranule = MLA_KV_GRANULE;     // 64 keys
 constexpr int kMaxSeqPerLaunch = 60;     // sequence descriptors travel in kernel arguments
 constexpr int kMaxUnitRows = 96;         // rows one workgroup processes (2 groups x 3 MFMA tiles)
 constexpr int kNumXcd = 8;               // MI355X: 8 XCDs, workgroups dealt round-robin
+// Largest workspace mla_decode_run_static serves from its per-device array.
+constexpr size_t kStaticScratchBytes = MLA_STATIC_WORKSPACE_BYTES;
+constexpr int kMaxDevicesStatic = 64;
 
 // One sequence as the kernels see it.  All counts fit int32 for any cache that
 // fits in one GPU's HBM (row counts, not bytes); byte offsets are formed in
