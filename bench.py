@@ -43,8 +43,11 @@ HEADLINE = "h12_1m_fp8"
 # The pages' own figure for this shape (B300, cute-dsl fold_sq, H=12 q=8 ctx~1M
 # fp8, median us/call): context on other hardware, not a baseline of this run.
 PAGES_FP8_1M_US_B300 = 168.2
-KERNEL_SOURCE = os.path.join(ROOT, "mla_token_decode_amd", "csrc", "kernels.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mla_decode_main_fp8_h12_q8_1m_hbm_traffic.txt")
+# sources of the headline's main kernel (fp8 KV): their hash ties a counter
+# summary to the code it was taken on
+KERNEL_SOURCES = [os.path.join(ROOT, "mla_token_decode_amd", "csrc", f)
+                  for f in ("fp8_decode.hip", "fp8_agpr.hpp", "device_common.hpp")]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "mla_decode_fp8_h12_q8_1m_hbm_traffic.txt")
 
 
 def log(msg):
@@ -203,8 +206,11 @@ def measure(inp, dev, steps, warmup, flush, paged=None, settle_ms=0, **plan_opts
 
 
 def kernel_source_sha256():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():
@@ -436,7 +442,7 @@ def main():
                      "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
                      "traffic_fetch": traffic["fetch"] if traffic else None,
                      "traffic_write": traffic["write"] if traffic else None,
-                     "kernel": "mla_decode_main (fp8 KV)",
+                     "kernel": "mla_decode_fp8",
                      "algorithmic_bytes": head["kv_bytes"],
                      "kernel_us_mean": round(main_us, 2),
                      "kernel_source_sha256": kernel_source_sha256()},

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmla_decode.so")
-SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "kernels_paged.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "kernels_paged.hip", "fp8_decode.hip",
+           "fp8_decode_paged.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

@@ -15,6 +15,8 @@ namespace mla {
 const char* last_error();
 hipError_t launch_main_contiguous(const MainArgs& a, bool fp8, int nrt, hipStream_t stream);
 hipError_t launch_main_paged(const MainArgs& a, bool fp8, int nrt, hipStream_t stream);
+hipError_t launch_fp8_contiguous(const MainArgs& a, int nrt, hipStream_t stream);
+hipError_t launch_fp8_paged(const MainArgs& a, int nrt, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t static_scratch(void** ptr);
@@ -223,8 +225,10 @@ mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const
     // page-table rows of this launch's sequences (the kernel indexes them from 0)
     a.page_table = page_table ? page_table + static_cast<int64_t>(ln.seq_begin) * pt_stride : nullptr;
     for (int b = ln.seq_begin; b < ln.seq_end; ++b) a.seqs[b - ln.seq_begin] = plan->seqs[b];
-    hipError_t e = page_table ? launch_main_paged(a, fp8, ln.nrt, static_cast<hipStream_t>(stream))
-                              : launch_main_contiguous(a, fp8, ln.nrt, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = fp8 ? (page_table ? launch_fp8_paged(a, ln.nrt, s) : launch_fp8_contiguous(a, ln.nrt, s))
+                       : (page_table ? launch_main_paged(a, false, ln.nrt, s)
+                                     : launch_main_contiguous(a, false, ln.nrt, s));
     if (e != hipSuccess) {
       set_error("main kernel launch failed: %s", hipGetErrorString(e));
       return MLA_ERR_DEVICE;

@@ -1,0 +1,803 @@
+// MLA speculative-verify decode over an fp8 (OCP E4M3FN) KV cache, gfx950.
+//
+// One workgroup (4 waves) per work unit: up to 96 folded rows (F verify tokens
+// x H heads, one contiguous slab of Q) against one split-KV chunk of their
+// sequence, which is streamed from HBM once and shared by all rows -- the
+// fold_sq decode of "[Kimi-K3] Allow DSPARK verify on cutedsl_mla (fold_sq)"
+// (sglang PR #33650), section "Decision rule", paragraph "Why"; split chunks
+// leave normalised partials for the merge kernel (same PR, section "GPU
+// timeline").
+//
+// KV stream.  64-key tiles go from HBM straight into a 4-slot LDS ring with
+// buffer_load_dwordx4 ... lds (no staging registers): the latent part as
+// 64 rows of 512 e4m3 bytes, the rope part as 64 rows of 64 e4m3 bytes, both
+// with their 16-byte chunks XOR-swizzled by the key so that the fragment reads
+// below are free of bank conflicts.  Two tiles are in flight while one is
+// computed.  The per-tensor fp8 scale is folded into the softmax constant and
+// the epilogue.
+//
+// Work of one tile.  Wave w has two roles:
+//   scores  (key half kh = w & 1, row half rh = w >> 1): S^T for keys
+//           32 kh .. 32 kh + 31 of the tile and 16 N rows of the unit, over
+//           all 576 columns: v_mfma_f32_16x16x128_f8f6f4 with K (A operand)
+//           from LDS and Q (B operand) quantised per row to e4m3 in
+//           registers -- 4 latent blocks of 128 columns and the 64 rope
+//           columns zero-padded to 128; then the softmax of those scores into
+//           e4m3 P, written to a P buffer in LDS;
+//   values  (column quarter w): O^T[128 w .. 128 w + 127][all rows] +=
+//           V^T P^T with v_mfma_f32_32x32x64_f8f6f4: V^T from LDS through
+//           the transposing 8-bit reads, P^T from the P buffer.
+// The PV of tile t runs in the iteration after its scores, once the barrier
+// has published every wave's P.
+//
+// Softmax.  Base-2 logits with a lazy per-row reference m: P = 2^(c s - m),
+// c = sm_scale * kv_scale * log2(e) * s_q (the row's Q scale).  The reference
+// only moves when a row's scores pass it by more than 8 octaves (so P <= 2^8
+// stays inside e4m3, whose largest value is 448), as in the pages' own fp8
+// kernel ("bench(cake_mla_varq_dcp_decode): ..." (flashinfer PR #5588),
+// embedded follow-up, section "Summary": a lazy E4M3 reference and a deferred
+// O rescale).  Each wave checks its own scores against the reference and
+// publishes one flag with its P; when any flag of a tile is set, every wave
+// takes the rare path after the barrier: the two waves of each row exchange
+// row maxima, move the references, recompute that tile's P, and all waves
+// rescale the O rows and row sums formed against the old reference.  The
+// first tile of a unit takes that path to set the references.
+#include "device_common.hpp"
+#include "fp8_agpr.hpp"
+
+namespace mla {
+namespace fp8k {
+
+constexpr int kThreads = 256;
+constexpr int kKeys = 64;                    // keys per tile
+constexpr int kLatB = 512;                   // latent bytes of a key
+constexpr int kRopeB = 64;                   // rope bytes of a key
+constexpr int kRowB = kLatB + kRopeB;        // 576: one KV row in memory
+constexpr int kTileB = kKeys * kRowB;        // 36864: one LDS slot
+constexpr int kRopeOff = kKeys * kLatB;      // 32768: rope rows inside a slot
+constexpr int kSlots = 4;
+constexpr int kPOff = kSlots * kTileB;       // 147456: two P buffers
+constexpr int kPBuf = kMaxUnitRows * kKeys;  // 6144: rows x 64 e4m3
+constexpr int kMisc = kPOff + 2 * kPBuf;     // 159744
+constexpr int kFlagOff = kMisc;              // [2 parities][4 waves] u32
+constexpr int kRowMaxOff = kMisc + 64;       // [2 key halves][96 rows] f32
+constexpr int kFactorOff = kRowMaxOff + 768; // [96 rows] f32
+constexpr int kLsumOff = kFactorOff + 384;   // [2 key halves][96 rows] f32
+constexpr int kMrefOff = kLsumOff + 768;     // [96 rows] f32
+constexpr int kLdsBytes = kMisc + 4096;      // 163840: all of a CU's LDS
+static_assert(kMrefOff + 384 <= kLdsBytes, "misc area");
+static_assert(kMaxUnitRows == 96, "P buffer and misc arrays hold 96 rows");
+constexpr float kLazy = 8.0f;  // octaves a score may pass the reference by
+
+// --------------------------------------------------------------- KV stream
+
+// Where a unit's tiles live: a contiguous run of rows, or the pages of a pool
+// (pages of 2^shift >= 32 keys; a tile's two 32-key halves each lie in one
+// page).  Chunk-relative key k is sequence key lo + k.
+template <bool PAGED>
+struct Src {
+  const uint8_t* base;    // contiguous: row `lo` of the sequence; paged: the pool
+  const int32_t* pt_row;  // paged: the sequence's page-table row
+  int lo, nkeys, shift, last_idx;
+  unsigned max_page;
+
+  __device__ __forceinline__ int entry_idx(int t, int h) const {
+    return min((lo + kKeys * t + 32 * h) >> shift, last_idx);
+  }
+  // First row (of the pool, or of the chunk) of half h of tile t, given the
+  // page-table entry of that half (paged only).
+  __device__ __forceinline__ const uint8_t* half_base(int t, int h, int entry) const {
+    if constexpr (!PAGED) {
+      return base + (int64_t)(kKeys * t + 32 * h) * kRowB;
+    } else {
+      const int64_t prow = ((int64_t)min((unsigned)entry, max_page) << shift) +
+                           ((lo + kKeys * t + 32 * h) & ((1 << shift) - 1));
+      return base + prow * kRowB;
+    }
+  }
+  // Keys of half h of tile t that exist (0..32): the rest read as zero.
+  __device__ __forceinline__ int half_rows(int t, int h) const {
+    return max(0, min(32, nkeys - kKeys * t - 32 * h));
+  }
+};
+
+// Page-table entries of the two halves of tile t, fetched by scalar loads
+// waited for together with the LDS traffic in front of the tile barrier (no
+// scalar load is ever outstanding while the loop's LDS waits run).
+template <bool PAGED>
+__device__ __forceinline__ void barrier_fetch(const Src<PAGED>& src, int t, int (&e)[2]) {
+  if constexpr (PAGED) {
+    asm volatile("s_load_dword %0, %2, %3\n\ts_load_dword %1, %2, %4\n\ts_waitcnt lgkmcnt(0)\n\t"
+                 "s_barrier"
+                 : "=&s"(e[0]), "=&s"(e[1])
+                 : "s"(src.pt_row), "s"(4 * src.entry_idx(t, 0)), "s"(4 * src.entry_idx(t, 1))
+                 : "memory");
+  } else {
+    e[0] = e[1] = 0;
+    lds_barrier();
+  }
+}
+template <bool PAGED>
+__device__ __forceinline__ void fetch_now(const Src<PAGED>& src, int t, int (&e)[2]) {
+  if constexpr (PAGED) {
+    asm volatile("s_load_dword %0, %2, %3\n\ts_load_dword %1, %2, %4\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&s"(e[0]), "=&s"(e[1])
+                 : "s"(src.pt_row), "s"(4 * src.entry_idx(t, 0)), "s"(4 * src.entry_idx(t, 1))
+                 : "memory");
+  } else {
+    e[0] = e[1] = 0;
+  }
+}
+
+// One 16-byte-per-lane load of global memory straight into LDS: the wave's 64
+// lanes fill the 1 KB at `dst` (lane i at dst + 16 i) from their own offsets
+// into the descriptor's range (bytes past the range read as zero).  Counted
+// by vmcnt; the compiler does not see it, so every wait for it is explicit.
+__device__ __forceinline__ void dma16(const lds_u8* dst, int voff, __amdgpu_buffer_rsrc_t r) {
+  const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0v), "v"(voff), "s"(r) : "memory");
+}
+
+// Per-lane global offsets of the 9 loads of a tile (8 latent, 1 rope).  Load
+// k < 8 fills LDS chunks 256 k + tid of the latent rows: key 8 k + tid / 32,
+// physical chunk tid % 32 = logical chunk ^ (key & 7) (the XOR is an
+// involution; key & 7 = tid / 32).  Load 8 fills rope chunk tid: key tid / 4,
+// physical chunk tid % 4 = logical ^ ((key >> 1) & 3).
+struct DmaLanes {
+  int lat, rope;
+};
+__device__ __forceinline__ DmaLanes dma_lanes(int tid) {
+  DmaLanes d;
+  d.lat = (tid >> 5) * kRowB + 16 * ((tid & 31) ^ (tid >> 5));
+  d.rope = ((tid >> 2) & 31) * kRowB + kLatB + 16 * ((tid & 3) ^ ((tid >> 3) & 3));
+  return d;
+}
+
+// Issue the 9 loads of tile t into `slot` (tiles past the chunk load nothing
+// but still count).  e: page-table entries of the tile's halves (paged).
+template <bool PAGED>
+__device__ __forceinline__ void issue_tile(const Src<PAGED>& src, int t, const int (&e)[2],
+                                           lds_u8* slot, const DmaLanes& dl, int wave) {
+  const uint8_t* hb[2] = {src.half_base(t, 0, e[0]), src.half_base(t, 1, e[1])};
+  const int hr[2] = {src.half_rows(t, 0), src.half_rows(t, 1)};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int h = k >> 2, sub = k & 3;  // keys 8 sub .. 8 sub + 7 of half h
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, hr[h] - 8 * sub));
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(uniform_ptr(hb[h] + 8 * sub * kRowB), (uint32_t)(rows * kRowB));
+    dma16(slot + 4096 * k + 1024 * wave, dl.lat, r);
+  }
+  {
+    const int h = wave >> 1;  // rope keys of this wave: 16 wave .. 16 wave + 15
+    const int rows = __builtin_amdgcn_readfirstlane(hr[h]);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr(hb[h]), (uint32_t)(rows * kRowB));
+    dma16(slot + kRopeOff + 1024 * wave, dl.rope, r);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_tiles_behind() {
+  static_assert(N == 9 || N == 18, "9 loads per tile");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// ------------------------------------------------------------------ MFMAs
+//
+// Inline assembly with explicit register files (the compiler pads no hazards
+// around it: the callers keep >= 2 wait states between a VALU write and an
+// MFMA read of the same VGPRs, and >= 19 between an MFMA result and its first
+// VALU or LDS read).
+
+// S^T (16 keys x 16 rows) += K (A, 16 x 128 e4m3) . Q^T (B, 128 x 16 e4m3).
+template <bool ZERO, bool QA>
+__device__ __forceinline__ void mfma_qk(f32x4& acc, const i32x8& k, const i32x8& q) {
+  if constexpr (ZERO && QA)
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "a"(q));
+  else if constexpr (ZERO)
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "v"(q));
+  else if constexpr (QA)
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "a"(q));
+  else
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "v"(q));
+}
+// O^T (32 value columns x 32 rows) += V^T (A, 32 x 64) . P^T (B, 64 x 32):
+// OAcc<b>::pv, with O block b = cb N + pbk in fixed AGPRs (fp8_agpr.hpp).
+
+// ------------------------------------------------------------ fragments
+
+// K fragment (A operand) of key block kb (16 keys), column block db (0..3
+// latent, 4 rope): lane 16 g + m holds key 32 kh + 16 kb + m, columns
+// 128 db + 32 g .. + 31 (rope: rope columns 32 (g & 1) .. + 31; lanes g >= 2
+// meet zero Q columns).  Two 16-byte reads from per-lane bases that carry the
+// swizzle; kb and db are immediate offsets.
+struct KBase {
+  int lat[2], rope[2];
+};
+__device__ __forceinline__ KBase k_base(int kh, int l16, int g) {
+  KBase b;
+  const int key = 32 * kh + l16;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    b.lat[x] = key * kLatB + 16 * ((2 * g + x) ^ (l16 & 7));
+    b.rope[x] = kRopeOff + key * kRopeB + 16 * ((2 * (g & 1) + x) ^ ((l16 >> 1) & 3));
+  }
+  return b;
+}
+template <int KB, int DB>
+__device__ __forceinline__ i32x8 read_k(const lds_u8* slot, const KBase& b) {
+  i32x4 a, c;
+  if constexpr (DB < 4) {
+    a = *(const i32x4*)(slot + b.lat[0] + 8192 * KB + 128 * DB);
+    c = *(const i32x4*)(slot + b.lat[1] + 8192 * KB + 128 * DB);
+  } else {
+    a = *(const i32x4*)(slot + b.rope[0] + 1024 * KB);
+    c = *(const i32x4*)(slot + b.rope[1] + 1024 * KB);
+  }
+  return i32x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+}
+
+// V^T fragment (A operand of the PV MFMA) of value columns 128 cq + 32 cb ..
+// + 31: lane l holds column l % 32, keys 32 (l / 32) .. + 31, from four
+// transposing reads of 8 keys each.  In a 16-lane group q of one read, lane
+// 2 j + h points at key 32 (q >> 1) + 8 i + j, columns 16 (q & 1) + 8 h .. + 7
+// of the block, and lane n receives column n of the 8 keys (in key order).
+struct VBase {
+  int cb[4];
+};
+__device__ __forceinline__ VBase v_base(int cq, int lane) {
+  VBase b;
+  const int q = lane >> 4, idx = lane & 15, j = idx >> 1, h = idx & 1;
+  const int key = 32 * (q >> 1) + j;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+    b.cb[cb] = key * kLatB + 16 * (8 * cq + ((2 * cb + (q & 1)) ^ j)) + 8 * h;
+  return b;
+}
+template <int CB>
+__device__ __forceinline__ i32x8 read_v(const lds_u8* slot, const VBase& b) {
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  const lds_u8* p = slot + b.cb[CB];
+  const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
+  const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 4096));
+  const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 8192));
+  const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 12288));
+  return i32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+}
+
+// P buffer: row r holds the tile's 64 e4m3 P values of unit row r in key
+// order, its four 16-byte chunks XOR-swizzled by (r >> 1) & 3.  PV fragment
+// (B operand) of row block pb: lane l holds row 32 pb + l % 32, keys
+// 32 (l / 32) .. + 31.
+struct PBase {
+  int rd[2];   // PV reads: chunk 2 G + x of row l % 32
+  int wr[2];   // score-side writes, key block kb: chunk 2 kh + kb of row l16, byte 4 g
+};
+__device__ __forceinline__ PBase p_base(int kh, int rh, int N, int lane) {
+  PBase b;
+  const int l32 = lane & 31, G = lane >> 5, l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) b.rd[x] = l32 * 64 + 16 * ((2 * G + x) ^ ((l32 >> 1) & 3));
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+    b.wr[kb] = (16 * N * rh + l16) * 64 + 16 * ((2 * kh + kb) ^ ((l16 >> 1) & 3)) + 4 * g;
+  return b;
+}
+template <int PB>
+__device__ __forceinline__ i32x8 read_p(const lds_u8* pbuf, const PBase& b) {
+  const i32x4 a = *(const i32x4*)(pbuf + b.rd[0] + 2048 * PB);
+  const i32x4 c = *(const i32x4*)(pbuf + b.rd[1] + 2048 * PB);
+  return i32x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+}
+
+// ------------------------------------------------------------------ Q
+
+// e4m3 Q of this wave's 16 N rows: [rb][db], db 0..3 latent, 4 rope (zero in
+// lanes g >= 2).  With N = 3, row block 2 and the rope blocks of row blocks 0
+// and 1 live in the AGPR groups after O (QAcc 0..6), the rest in VGPRs.
+template <int N>
+constexpr int q_group(int rb, int db) {
+  return N != 3 ? -1 : rb == 2 ? db : db == 4 ? 5 + rb : -1;
+}
+template <int N>
+struct QFrag {
+  i32x8 q[N][5];
+};
+
+// Raw bf16 Q of one row block: lane (l16, g) holds row `row` (clamped to the
+// unit), columns 128 db + 32 g .. + 31 and rope columns 32 g .. + 31 (g < 2;
+// zero otherwise).  Inline-assembly buffer loads, waited for explicitly with
+// wait_q (the tile loads issued after them may stay in flight meanwhile).
+struct QRaw {
+  u32x4 v[5][4];
+};
+__device__ __forceinline__ void load_q_raw(QRaw& r, __amdgpu_buffer_rsrc_t qr, int row, int g) {
+#pragma unroll
+  for (int db = 0; db < 5; ++db) {
+    const int col = db < 4 ? 128 * db + 32 * g : 512 + 32 * (g & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen"
+                   : "=&v"(r.v[db][i]) : "v"(row * (2 * kDqk) + 2 * (col + 8 * i)), "s"(qr) : "memory");
+  }
+}
+// Wait until at most N vector-memory loads issued after r's are outstanding;
+// r's registers are tied to the wait so that no use (or copy) moves above it.
+template <int N>
+__device__ __forceinline__ void wait_q(QRaw& r) {
+#pragma unroll
+  for (int db = 0; db < 5; ++db)
+    asm volatile("s_waitcnt vmcnt(%4)"
+                 : "+v"(r.v[db][0]), "+v"(r.v[db][1]), "+v"(r.v[db][2]), "+v"(r.v[db][3])
+                 : "n"(N) : "memory");
+}
+
+// Quantise one row block to e4m3: the row's scale s = max |q| / 448 over all
+// 576 columns (one shared scale: the rope and latent parts feed one
+// accumulator), bounded below (q8_inv_scale); c = scale_log2 * s.
+template <int N, int RB>
+__device__ __forceinline__ void quantise_q(const UnitSetup& us, QRaw& raw, int g, QFrag<N>& qf,
+                                           float& c) {
+  if (g >= 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw.v[4][i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // max |q| on the packed bf16 bits: with the sign bits cleared, the order of
+  // the 16-bit patterns is the order of the magnitudes (no unpacked copies)
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 mb = {0, 0};
+#pragma unroll
+  for (int db = 0; db < 5; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        mb = __builtin_elementwise_max(mb, __builtin_bit_cast(u16x2, raw.v[db][i][w] & 0x7fff7fffu));
+  const unsigned top = (unsigned)(mb[0] > mb[1] ? mb[0] : mb[1]) << 16;
+  const float M = wave_max_across_groups(__builtin_bit_cast(float, top));
+  const float inv = q8_inv_scale(M);
+  c = us.scale_log2 / inv;
+  static_for<5>([&](auto dc) {
+    constexpr int db = decltype(dc)::value;
+    i32x8 v8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {  // dword k: columns 4 k .. 4 k + 3 of the lane's 32
+      const unsigned x0 = raw.v[db][k >> 1][2 * (k & 1)], x1 = raw.v[db][k >> 1][2 * (k & 1) + 1];
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_bit_cast(float, x0 << 16) * inv,
+                                             __builtin_bit_cast(float, x0 & 0xffff0000u) * inv, 0,
+                                             false);
+      v = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_bit_cast(float, x1 << 16) * inv,
+                                         __builtin_bit_cast(float, x1 & 0xffff0000u) * inv, v,
+                                         true);
+      v8[k] = v;
+    }
+    if constexpr (q_group<N>(RB, db) >= 0)
+      QAcc<q_group<N>(RB, db)>::set(v8);
+    else
+      qf.q[RB][db] = v8;
+  });
+}
+
+// ------------------------------------------------------------------ softmax
+
+// Per-lane softmax state of the lane's rows (one per row block rb).
+template <int N>
+struct Soft {
+  float m[N];     // reference (base-2 logit units); -inf until the row sees a key
+  float nmu[N];   // -m, or 0 while m = -inf
+  float l[N];     // row sum (this lane's keys), tiles up to the last confirmed one
+  float ps[N];    // row sum of the tile whose P was formed last (not yet confirmed)
+  float c[N];     // logit scale of the row
+  int lim[N];     // last chunk-relative key the row may see
+};
+
+// P of score block (kb, rb) of a tile, in two halves (keys 4 g + 0, 1, then
+// 4 g + 2, 3 of the lane's row): the first masks the block in place on the
+// chunk's last tiles (keys past the row's causal limit get -inf), then
+// P = 2^(c s - m) (v_exp_f32 flushes results below the fp32 normal range to
+// 0), packed to e4m3 (keys 4 g .. 4 g + 3 -> bytes 0..3 of one dword) and
+// stored into the P buffer by the second half, which also adds the block's
+// row sum to ps and raises `flag` when an exponent c s - m passes kLazy (a P
+// value above 2^8).  The flag looks at the exponents, not at P: a v_exp_f32
+// result needs one wait state before a dependent VALU read, which the
+// compiler does not pad in front of inline assembly such as max2/max3.
+struct HalfTmp {
+  int pk;
+  float sum, xmax;
+};
+template <int N, int KB, int RB, int HALF>
+__device__ __forceinline__ void softmax_half(f32x4 (&S)[2][N], Soft<N>& sm, int k0, bool edge,
+                                             lds_u8* pbuf, const PBase& pb, HalfTmp& ht,
+                                             bool& flag) {
+  f32x4& s = S[KB][RB];
+  if constexpr (HALF == 0) {
+    if (edge) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = k0 + 16 * KB + i <= sm.lim[RB] ? s[i] : -INFINITY;
+    }
+    const float x0 = __builtin_fmaf(s[0], sm.c[RB], sm.nmu[RB]);
+    const float x1 = __builtin_fmaf(s[1], sm.c[RB], sm.nmu[RB]);
+    const float p0 = __builtin_amdgcn_exp2f(x0);
+    const float p1 = __builtin_amdgcn_exp2f(x1);
+    ht.pk = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __builtin_bit_cast(int, p0), false);
+    ht.sum = p0 + p1;
+    ht.xmax = max2(x0, x1);
+  } else {
+    const float x2 = __builtin_fmaf(s[2], sm.c[RB], sm.nmu[RB]);
+    const float x3 = __builtin_fmaf(s[3], sm.c[RB], sm.nmu[RB]);
+    const float p2 = __builtin_amdgcn_exp2f(x2);
+    const float p3 = __builtin_amdgcn_exp2f(x3);
+    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, ht.pk, true);
+    sm.ps[RB] += ht.sum + (p2 + p3);
+    flag = flag || max3(ht.xmax, x2, x3) > kLazy;
+    *(int*)(pbuf + pb.wr[KB] + 1024 * RB) = pk;
+  }
+}
+
+// The whole softmax of a tile (rare path).
+template <int N>
+__device__ __forceinline__ void softmax_tile(f32x4 (&S)[2][N], Soft<N>& sm, int k0, bool edge,
+                                             lds_u8* pbuf, const PBase& pb) {
+#pragma unroll
+  for (int rb = 0; rb < N; ++rb) sm.ps[rb] = 0.0f;
+  bool flag = false;
+  static_for<2 * N>([&](auto bc) {
+    constexpr int kb = decltype(bc)::value % 2, rb = decltype(bc)::value / 2;
+    HalfTmp ht;
+    softmax_half<N, kb, rb, 0>(S, sm, k0, edge, pbuf, pb, ht, flag);
+    softmax_half<N, kb, rb, 1>(S, sm, k0, edge, pbuf, pb, ht, flag);
+  });
+}
+
+// Rare path for tile t (its scores S still in registers): the references of
+// the rows whose scores passed them move to the row maxima, the tile's P is
+// formed again, and every O row and row sum formed against an old reference
+// is rescaled.  Every wave of the workgroup calls it (two barriers).
+template <int N>
+__device__ __forceinline__ void move_references(f32x4 (&S)[2][N], Soft<N>& sm, int k0,
+                                                bool edge, lds_u8* lds, lds_u8* pbuf,
+                                                const PBase& pb, int kh, int rh, int lane) {
+  const int l16 = lane & 15, g = lane >> 4, l32 = lane & 31;
+  typedef __attribute__((address_space(3))) float lds_f32;
+  lds_f32* rowmax = (lds_f32*)(lds + kRowMaxOff);
+  lds_f32* factor = (lds_f32*)(lds + kFactorOff);
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // MFMA results settled
+#pragma unroll
+  for (int rb = 0; rb < N; ++rb) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s = !edge || k0 + 16 * kb + i <= sm.lim[rb] ? S[kb][rb][i] : -INFINITY;
+        mx = fmaxf(mx, s);
+      }
+    mx = wave_max_across_groups(mx);
+    if (g == 0) rowmax[kh * kMaxUnitRows + 16 * N * rh + 16 * rb + l16] = mx;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int rb = 0; rb < N; ++rb) {
+    const int row = 16 * N * rh + 16 * rb + l16;
+    const float M = fmaxf(rowmax[row], rowmax[kMaxUnitRows + row]) * sm.c[rb];
+    const bool first = sm.m[rb] == -INFINITY;
+    const bool move = M > sm.m[rb] + kLazy;  // false for M = -inf
+    const float mn = move ? M : sm.m[rb];
+    const float f = !move ? 1.0f : first ? 0.0f : __builtin_amdgcn_exp2f(sm.m[rb] - mn);
+    sm.l[rb] *= f;
+    sm.m[rb] = mn;
+    sm.nmu[rb] = mn == -INFINITY ? 0.0f : -mn;
+    if (kh == 0 && g == 0) factor[row] = f;
+  }
+  softmax_tile<N>(S, sm, k0, edge, pbuf, pb);
+#pragma unroll
+  for (int rb = 0; rb < N; ++rb) sm.l[rb] += sm.ps[rb];
+  lds_barrier();
+  // O rows of row block pbk: every lane scales its row (rare: the AGPRs are
+  // read, scaled and written back in place)
+  static_for<N>([&](auto pc) {
+    constexpr int pbk = decltype(pc)::value;
+    const float f = factor[32 * pbk + l32];
+    if (__builtin_amdgcn_ballot_w64(f != 1.0f) != 0) {
+      static_for<4>([&](auto cc) { OAcc<decltype(cc)::value * N + pbk>::scale(f); });
+    }
+  });
+}
+
+// ------------------------------------------------------------------ unit
+
+template <int N, bool PAGED>
+__device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* smem) {
+  UnitSetup us;
+  if (!unit_setup<kRowB, kKeys>(args, us)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = wave & 1, rh = wave >> 1;
+  const int l16 = lane & 15, g = lane >> 4, l32 = lane & 31, G = lane >> 5;
+  lds_u8* lds = (lds_u8*)smem;
+  const int T = us.uc.ntiles;
+
+  Src<PAGED> src;
+  src.base = us.kv_unit;
+  src.pt_row = us.pt_row;
+  src.lo = us.uc.lo;
+  src.nkeys = us.uc.nkeys;
+  src.shift = PAGED ? us.page_shift : 0;
+  src.last_idx = PAGED ? us.last_page_idx : 0;
+  src.max_page = PAGED ? (unsigned)(us.num_pages - 1) : 0u;
+  const DmaLanes dl = dma_lanes(tid);
+
+  // Q loads of the first row block, then tiles 0, 1, 2 start streaming into
+  // slots 0, 1, 2, then Q is quantised (row block by row block) while the
+  // tiles land.
+  Soft<N> sm;
+  QFrag<N> qf;
+  const __amdgpu_buffer_rsrc_t qr =
+      make_rsrc(uniform_ptr(us.q + (int64_t)us.row0 * kDqk), (uint32_t)(us.RU * kDqk * 2));
+  auto q_row = [&](int rb) { return min(16 * N * rh + 16 * rb + l16, us.RU - 1); };
+  static_for<N>([&](auto rc) {
+    constexpr int rb = decltype(rc)::value;
+    const int rv = q_row(rb);
+    sm.lim[rb] = min(us.hi_eff - 1, us.tail0 + (us.rowb0 + rv) / us.H) - us.uc.lo;
+    sm.m[rb] = -INFINITY;
+    sm.nmu[rb] = 0.0f;
+    sm.l[rb] = 0.0f;
+    sm.ps[rb] = 0.0f;
+  });
+  {
+    QRaw raw;
+    load_q_raw(raw, qr, q_row(0), g);
+    int e[2];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      fetch_now(src, k, e);
+      issue_tile(src, k, e, lds + k * kTileB, dl, wave);
+    }
+    wait_q<27>(raw);
+    quantise_q<N, 0>(us, raw, g, qf, sm.c[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<N - 1>([&](auto rc) {
+      constexpr int rb = decltype(rc)::value + 1;
+      load_q_raw(raw, qr, q_row(rb), g);
+      wait_q<0>(raw);
+      quantise_q<N, rb>(us, raw, g, qf, sm.c[rb]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+  {
+    const i32x8 z = {};
+    static_for<4 * N>([&](auto bc) { OAcc<decltype(bc)::value>::zero(z); });
+  }
+
+  const KBase kb_ = k_base(kh, l16, g);
+  const VBase vb = v_base(wave, lane);
+  const PBase pb = p_base(kh, rh, N, lane);
+  lds_u8* pbuf0 = lds + kPOff;
+
+  f32x4 S[2][N];
+  // Score MFMAs of one step (key block kb, column block db) into S[kb][.].
+  auto qk_step = [&](auto kbc, auto dbc, const i32x8& kf) {
+    constexpr int kb = decltype(kbc)::value, db = decltype(dbc)::value;
+    static_for<N>([&](auto rc) {
+      constexpr int rb = decltype(rc)::value;
+      if constexpr (q_group<N>(rb, db) >= 0)
+        QAcc<q_group<N>(rb, db)>::template qk<db == 0>(S[kb][rb], kf);
+      else
+        mfma_qk<db == 0, false>(S[kb][rb], kf, qf.q[rb][db]);
+    });
+  };
+  // Scores of tile t (slot t % 4) into S, K fragments one step ahead of their
+  // MFMAs.  N >= 2: key block 0 first (N independent accumulators per step),
+  // and after(i) runs after each of key block 1's 5 steps (the softmax of
+  // key block 0 goes there); N = 1: the two key blocks alternate (their
+  // accumulators are the independent MFMAs between dependent ones).
+  auto scores = [&](int t, auto&& after) {
+    const lds_u8* slot = lds + (t % kSlots) * kTileB;
+    constexpr bool kMajor = N >= 2;
+    auto step_kb = [](int st) { return kMajor ? st / 5 : st % 2; };
+    auto step_db = [](int st) { return kMajor ? st % 5 : st / 2; };
+    i32x8 kf[2];
+    kf[0] = read_k<0, 0>(slot, kb_);
+    static_for<10>([&](auto sc) {
+      constexpr int st = decltype(sc)::value;
+      constexpr int kb = kMajor ? st / 5 : st % 2, db = kMajor ? st % 5 : st / 2;
+      if constexpr (st + 1 < 10)
+        kf[(st + 1) % 2] = read_k<(kMajor ? (st + 1) / 5 : (st + 1) % 2),
+                                  (kMajor ? (st + 1) % 5 : (st + 1) / 2)>(slot, kb_);
+      qk_step(std::integral_constant<int, kb>{}, std::integral_constant<int, db>{}, kf[st % 2]);
+      if constexpr (kMajor && st == 4)
+        asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // key block 0 retired before its softmax
+      if constexpr (kMajor && st >= 5) after(std::integral_constant<int, st - 5>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    (void)step_kb;
+    (void)step_db;
+    asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // score MFMAs retired before VALU reads
+  };
+
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  typedef __attribute__((address_space(3))) unsigned lds_u32;
+  if (T > 0) {
+    wait_tiles_behind<18>();  // tile 0 landed (tiles 1 and 2 may still be in flight)
+    lds_barrier();
+    scores(0, [](auto) {});
+    // tile 0 sets the references: its flags force the rare path in the loop
+    if (lane == 0) *(lds_u32*)(lds + kFlagOff + 4 * wave) = 1u;
+  }
+
+  for (int t = 0; t < T; ++t) {
+    // tile t + 1 landed (tile t + 2 may still be in flight); the barrier
+    // publishes it, P(t) and the flags of tile t
+    wait_tiles_behind<9>();
+    int e[2];
+    barrier_fetch(src, t + 3, e);
+    lds_u8* pbuf_t = pbuf0 + (t & 1) * kPBuf;
+    const u32x4 fl = *(const lds_u32x4*)(lds + kFlagOff + (t & 1) * 16);
+    // tile t + 3 into the slot of tile t - 1 (read by the PV of the last iteration)
+    issue_tile(src, t + 3, e, lds + ((t + 3) % kSlots) * kTileB, dl, wave);
+    if (__builtin_amdgcn_readfirstlane((fl[0] | fl[1]) | (fl[2] | fl[3])) != 0) {
+      move_references<N>(S, sm, kKeys * t + 32 * kh + 4 * g, kKeys * t + kKeys - 1 > us.uc.min_lim,
+                         lds, pbuf_t, pb, kh, rh, lane);
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < N; ++rb) sm.l[rb] += sm.ps[rb];
+    }
+
+    const bool more = t + 1 < T;
+    const lds_u8* slot_t = lds + (t % kSlots) * kTileB;
+    const int kq = kKeys * (t + 1) + 32 * kh + 4 * g;  // lane's first key of tile t + 1
+    const bool edge1 = kKeys * (t + 1) + kKeys - 1 > us.uc.min_lim;
+    lds_u8* pbuf_n = pbuf0 + ((t + 1) & 1) * kPBuf;
+#pragma unroll
+    for (int rb = 0; rb < N; ++rb) sm.ps[rb] = 0.0f;
+    bool flag = false;
+    HalfTmp ht;
+    // half-slice h of the softmax of tile t + 1 over key block KB: row block
+    // h / 2, half h % 2
+    auto soft_half = [&](auto kbc, auto hc) {
+      constexpr int kb = decltype(kbc)::value, h = decltype(hc)::value;
+      softmax_half<N, kb, h / 2, h % 2>(S, sm, kq, edge1, pbuf_n, pb, ht, flag);
+    };
+    // P(t) and the first V fragments are read ahead of the PV MFMAs
+    i32x8 P[N];
+    i32x8 V[2];
+    if (more) {
+      scores(t + 1, [&](auto ic) {  // key block 0's softmax under key block 1's MFMAs
+        constexpr int i = decltype(ic)::value;  // step 0..4 of key block 1
+        static_for<2 * N>([&](auto hc) {
+          constexpr int h = decltype(hc)::value;
+          if constexpr ((h * 5) / (2 * N) == i) soft_half(std::integral_constant<int, 0>{}, hc);
+        });
+      });
+    }
+    static_for<N>([&](auto pc) {
+      constexpr int pbk = decltype(pc)::value;
+      P[pbk] = read_p<pbk>(pbuf_t, pb);
+    });
+    V[0] = read_v<0>(slot_t, vb);
+    __builtin_amdgcn_sched_barrier(0);
+    // PV of tile t; the rest of the softmax of tile t + 1 between its MFMAs
+    // (key block 1; with N = 1 both key blocks)
+    constexpr int kHalves = N >= 2 ? 2 * N : 4 * N;
+    static_for<4>([&](auto cc) {
+      constexpr int cb = decltype(cc)::value;
+      if constexpr (cb + 1 < 4) V[(cb + 1) % 2] = read_v<cb + 1>(slot_t, vb);
+      static_for<N>([&](auto pc) {
+        constexpr int pbk = decltype(pc)::value;
+        OAcc<cb * N + pbk>::pv(V[cb % 2], P[pbk]);
+        constexpr int mi = cb * N + pbk;  // MFMA index 0 .. 4 N - 1
+        if (more) {
+          static_for<kHalves>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            if constexpr ((h * 4 * N) / kHalves == mi) {
+              if constexpr (N >= 2)
+                soft_half(std::integral_constant<int, 1>{}, hc);
+              else  // N = 1: halves 0..3 = key block 0 (h 0, 1), key block 1 (h 2, 3)
+                soft_half(std::integral_constant<int, h / 2>{}, std::integral_constant<int, h % 2>{});
+            }
+          });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+    if (more) {
+      const unsigned any = __builtin_amdgcn_ballot_w64(flag) != 0 ? 1u : 0u;
+      if (lane == 0) *(lds_u32*)(lds + kFlagOff + ((t + 1) & 1) * 16 + 4 * wave) = any;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads issued past the end
+
+  // ---- epilogue: row sums, then O / l through LDS in full rows
+  typedef __attribute__((address_space(3))) float lds_f32;
+  lds_f32* lsum = (lds_f32*)(lds + kLsumOff);
+  lds_f32* mref = (lds_f32*)(lds + kMrefOff);
+#pragma unroll
+  for (int rb = 0; rb < N; ++rb) {
+    const float lt = wave_sum_across_groups(sm.l[rb]);
+    const int row = 16 * N * rh + 16 * rb + l16;
+    if (g == 0) {
+      lsum[kh * kMaxUnitRows + row] = lt;
+      if (kh == 0) mref[row] = sm.m[rb];
+    }
+  }
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");  // last PV MFMAs retired
+  lds_barrier();
+  const bool split = us.S > 1;
+  lds_u8* stage = lds + wave * (kMaxUnitRows * 256);  // this wave's 96 rows x 128 bf16 columns
+  float inv[N];
+#pragma unroll
+  for (int pbk = 0; pbk < N; ++pbk) {
+    const int row = 32 * pbk + l32;
+    const float l = lsum[row] + lsum[kMaxUnitRows + row];
+    inv[pbk] = l > 0.0f ? us.o_scale / l : 0.0f;
+    if (wave == 0 && G == 0 && row < us.RU) {
+      const float lse = l > 0.0f ? (mref[row] + log2f(l)) * 0.69314718055994530942f : -INFINITY;
+      if (split)
+        us.part_lse[(int64_t)us.part_row0 + ((int64_t)us.t * us.S + us.s) * us.R + us.rowb0 + row] = lse;
+      else
+        us.lse[(int64_t)us.row0 + row] = lse;
+    }
+  }
+  static_for<4>([&](auto cc) {
+    constexpr int cb = decltype(cc)::value;
+    static_for<N>([&](auto pc) {
+      constexpr int pbk = decltype(pc)::value;
+      const int row = 32 * pbk + l32;
+      const f32x16 o = OAcc<cb * N + pbk>::read();  // one block through VGPRs at a time
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        uint2 pk;
+        pk.x = pack_bf16x2(o[4 * a] * inv[pbk], o[4 * a + 1] * inv[pbk]);
+        pk.y = pack_bf16x2(o[4 * a + 2] * inv[pbk], o[4 * a + 3] * inv[pbk]);
+        const int lc = 4 * cb + a;  // 8-column chunk of the wave's 128 columns
+        *(uint2*)(stage + row * 256 + 16 * (lc ^ (row & 15)) + 8 * G) = pk;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  });
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  uint16_t* out = split ? us.part_o + ((int64_t)us.part_row0 + ((int64_t)us.t * us.S + us.s) * us.R +
+                                       us.rowb0) * kDv
+                        : us.o + (int64_t)us.row0 * kDv;
+#pragma unroll
+  for (int i = 0; i < 8 * N; ++i) {
+    const int row = 4 * i + (lane >> 4), lc = lane & 15;
+    if (row < us.RU) {
+      const u32x4 v = *(const u32x4*)(stage + row * 256 + 16 * (lc ^ (row & 15)));
+      *(u32x4*)(out + (int64_t)row * kDv + 128 * wave + 8 * lc) = v;
+    }
+  }
+}
+
+template <int N, bool PAGED>
+__global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8(const MainArgs args) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsBytes];
+  unit_fp8<N, PAGED>(args, smem);
+}
+
+}  // namespace fp8k
+
+// Launch of the fp8-KV main kernel over a launch's units; nrt = 16-row blocks
+// per row half of the widest unit (1..3).
+#ifdef MLA_PAGED_KV
+hipError_t launch_fp8_paged(const MainArgs& a, int nrt, hipStream_t stream) {
+  constexpr bool kPaged = true;
+#else
+hipError_t launch_fp8_contiguous(const MainArgs& a, int nrt, hipStream_t stream) {
+  constexpr bool kPaged = false;
+#endif
+  const int grid = ((a.num_units + kNumXcd - 1) / kNumXcd) * kNumXcd;
+  if (grid == 0) return hipSuccess;
+  if (nrt == 1)
+    hipLaunchKernelGGL((fp8k::mla_decode_fp8<1, kPaged>), dim3(grid), dim3(fp8k::kThreads), 0, stream, a);
+  else if (nrt == 2)
+    hipLaunchKernelGGL((fp8k::mla_decode_fp8<2, kPaged>), dim3(grid), dim3(fp8k::kThreads), 0, stream, a);
+  else if (nrt == 3)
+    hipLaunchKernelGGL((fp8k::mla_decode_fp8<3, kPaged>), dim3(grid), dim3(fp8k::kThreads), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -38,24 +38,15 @@
 #include <mutex>
 #include <type_traits>
 
+#include "device_common.hpp"
 #include "plan.hpp"
 
 namespace mla {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr int kTK = 32;        // keys per compute tile
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = 4;
-constexpr unsigned kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer: range-checked, zero on OOB
 // Softmax reference slack in log2 units: P = 2^(x - m_ref) may reach 2^60
 // with bf16 P (bf16 P and fp32 sums have the range) and 2^8 with e4m3 P (fp8
 // KV: its largest finite value is 448); a larger jump moves the reference and
@@ -63,21 +54,6 @@ constexpr unsigned kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer: range-checked,
 template <bool FP8P>
 constexpr float lazy_octaves() { return FP8P ? 8.0f : 60.0f; }
 
-// fp8 Q: a row's largest |q| maps to the e4m3 maximum 448.  The fp32
-// rounding of 448 / M and of q * (448 / M) can put a value up to 2 ulps above
-// 448; the gfx950 conversion rounds to nearest before it saturates (inputs up
-// to 463 give 448, checked on the MI355X), so no clamp is needed there.
-constexpr float kQ8Top = 448.0f;
-
-// 1 / s for a row whose largest |q| (the scale rule's M) is M, s = M / 448.
-// Below 2^-100 (a zero row, or values near the bottom of the fp32 range, where
-// 448 / M would overflow to +inf and turn the row into NaN) 1 / s stays at
-// 448 * 2^100: q / s is then finite and far inside the e4m3 range, and the
-// row's scores (all below 2^-100 in size) give a near-uniform softmax.  The
-// row's softmax constant is scale_log2 / inv_s in both cases.
-__device__ __forceinline__ float q8_inv_scale(float M) {
-  return M > 0x1p-100f ? kQ8Top / M : kQ8Top * 0x1p100f;
-}
 
 // LDS holds every KV tile as bf16 rows: 1152 bytes = 72 chunks of 16 B,
 // physical chunk = logical chunk XOR swz(key) inside aligned groups of 8
@@ -118,60 +94,6 @@ struct Stage {
 template <bool FP8, int NRT>
 constexpr int stage_sets() { return FP8 ? (NRT == 1 ? 3 : 2) : (NRT == 3 ? 1 : 2); }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           (int)kRsrcWord3);
-}
-
-// A pointer every lane agrees on, moved to scalar registers.
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
-}
-
-// Workgroup barrier that orders LDS traffic only (global loads stay in flight).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) with
-// the gfx950 lane-swap instructions: permlane16_swap exchanges the odd 16-lane
-// rows of one operand with the even rows of the other, permlane32_swap the
-// upper half with the lower half; feeding the same value to both operands and
-// combining the two results gives every lane the value of its partner.
-// Maxima of values that are never NaN, as plain instructions: fmaxf would
-// first quiet possible signalling NaNs of operands the compiler cannot see the
-// origin of (inline-assembly results), one extra instruction per operand.
-__device__ __forceinline__ float max2(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-__device__ __forceinline__ float wave_max_across_groups(float v) {
-  const unsigned u = __builtin_bit_cast(unsigned, v);
-  auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = max2(__builtin_bit_cast(float, (unsigned)r16[0]), __builtin_bit_cast(float, (unsigned)r16[1]));
-  const unsigned w = __builtin_bit_cast(unsigned, v);
-  auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return max2(__builtin_bit_cast(float, (unsigned)r32[0]), __builtin_bit_cast(float, (unsigned)r32[1]));
-}
-
-__device__ __forceinline__ float wave_sum_across_groups(float v) {
-  const unsigned u = __builtin_bit_cast(unsigned, v);
-  auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = __builtin_bit_cast(float, (unsigned)r16[0]) + __builtin_bit_cast(float, (unsigned)r16[1]);
-  const unsigned w = __builtin_bit_cast(unsigned, v);
-  auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return __builtin_bit_cast(float, (unsigned)r32[0]) + __builtin_bit_cast(float, (unsigned)r32[1]);
-}
 
 // 8 fp8 codes (two dwords) -> 8 bf16, exact (OCP E4M3FN -> bf16 never rounds).
 __device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 w) {
@@ -183,22 +105,9 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 w) {
                __builtin_bit_cast(unsigned, c), __builtin_bit_cast(unsigned, d)};
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  uint16_t xu = __builtin_bit_cast(uint16_t, x), yu = __builtin_bit_cast(uint16_t, y);
-  return (uint32_t)xu | ((uint32_t)yu << 16);
-}
 
 // ------------------------------------------------------------------ loader
 
-// Compile-time loop helper.
-template <int N, typename F, int I = 0>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<N, F, I + 1>(static_cast<F&&>(f));
-  }
-}
 
 // Descriptor of compute tile `t` of the unit (keys [32 t, 32 t + 32)): rows
 // past `nkeys` read as zero, tiles past the end read nothing.  (readfirstlane:
@@ -560,74 +469,6 @@ constexpr int exchange_bytes() { return key_split<FP8, NRT>() ? 49152 : 2 * kWav
 template <bool FP8>
 constexpr bool stage_with_scores() { return !FP8; }
 
-struct UnitCtx {
-  int lo, nkeys, ntiles, min_lim;
-};
-
-// Everything a unit needs, copied out of the launch arguments (all fields are
-// workgroup-uniform).
-struct UnitSetup {
-  UnitCtx uc;
-  int t, s, R, H, S, rowb0, RU, row0, tail0, hi_eff, part_row0;
-  float scale_log2, o_scale;
-  const uint16_t* q;
-  const uint8_t* kv_unit;  // contiguous KV: first row of the unit's chunk; paged: the pool
-  const int32_t* pt_row;   // paged KV: the sequence's page-table row (null: contiguous)
-  int page_shift, last_page_idx, num_pages;
-  uint16_t* o;
-  float* lse;
-  float* part_lse;
-  uint16_t* part_o;
-};
-
-template <bool FP8>
-__device__ __forceinline__ bool unit_setup(const MainArgs& args, UnitSetup& us) {
-  const int p = blockIdx.x;
-  const int u = (p % kNumXcd) * args.units_per_xcd + p / kNumXcd;  // XCD-aware order
-  if (u >= args.num_units) return false;
-  int b = 0;
-  while (b + 1 < args.num_seqs && args.seqs[b + 1].unit0 <= u) ++b;
-  const SeqDesc& sd = args.seqs[b];
-  const int v = u - sd.unit0;
-  const int per_chunk = sd.T * sd.NRB;  // units sharing one KV chunk are consecutive
-  us.s = v / per_chunk;
-  us.t = (v % per_chunk) / sd.NRB;
-  const int rb = v % sd.NRB;
-  us.R = sd.R;
-  us.H = args.H;
-  us.S = sd.S;
-  us.part_row0 = sd.part_row0;
-  us.scale_log2 = args.scale_log2;
-  us.o_scale = args.o_scale;
-  us.q = args.q;
-  us.o = args.o;
-  us.lse = args.lse;
-  us.part_lse = args.part_lse;
-  us.part_o = args.part_o;
-  us.rowb0 = rb * sd.RBS;                          // first tile row of this unit
-  us.RU = min(sd.RBS, us.R - us.rowb0);            // rows of this unit
-  us.row0 = sd.q_row0 + us.t * us.R + us.rowb0;    // first Q/O row of this unit
-  us.uc.lo = us.s * sd.L;
-  const int hi = min(us.uc.lo + sd.L, sd.n);
-  us.tail0 = sd.ce - sd.qlen + us.t * sd.F;        // tile row r sees keys <= tail0 + r / H
-  const int vis_lo = us.tail0 + us.rowb0 / us.H;   // every unit row sees keys <= vis_lo
-  const int vis_hi = us.tail0 + (us.rowb0 + us.RU - 1) / us.H;
-  us.hi_eff = min(hi, vis_hi + 1);                 // no unit row sees keys >= hi_eff
-  us.uc.nkeys = us.hi_eff - us.uc.lo;              // may be <= 0 (chunk hidden from every row)
-  us.uc.ntiles = us.uc.nkeys > 0 ? (us.uc.nkeys + kTK - 1) / kTK : 0;
-  us.uc.min_lim = min(us.hi_eff - 1, vis_lo) - us.uc.lo;  // every row sees keys <= this
-  if (args.page_table == nullptr) {
-    us.pt_row = nullptr;
-    us.kv_unit = args.kv + ((int64_t)sd.kv_row0 + us.uc.lo) * Stage<FP8>::kGlobalRowBytes;
-  } else {
-    us.pt_row = args.page_table + (int64_t)b * args.pt_stride;
-    us.kv_unit = args.kv;
-    us.page_shift = args.page_shift;
-    us.last_page_idx = (sd.n - 1) >> args.page_shift;
-    us.num_pages = args.num_pages;
-  }
-  return true;
-}
 
 template <bool FP8, bool PAGED>
 __device__ __forceinline__ KvSource<FP8, PAGED> kv_source(const UnitSetup& us) {
@@ -1774,7 +1615,7 @@ __device__ __forceinline__ void total_row_sums(float* xs, int wave, float (&l_ru
 template <bool FP8, int NRT, int DH, bool PAGED>
 __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* smem) {
   UnitSetup us;
-  if (!unit_setup<FP8>(args, us)) return;
+  if (!unit_setup<Stage<FP8>::kGlobalRowBytes, kTK>(args, us)) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;

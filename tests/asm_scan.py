@@ -12,21 +12,29 @@ inline assembly nor knows that an inline-assembly load completes later, so:
   loop that issues staged loads, nor between a prologue's loads and its loop
   (the copy would read it before the data arrives);
 * the tile loop must not move MFMA accumulators or operands between register
-  files (v_accvgpr_*), which is what keeps the loop short.
+  files (v_accvgpr_*), which is what keeps the loop short;
+* a transcendental result (v_exp_f32 and the like) must not be read by the
+  very next instruction (one wait state), a hazard the compiler pads only in
+  front of its own instructions;
+* in the fp8 kernel, whose MFMA accumulators live in AGPRs named by its
+  inline assembly, the compiler must not place anything in an AGPR.
 """
 from __future__ import annotations
 
 import re
 
 MAIN_KERNEL = re.compile(r"^(_Z\S*mla_decode_main\S*):", re.M)
+FP8_KERNEL = re.compile(r"^(_Z\S*mla_decode_fp8\S*):", re.M)
+TRANS_OP = re.compile(r"^v_(exp|log|rcp|rcp_iflag|rsq|sqrt|sin|cos)(_legacy)?_f(16|32)")
 STAGED_LOAD = re.compile(r"buffer_load_dwordx[24] (v\S+?),? v\d+, s\[\d+:\d+\], s\d+ offen")
 
 
-def kernels(asm: str) -> dict:
-    """Main-kernel name -> list of its assembly lines (the body and the
-    compiler's resource summary comments that follow it)."""
+def kernels(asm: str, pattern=MAIN_KERNEL) -> dict:
+    """Kernel name -> list of its assembly lines (the body and the compiler's
+    resource summary comments that follow it), for the kernels whose symbol
+    matches `pattern`."""
     out = {}
-    for m in MAIN_KERNEL.finditer(asm):
+    for m in pattern.finditer(asm):
         end = asm.find(".Lfunc_end", m.end())
         stats = asm.find("; Occupancy:", end)
         out[m.group(1)] = asm[m.end():stats if stats >= 0 else end].split("\n")
@@ -201,3 +209,38 @@ def staged_loads_in_loops(lines) -> int:
 def accvgpr_moves_in_loops(lines) -> list:
     return [f"{lab}: {lines[k].strip()}" for lab, idx in tile_loops(lines).items()
             for k in idx if "v_accvgpr_" in lines[k]]
+
+
+def trans_hazards(lines) -> list:
+    """Transcendental results read by the instruction right after them."""
+    ins = _instructions(lines)
+    found = []
+    for i in range(len(ins) - 1):
+        op, ops = ins[i]
+        if not TRANS_OP.match(op) or not ops:
+            continue
+        nop, nops = ins[i + 1]
+        if nop == "LABEL" or not nop.startswith("v_") or len(nops) < 2:
+            continue
+        if set().union(*[regs(o) for o in nops[1:]]) & regs(ops[0]):
+            found.append(f"{op} {ops[0]} -> {nop} {','.join(nops)}")
+    return found
+
+
+def compiler_agprs(lines) -> list:
+    """AGPRs named outside inline-assembly blocks (the compiler's own use)."""
+    found = []
+    inasm = False
+    for line in lines:
+        t = line.strip()
+        if ";;#ASMSTART" in t:
+            inasm = True
+            continue
+        if ";;#ASMEND" in t:
+            inasm = False
+            continue
+        if inasm or not t or t.startswith(";") or t.startswith("."):
+            continue
+        if any(kind == "a" for kind, _ in regs(t.split(";")[0])):
+            found.append(t)
+    return found

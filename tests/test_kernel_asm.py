@@ -1,7 +1,8 @@
-"""CPU checks of the main kernel's gfx950 assembly (hipcc cross-compiles it
-here with the library's own flags): hazards around the inline-assembly
-MFMAs, no copies of registers that staged loads are filling, and no
-register-file moves inside the KV tile loop."""
+"""CPU checks of the decode kernels' gfx950 assembly (hipcc cross-compiles
+them here with the library's own flags): hazards around the inline-assembly
+MFMAs and transcendental results, no copies of registers that staged loads
+are filling, no register-file moves inside the bf16 KV tile loop, and no
+compiler use of the AGPRs that the fp8 kernel allocates by hand."""
 import os
 import shutil
 import subprocess
@@ -15,23 +16,43 @@ HIPCC = hipbuild.HIPCC
 
 
 @pytest.fixture(scope="module")
-def kernels(tmp_path_factory):
+def assembly(tmp_path_factory):
+    """Source name -> its gfx950 assembly text (all four compiled in parallel)."""
     if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
         pytest.skip("hipcc not available")
     tmp = tmp_path_factory.mktemp("asm")
     procs = []
-    for name in ("kernels", "kernels_paged"):  # contiguous and paged KV, compiled in parallel
+    for name in ("kernels", "kernels_paged", "fp8_decode", "fp8_decode_paged"):
         out = tmp / f"{name}.s"
         src = os.path.join(hipbuild.CSRC, f"{name}.hip")
         cmd = [HIPCC, *hipbuild.compile_flags(), "-S", "--cuda-device-only", "-o", str(out), src]
-        procs.append((out, subprocess.Popen(cmd)))
-    ks = {}
-    for out, p in procs:
+        procs.append((name, out, subprocess.Popen(cmd)))
+    texts = {}
+    for name, out, p in procs:
         assert p.wait() == 0
-        part = asm_scan.kernels(out.read_text())
+        texts[name] = out.read_text()
+    return texts
+
+
+@pytest.fixture(scope="module")
+def kernels(assembly):
+    ks = {}
+    for name in ("kernels", "kernels_paged"):  # contiguous and paged KV
+        part = asm_scan.kernels(assembly[name])
         assert len(part) == 6, sorted(part)  # {bf16, fp8} x {16, 32, 48 rows per row group}
         ks.update(part)
     assert len(ks) == 12, sorted(ks)
+    return ks
+
+
+@pytest.fixture(scope="module")
+def fp8_kernels(assembly):
+    ks = {}
+    for name in ("fp8_decode", "fp8_decode_paged"):
+        part = asm_scan.kernels(assembly[name], asm_scan.FP8_KERNEL)
+        assert len(part) == 3, sorted(part)  # 32, 64, 96 rows per unit
+        ks.update(part)
+    assert len(ks) == 6, sorted(ks)
     return ks
 
 
@@ -43,6 +64,24 @@ def test_main_kernels_use_no_scratch(kernels):
 
 def test_no_unpadded_mfma_hazards(kernels):
     for name, lines in kernels.items():
+        assert asm_scan.mfma_hazards(lines) == [], name
+
+
+def test_no_unpadded_transcendental_reads(kernels, fp8_kernels):
+    for name, lines in {**kernels, **fp8_kernels}.items():
+        assert asm_scan.trans_hazards(lines) == [], name
+
+
+def test_fp8_kernels_use_no_scratch_and_leave_agprs_to_the_asm(fp8_kernels):
+    """The fp8 kernel keeps O and part of Q in AGPRs that its inline assembly
+    names; anything the compiler put there would be overwritten."""
+    for name, lines in fp8_kernels.items():
+        assert asm_scan.scratch_bytes(lines) == 0, name
+        assert asm_scan.compiler_agprs(lines) == [], name
+
+
+def test_fp8_kernels_pad_mfma_hazards(fp8_kernels):
+    for name, lines in fp8_kernels.items():
         assert asm_scan.mfma_hazards(lines) == [], name
 
 
@@ -77,3 +116,20 @@ def test_scan_detects_a_planted_staged_copy():
     # the register was redefined (reused for another value) before the copy: no flag
     reused = loop[:3] + ["\tv_add_f32_e32 v10, v2, v3"] + loop[3:]
     assert asm_scan.staged_copies_in_loops(reused) == []
+
+
+def test_scan_detects_a_planted_transcendental_read():
+    planted = ["\tv_exp_f32_e32 v59, v59",
+               ";;#ASMSTART",
+               "\tv_max_f32 v105, v58, v59",
+               ";;#ASMEND",
+               "\tv_exp_f32_e32 v60, v60",
+               "\ts_nop 0",
+               "\tv_max_f32 v106, v58, v60"]
+    assert len(asm_scan.trans_hazards(planted)) == 1
+
+
+def test_scan_detects_a_compiler_agpr():
+    lines = [";;#ASMSTART", "\tv_accvgpr_write_b32 a3, v1", ";;#ASMEND",
+             "\tv_accvgpr_read_b32 v2, a4"]
+    assert asm_scan.compiler_agprs(lines) == ["v_accvgpr_read_b32 v2, a4"]
