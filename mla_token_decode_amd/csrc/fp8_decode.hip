@@ -154,27 +154,41 @@ __device__ __forceinline__ DmaLanes dma_lanes(int tid) {
   return d;
 }
 
-// Issue the 9 loads of tile t into `slot` (tiles past the chunk load nothing
-// but still count).  e: page-table entries of the tile's halves (paged).
+// The 9 loads of tile t into `slot` (tiles past the chunk load nothing but
+// still count): issue<k>() issues load k, so that the loop can spread them
+// between its MFMAs.  e: page-table entries of the tile's halves (paged).
+template <bool PAGED>
+struct TileLoads {
+  const uint8_t* hb[2];
+  int hr[2];
+  lds_u8* slot;
+  __device__ __forceinline__ TileLoads(const Src<PAGED>& src, int t, const int (&e)[2],
+                                       lds_u8* slot_)
+      : hb{src.half_base(t, 0, e[0]), src.half_base(t, 1, e[1])},
+        hr{src.half_rows(t, 0), src.half_rows(t, 1)},
+        slot(slot_) {}
+  template <int K>
+  __device__ __forceinline__ void issue(const DmaLanes& dl, int wave) const {
+    if constexpr (K < 8) {
+      constexpr int h = K >> 2, sub = K & 3;  // keys 8 sub .. 8 sub + 7 of half h
+      const int rows = __builtin_amdgcn_readfirstlane(max(0, hr[h] - 8 * sub));
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc(uniform_ptr(hb[h] + 8 * sub * kRowB), (uint32_t)(rows * kRowB));
+      dma16(slot + 4096 * K + 1024 * wave, dl.lat, r);
+    } else {
+      const bool h1 = wave >= 2;  // rope keys of this wave: 16 wave .. 16 wave + 15
+      const int rows = __builtin_amdgcn_readfirstlane(h1 ? hr[1] : hr[0]);
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc(uniform_ptr(h1 ? hb[1] : hb[0]), (uint32_t)(rows * kRowB));
+      dma16(slot + kRopeOff + 1024 * wave, dl.rope, r);
+    }
+  }
+};
 template <bool PAGED>
 __device__ __forceinline__ void issue_tile(const Src<PAGED>& src, int t, const int (&e)[2],
                                            lds_u8* slot, const DmaLanes& dl, int wave) {
-  const uint8_t* hb[2] = {src.half_base(t, 0, e[0]), src.half_base(t, 1, e[1])};
-  const int hr[2] = {src.half_rows(t, 0), src.half_rows(t, 1)};
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int h = k >> 2, sub = k & 3;  // keys 8 sub .. 8 sub + 7 of half h
-    const int rows = __builtin_amdgcn_readfirstlane(max(0, hr[h] - 8 * sub));
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(uniform_ptr(hb[h] + 8 * sub * kRowB), (uint32_t)(rows * kRowB));
-    dma16(slot + 4096 * k + 1024 * wave, dl.lat, r);
-  }
-  {
-    const int h = wave >> 1;  // rope keys of this wave: 16 wave .. 16 wave + 15
-    const int rows = __builtin_amdgcn_readfirstlane(hr[h]);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform_ptr(hb[h]), (uint32_t)(rows * kRowB));
-    dma16(slot + kRopeOff + 1024 * wave, dl.rope, r);
-  }
+  const TileLoads<PAGED> tl(src, t, e, slot);
+  static_for<9>([&](auto kc) { tl.template issue<decltype(kc)::value>(dl, wave); });
 }
 
 template <int N>
@@ -393,26 +407,27 @@ struct Soft {
 };
 
 // P of score block (kb, rb) of a tile, in two halves (keys 4 g + 0, 1, then
-// 4 g + 2, 3 of the lane's row): the first masks the block in place on the
-// chunk's last tiles (keys past the row's causal limit get -inf), then
+// 4 g + 2, 3 of the lane's row): on the chunk's last tiles (EDGE) the first
+// masks the block in place (keys past the row's causal limit get -inf), then
 // P = 2^(c s - m) (v_exp_f32 flushes results below the fp32 normal range to
 // 0), packed to e4m3 (keys 4 g .. 4 g + 3 -> bytes 0..3 of one dword) and
 // stored into the P buffer by the second half, which also adds the block's
-// row sum to ps and raises `flag` when an exponent c s - m passes kLazy (a P
-// value above 2^8).  The flag looks at the exponents, not at P: a v_exp_f32
-// result needs one wait state before a dependent VALU read, which the
-// compiler does not pad in front of inline assembly such as max2/max3.
+// row sum to ps.  xrun keeps the largest exponent c s - m the lane has met in
+// the tile; the reference must move when it passes kLazy (a P value above
+// 2^8).  It looks at the exponents, not at P: a v_exp_f32 result needs one
+// wait state before a dependent VALU read, which the compiler does not pad in
+// front of inline assembly such as max3.
 struct HalfTmp {
   int pk;
   float sum, xmax;
 };
-template <int N, int KB, int RB, int HALF>
-__device__ __forceinline__ void softmax_half(f32x4 (&S)[2][N], Soft<N>& sm, int k0, bool edge,
+template <int N, int KB, int RB, int HALF, bool EDGE>
+__device__ __forceinline__ void softmax_half(f32x4 (&S)[2][N], Soft<N>& sm, int k0,
                                              lds_u8* pbuf, const PBase& pb, HalfTmp& ht,
-                                             bool& flag) {
+                                             float& xrun) {
   f32x4& s = S[KB][RB];
   if constexpr (HALF == 0) {
-    if (edge) {
+    if constexpr (EDGE) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[i] = k0 + 16 * KB + i <= sm.lim[RB] ? s[i] : -INFINITY;
     }
@@ -422,7 +437,7 @@ __device__ __forceinline__ void softmax_half(f32x4 (&S)[2][N], Soft<N>& sm, int 
     const float p1 = __builtin_amdgcn_exp2f(x1);
     ht.pk = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __builtin_bit_cast(int, p0), false);
     ht.sum = p0 + p1;
-    ht.xmax = max2(x0, x1);
+    ht.xmax = max3(xrun, x0, x1);
   } else {
     const float x2 = __builtin_fmaf(s[2], sm.c[RB], sm.nmu[RB]);
     const float x3 = __builtin_fmaf(s[3], sm.c[RB], sm.nmu[RB]);
@@ -430,24 +445,32 @@ __device__ __forceinline__ void softmax_half(f32x4 (&S)[2][N], Soft<N>& sm, int 
     const float p3 = __builtin_amdgcn_exp2f(x3);
     const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, ht.pk, true);
     sm.ps[RB] += ht.sum + (p2 + p3);
-    flag = flag || max3(ht.xmax, x2, x3) > kLazy;
+    xrun = max3(ht.xmax, x2, x3);
     *(int*)(pbuf + pb.wr[KB] + 1024 * RB) = pk;
   }
 }
 
 // The whole softmax of a tile (rare path).
-template <int N>
-__device__ __forceinline__ void softmax_tile(f32x4 (&S)[2][N], Soft<N>& sm, int k0, bool edge,
-                                             lds_u8* pbuf, const PBase& pb) {
+template <int N, bool EDGE>
+__device__ __forceinline__ void softmax_tile_as(f32x4 (&S)[2][N], Soft<N>& sm, int k0,
+                                                lds_u8* pbuf, const PBase& pb) {
 #pragma unroll
   for (int rb = 0; rb < N; ++rb) sm.ps[rb] = 0.0f;
-  bool flag = false;
+  float xrun = -INFINITY;
   static_for<2 * N>([&](auto bc) {
     constexpr int kb = decltype(bc)::value % 2, rb = decltype(bc)::value / 2;
     HalfTmp ht;
-    softmax_half<N, kb, rb, 0>(S, sm, k0, edge, pbuf, pb, ht, flag);
-    softmax_half<N, kb, rb, 1>(S, sm, k0, edge, pbuf, pb, ht, flag);
+    softmax_half<N, kb, rb, 0, EDGE>(S, sm, k0, pbuf, pb, ht, xrun);
+    softmax_half<N, kb, rb, 1, EDGE>(S, sm, k0, pbuf, pb, ht, xrun);
   });
+}
+template <int N>
+__device__ __forceinline__ void softmax_tile(f32x4 (&S)[2][N], Soft<N>& sm, int k0, bool edge,
+                                             lds_u8* pbuf, const PBase& pb) {
+  if (edge)
+    softmax_tile_as<N, true>(S, sm, k0, pbuf, pb);
+  else
+    softmax_tile_as<N, false>(S, sm, k0, pbuf, pb);
 }
 
 // Rare path for tile t (its scores S still in registers): the references of
@@ -588,15 +611,14 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
     });
   };
   // Scores of tile t (slot t % 4) into S, K fragments one step ahead of their
-  // MFMAs.  N >= 2: key block 0 first (N independent accumulators per step),
-  // and after(i) runs after each of key block 1's 5 steps (the softmax of
-  // key block 0 goes there); N = 1: the two key blocks alternate (their
-  // accumulators are the independent MFMAs between dependent ones).
-  auto scores = [&](int t, auto&& after) {
+  // MFMAs; hook(st) runs after the MFMAs of step st (0..9).  N >= 2: key
+  // block 0 first (N independent accumulators per step), so that the softmax
+  // of key block 0 can run under the MFMAs of key block 1 (steps 5..9); N = 1:
+  // the two key blocks alternate (their accumulators are the independent
+  // MFMAs between dependent ones).
+  constexpr bool kMajor = N >= 2;
+  auto scores = [&](int t, auto&& hook) {
     const lds_u8* slot = lds + (t % kSlots) * kTileB;
-    constexpr bool kMajor = N >= 2;
-    auto step_kb = [](int st) { return kMajor ? st / 5 : st % 2; };
-    auto step_db = [](int st) { return kMajor ? st % 5 : st / 2; };
     i32x8 kf[2];
     kf[0] = read_k<0, 0>(slot, kb_);
     static_for<10>([&](auto sc) {
@@ -608,11 +630,9 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
       qk_step(std::integral_constant<int, kb>{}, std::integral_constant<int, db>{}, kf[st % 2]);
       if constexpr (kMajor && st == 4)
         asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // key block 0 retired before its softmax
-      if constexpr (kMajor && st >= 5) after(std::integral_constant<int, st - 5>{});
+      hook(sc);
       __builtin_amdgcn_sched_barrier(0);
     });
-    (void)step_kb;
-    (void)step_db;
     asm volatile("s_nop 15\n\ts_nop 3" ::: "memory");  // score MFMAs retired before VALU reads
   };
 
@@ -626,7 +646,12 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
     if (lane == 0) *(lds_u32*)(lds + kFlagOff + 4 * wave) = 1u;
   }
 
-  for (int t = 0; t < T; ++t) {
+  // Iteration t: PV of tile t; with MORE (t + 1 < T) also the scores and P of
+  // tile t + 1, masked when EDGE (tile t + 1 reaches past the smallest causal
+  // limit of the unit's rows), and the 9 loads of tile t + 3.  Each variant is
+  // straight-line code: no branch inside the MFMA stream.
+  auto iteration = [&](int t, auto edge_c, auto more_c) {
+    constexpr bool EDGE = decltype(edge_c)::value, MORE = decltype(more_c)::value;
     // tile t + 1 landed (tile t + 2 may still be in flight); the barrier
     // publishes it, P(t) and the flags of tile t
     wait_tiles_behind<9>();
@@ -634,8 +659,8 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
     barrier_fetch(src, t + 3, e);
     lds_u8* pbuf_t = pbuf0 + (t & 1) * kPBuf;
     const u32x4 fl = *(const lds_u32x4*)(lds + kFlagOff + (t & 1) * 16);
-    // tile t + 3 into the slot of tile t - 1 (read by the PV of the last iteration)
-    issue_tile(src, t + 3, e, lds + ((t + 3) % kSlots) * kTileB, dl, wave);
+    // tile t + 3 goes into the slot of tile t - 1 (read by the last PV)
+    const TileLoads<PAGED> tl(src, t + 3, e, lds + ((t + 3) % kSlots) * kTileB);
     if (__builtin_amdgcn_readfirstlane((fl[0] | fl[1]) | (fl[2] | fl[3])) != 0) {
       move_references<N>(S, sm, kKeys * t + 32 * kh + 4 * g, kKeys * t + kKeys - 1 > us.uc.min_lim,
                          lds, pbuf_t, pb, kh, rh, lane);
@@ -644,31 +669,33 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
       for (int rb = 0; rb < N; ++rb) sm.l[rb] += sm.ps[rb];
     }
 
-    const bool more = t + 1 < T;
     const lds_u8* slot_t = lds + (t % kSlots) * kTileB;
     const int kq = kKeys * (t + 1) + 32 * kh + 4 * g;  // lane's first key of tile t + 1
-    const bool edge1 = kKeys * (t + 1) + kKeys - 1 > us.uc.min_lim;
     lds_u8* pbuf_n = pbuf0 + ((t + 1) & 1) * kPBuf;
 #pragma unroll
     for (int rb = 0; rb < N; ++rb) sm.ps[rb] = 0.0f;
-    bool flag = false;
+    float xrun = -INFINITY;
     HalfTmp ht;
     // half-slice h of the softmax of tile t + 1 over key block KB: row block
     // h / 2, half h % 2
     auto soft_half = [&](auto kbc, auto hc) {
       constexpr int kb = decltype(kbc)::value, h = decltype(hc)::value;
-      softmax_half<N, kb, h / 2, h % 2>(S, sm, kq, edge1, pbuf_n, pb, ht, flag);
+      softmax_half<N, kb, h / 2, h % 2, EDGE>(S, sm, kq, pbuf_n, pb, ht, xrun);
     };
     // P(t) and the first V fragments are read ahead of the PV MFMAs
     i32x8 P[N];
     i32x8 V[2];
-    if (more) {
-      scores(t + 1, [&](auto ic) {  // key block 0's softmax under key block 1's MFMAs
-        constexpr int i = decltype(ic)::value;  // step 0..4 of key block 1
-        static_for<2 * N>([&](auto hc) {
-          constexpr int h = decltype(hc)::value;
-          if constexpr ((h * 5) / (2 * N) == i) soft_half(std::integral_constant<int, 0>{}, hc);
-        });
+    if constexpr (MORE) {
+      scores(t + 1, [&](auto sc) {
+        constexpr int st = decltype(sc)::value;
+        if constexpr (st < 9) tl.template issue<st>(dl, wave);  // load st of tile t + 3
+        if constexpr (kMajor && st >= 5) {  // key block 0's softmax under key block 1's MFMAs
+          constexpr int i = st - 5;
+          static_for<2 * N>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            if constexpr ((h * 5) / (2 * N) == i) soft_half(std::integral_constant<int, 0>{}, hc);
+          });
+        }
       });
     }
     static_for<N>([&](auto pc) {
@@ -687,7 +714,7 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
         constexpr int pbk = decltype(pc)::value;
         OAcc<cb * N + pbk>::pv(V[cb % 2], P[pbk]);
         constexpr int mi = cb * N + pbk;  // MFMA index 0 .. 4 N - 1
-        if (more) {
+        if constexpr (MORE) {
           static_for<kHalves>([&](auto hc) {
             constexpr int h = decltype(hc)::value;
             if constexpr ((h * 4 * N) / kHalves == mi) {
@@ -701,11 +728,22 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
         __builtin_amdgcn_sched_barrier(0);
       });
     });
-    if (more) {
-      const unsigned any = __builtin_amdgcn_ballot_w64(flag) != 0 ? 1u : 0u;
+    if constexpr (MORE) {
+      const unsigned any = __builtin_amdgcn_ballot_w64(xrun > kLazy) != 0 ? 1u : 0u;
       if (lane == 0) *(lds_u32*)(lds + kFlagOff + ((t + 1) & 1) * 16 + 4 * wave) = any;
     }
-  }
+  };
+
+  // first tile that reaches past the smallest causal limit of the unit's rows
+  const int min_lim = us.uc.min_lim;
+  const int e0 = min_lim >= kKeys - 1 ? (min_lim - (kKeys - 1)) / kKeys + 1 : 0;
+  const int t_plain = min(max(e0 - 1, 0), T - 1);
+  const std::integral_constant<bool, false> no;
+  const std::integral_constant<bool, true> yes;
+  int t = 0;
+  for (; t < t_plain; ++t) iteration(t, no, yes);
+  for (; t < T - 1; ++t) iteration(t, yes, yes);
+  if (T > 0) iteration(T - 1, no, no);  // the last tile's PV (its loads past the end are not issued)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads issued past the end
 
   // ---- epilogue: row sums, then O / l through LDS in full rows
