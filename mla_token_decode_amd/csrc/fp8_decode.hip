@@ -347,6 +347,47 @@ __device__ __forceinline__ void wait_q(QRaw& r) {
                  : "n"(N) : "memory");
 }
 
+// Raw bf16 Q of row blocks 1 .. N - 1 of both row halves (32 (N - 1) rows)
+// is copied into LDS slots 2 (and 3) by LDS DMA when a unit starts, so that
+// the tile loads issued after it need not land before those rows are
+// quantised.  LDS row lr holds unit row 16 N h + 16 + j (h = lr / (16 (N - 1)),
+// j = lr % (16 (N - 1))) as 72 16-byte chunks, chunk c at position
+// c ^ (lr & 7): the 8 lanes of one 16-byte read (8 rows, one chunk) then
+// meet 8 different bank groups.  Rows past the unit read as zero.
+constexpr int kQOff = 2 * kTileB;
+constexpr int kQChunks = 2 * kDqk / 16;  // 72 chunks of one bf16 row
+template <int N>
+constexpr int q_dma_loads() { return 9 * (N - 1); }  // per wave: 36 (N - 1) KB in all
+static_assert(kQOff + 4 * q_dma_loads<3>() * 1024 <= kPOff, "Q rows fit slots 2 and 3");
+template <int N>
+__device__ __forceinline__ void q_to_lds(__amdgpu_buffer_rsrc_t qr, lds_u8* lds, int wave,
+                                         int lane) {
+  constexpr int kRowsHalf = 16 * (N - 1);
+#pragma unroll
+  for (int j = 0; j < q_dma_loads<N>(); ++j) {
+    const int J = 4 * j + wave;      // 1 KB block of the LDS rows
+    const int C = 64 * J + lane;     // the lane's chunk position
+    const int lr = C / kQChunks, cl = C - lr * kQChunks;
+    const int h = lr >= kRowsHalf ? 1 : 0;
+    const int urow = 16 * N * h + 16 + (lr - h * kRowsHalf);
+    dma16(lds + kQOff + 1024 * J, urow * (2 * kDqk) + 16 * (cl ^ (lr & 7)), qr);
+  }
+}
+// Row block RB (>= 1) of row half rh from the LDS rows into the QRaw layout.
+template <int N, int RB>
+__device__ __forceinline__ void q_from_lds(QRaw& r, const lds_u8* lds, int rh, int l16, int g) {
+  const int lr = 16 * (N - 1) * rh + 16 * (RB - 1) + l16;
+  const lds_u8* row = lds + kQOff + lr * (2 * kDqk);
+  const int x = lr & 7;
+#pragma unroll
+  for (int db = 0; db < 5; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = db < 4 ? 16 * db + 4 * g + i : 64 + 4 * (g & 1) + i;
+      r.v[db][i] = *(const u32x4*)(row + 16 * (c ^ x));
+    }
+}
+
 // Quantise one row block to e4m3: the row's scale s = max |q| / 448 over all
 // 576 columns (one shared scale: the rope and latent parts feed one
 // accumulator), bounded below (q8_inv_scale); c = scale_log2 * s.
@@ -568,25 +609,36 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
     sm.l[rb] = 0.0f;
     sm.ps[rb] = 0.0f;
   });
+  // Q of row block 0 into registers and (N >= 2) the other row blocks into
+  // LDS slots 2..3, then tiles 0 and 1 start streaming while Q is quantised;
+  // tile 2 follows once slot 2 is free again.
   {
     QRaw raw;
     load_q_raw(raw, qr, q_row(0), g);
+    if constexpr (N >= 2) q_to_lds<N>(qr, lds, wave, lane);
     int e[2];
+    constexpr int kEarly = N == 1 ? 3 : 2;  // tiles issued before the quantisation
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
+    for (int k = 0; k < kEarly; ++k) {
       fetch_now(src, k, e);
       issue_tile(src, k, e, lds + k * kTileB, dl, wave);
     }
-    wait_q<27>(raw);
+    wait_q<q_dma_loads<N>() + 9 * kEarly>(raw);
     quantise_q<N, 0>(us, raw, g, qf, sm.c[0]);
     __builtin_amdgcn_sched_barrier(0);
-    static_for<N - 1>([&](auto rc) {
-      constexpr int rb = decltype(rc)::value + 1;
-      load_q_raw(raw, qr, q_row(rb), g);
-      wait_q<0>(raw);
-      quantise_q<N, rb>(us, raw, g, qf, sm.c[rb]);
-      __builtin_amdgcn_sched_barrier(0);
-    });
+    if constexpr (N >= 2) {
+      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // this wave's Q rows landed
+      lds_barrier();                                      // and every other wave's
+      static_for<N - 1>([&](auto rc) {
+        constexpr int rb = decltype(rc)::value + 1;
+        q_from_lds<N, rb>(raw, lds, rh, l16, g);
+        quantise_q<N, rb>(us, raw, g, qf, sm.c[rb]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      lds_barrier();  // the Q rows are read before tile 2 overwrites slot 2
+      fetch_now(src, 2, e);
+      issue_tile(src, 2, e, lds + 2 * kTileB, dl, wave);
+    }
   }
   {
     const i32x8 z = {};
