@@ -663,16 +663,17 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
     });
   };
   // Scores of tile t (slot t % 4) into S, K fragments one step ahead of their
-  // MFMAs; hook(st) runs after the MFMAs of step st (0..9).  N >= 2: key
+  // MFMAs (the first one, k0, read by the caller); hook(st) runs after the
+  // MFMAs of step st (0..9).  N >= 2: key
   // block 0 first (N independent accumulators per step), so that the softmax
   // of key block 0 can run under the MFMAs of key block 1 (steps 5..9); N = 1:
   // the two key blocks alternate (their accumulators are the independent
   // MFMAs between dependent ones).
   constexpr bool kMajor = N >= 2;
-  auto scores = [&](int t, auto&& hook) {
+  auto scores = [&](int t, const i32x8& k0, auto&& hook) {
     const lds_u8* slot = lds + (t % kSlots) * kTileB;
     i32x8 kf[2];
-    kf[0] = read_k<0, 0>(slot, kb_);
+    kf[0] = k0;
     static_for<10>([&](auto sc) {
       constexpr int st = decltype(sc)::value;
       constexpr int kb = kMajor ? st / 5 : st % 2, db = kMajor ? st % 5 : st / 2;
@@ -693,7 +694,7 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
   if (T > 0) {
     wait_tiles_behind<18>();  // tile 0 landed (tiles 1 and 2 may still be in flight)
     lds_barrier();
-    scores(0, [](auto) {});
+    scores(0, read_k<0, 0>(lds, kb_), [](auto) {});
     // tile 0 sets the references: its flags force the rare path in the loop
     if (lane == 0) *(lds_u32*)(lds + kFlagOff + 4 * wave) = 1u;
   }
@@ -711,6 +712,10 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
     barrier_fetch(src, t + 3, e);
     lds_u8* pbuf_t = pbuf0 + (t & 1) * kPBuf;
     const u32x4 fl = *(const lds_u32x4*)(lds + kFlagOff + (t & 1) * 16);
+    // the first K fragment of tile t + 1 is read together with the flags
+    // (its LDS latency overlaps theirs; the rare path leaves it alone)
+    i32x8 k0;
+    if constexpr (MORE) k0 = read_k<0, 0>(lds + ((t + 1) % kSlots) * kTileB, kb_);
     // tile t + 3 goes into the slot of tile t - 1 (read by the last PV)
     const TileLoads<PAGED> tl(src, t + 3, e, lds + ((t + 3) % kSlots) * kTileB);
     if (__builtin_amdgcn_readfirstlane((fl[0] | fl[1]) | (fl[2] | fl[3])) != 0) {
@@ -738,7 +743,7 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
     i32x8 P[N];
     i32x8 V[2];
     if constexpr (MORE) {
-      scores(t + 1, [&](auto sc) {
+      scores(t + 1, k0, [&](auto sc) {
         constexpr int st = decltype(sc)::value;
         if constexpr (st < 9) tl.template issue<st>(dl, wave);  // load st of tile t + 3
         if constexpr (kMajor && st >= 5) {  // key block 0's softmax under key block 1's MFMAs
