@@ -144,43 +144,43 @@ __device__ __forceinline__ void dma16(const lds_u8* dst, int voff, __amdgpu_buff
 // physical chunk tid % 32 = logical chunk ^ (key & 7) (the XOR is an
 // involution; key & 7 = tid / 32).  Load 8 fills rope chunk tid: key tid / 4,
 // physical chunk tid % 4 = logical ^ ((key >> 1) & 3).
+// lat[sub]: offset of load k (sub = k % 4) from the base of its 32-key half.
 struct DmaLanes {
-  int lat, rope;
+  int lat[4], rope;
 };
 __device__ __forceinline__ DmaLanes dma_lanes(int tid) {
   DmaLanes d;
-  d.lat = (tid >> 5) * kRowB + 16 * ((tid & 31) ^ (tid >> 5));
+  const int lat = (tid >> 5) * kRowB + 16 * ((tid & 31) ^ (tid >> 5));
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub) d.lat[sub] = lat + 8 * sub * kRowB;
   d.rope = ((tid >> 2) & 31) * kRowB + kLatB + 16 * ((tid & 3) ^ ((tid >> 3) & 3));
   return d;
 }
 
 // The 9 loads of tile t into `slot` (tiles past the chunk load nothing but
 // still count): issue<k>() issues load k, so that the loop can spread them
-// between its MFMAs.  e: page-table entries of the tile's halves (paged).
+// between its MFMAs.  One descriptor per 32-key half, its range the half's
+// rows in the chunk (the range check on the lane offsets zero-fills the
+// rest).  e: page-table entries of the tile's halves (paged).
 template <bool PAGED>
 struct TileLoads {
-  const uint8_t* hb[2];
-  int hr[2];
+  __amdgpu_buffer_rsrc_t r[2];
   lds_u8* slot;
   __device__ __forceinline__ TileLoads(const Src<PAGED>& src, int t, const int (&e)[2],
                                        lds_u8* slot_)
-      : hb{src.half_base(t, 0, e[0]), src.half_base(t, 1, e[1])},
-        hr{src.half_rows(t, 0), src.half_rows(t, 1)},
-        slot(slot_) {}
+      : slot(slot_) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rows = __builtin_amdgcn_readfirstlane(src.half_rows(t, h));
+      r[h] = make_rsrc(uniform_ptr(src.half_base(t, h, e[h])), (uint32_t)(rows * kRowB));
+    }
+  }
   template <int K>
   __device__ __forceinline__ void issue(const DmaLanes& dl, int wave) const {
-    if constexpr (K < 8) {
-      constexpr int h = K >> 2, sub = K & 3;  // keys 8 sub .. 8 sub + 7 of half h
-      const int rows = __builtin_amdgcn_readfirstlane(max(0, hr[h] - 8 * sub));
-      const __amdgpu_buffer_rsrc_t r =
-          make_rsrc(uniform_ptr(hb[h] + 8 * sub * kRowB), (uint32_t)(rows * kRowB));
-      dma16(slot + 4096 * K + 1024 * wave, dl.lat, r);
-    } else {
-      const bool h1 = wave >= 2;  // rope keys of this wave: 16 wave .. 16 wave + 15
-      const int rows = __builtin_amdgcn_readfirstlane(h1 ? hr[1] : hr[0]);
-      const __amdgpu_buffer_rsrc_t r =
-          make_rsrc(uniform_ptr(h1 ? hb[1] : hb[0]), (uint32_t)(rows * kRowB));
-      dma16(slot + kRopeOff + 1024 * wave, dl.rope, r);
+    if constexpr (K < 8) {  // keys 8 (K % 4) .. + 7 of half K / 4
+      dma16(slot + 4096 * K + 1024 * wave, dl.lat[K & 3], r[K >> 2]);
+    } else {  // rope keys of this wave: 16 wave .. 16 wave + 15
+      dma16(slot + kRopeOff + 1024 * wave, dl.rope, wave >= 2 ? r[1] : r[0]);
     }
   }
 };
@@ -453,40 +453,33 @@ struct Soft {
 // P = 2^(c s - m) (v_exp_f32 flushes results below the fp32 normal range to
 // 0), packed to e4m3 (keys 4 g .. 4 g + 3 -> bytes 0..3 of one dword) and
 // stored into the P buffer by the second half, which also adds the block's
-// row sum to ps.  xrun keeps the largest exponent c s - m the lane has met in
-// the tile; the reference must move when it passes kLazy (a P value above
-// 2^8).  It looks at the exponents, not at P: a v_exp_f32 result needs one
-// wait state before a dependent VALU read, which the compiler does not pad in
-// front of inline assembly such as max3.
+// row sum to ps.  The reference must move when a P value passes 2^8 (a score
+// more than kLazy octaves above it); as P >= 0, every P of a row is at most
+// the lane's row sum ps, so the loop tests ps > 2^8 instead of every P (a
+// rare false alarm only sends the tile down the rare path, which finds no
+// reference to move and forms the same P again).
 struct HalfTmp {
   int pk;
-  float sum, xmax;
+  float sum;
 };
 template <int N, int KB, int RB, int HALF, bool EDGE>
 __device__ __forceinline__ void softmax_half(f32x4 (&S)[2][N], Soft<N>& sm, int k0,
-                                             lds_u8* pbuf, const PBase& pb, HalfTmp& ht,
-                                             float& xrun) {
+                                             lds_u8* pbuf, const PBase& pb, HalfTmp& ht) {
   f32x4& s = S[KB][RB];
   if constexpr (HALF == 0) {
     if constexpr (EDGE) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[i] = k0 + 16 * KB + i <= sm.lim[RB] ? s[i] : -INFINITY;
     }
-    const float x0 = __builtin_fmaf(s[0], sm.c[RB], sm.nmu[RB]);
-    const float x1 = __builtin_fmaf(s[1], sm.c[RB], sm.nmu[RB]);
-    const float p0 = __builtin_amdgcn_exp2f(x0);
-    const float p1 = __builtin_amdgcn_exp2f(x1);
-    ht.pk = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __builtin_bit_cast(int, p0), false);
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0], sm.c[RB], sm.nmu[RB]));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[1], sm.c[RB], sm.nmu[RB]));
     ht.sum = p0 + p1;
-    ht.xmax = max3(xrun, x0, x1);
+    ht.pk = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __builtin_bit_cast(int, p1), false);
   } else {
-    const float x2 = __builtin_fmaf(s[2], sm.c[RB], sm.nmu[RB]);
-    const float x3 = __builtin_fmaf(s[3], sm.c[RB], sm.nmu[RB]);
-    const float p2 = __builtin_amdgcn_exp2f(x2);
-    const float p3 = __builtin_amdgcn_exp2f(x3);
+    const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2], sm.c[RB], sm.nmu[RB]));
+    const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[3], sm.c[RB], sm.nmu[RB]));
     const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, ht.pk, true);
     sm.ps[RB] += ht.sum + (p2 + p3);
-    xrun = max3(ht.xmax, x2, x3);
     *(int*)(pbuf + pb.wr[KB] + 1024 * RB) = pk;
   }
 }
@@ -497,12 +490,11 @@ __device__ __forceinline__ void softmax_tile_as(f32x4 (&S)[2][N], Soft<N>& sm, i
                                                 lds_u8* pbuf, const PBase& pb) {
 #pragma unroll
   for (int rb = 0; rb < N; ++rb) sm.ps[rb] = 0.0f;
-  float xrun = -INFINITY;
   static_for<2 * N>([&](auto bc) {
     constexpr int kb = decltype(bc)::value % 2, rb = decltype(bc)::value / 2;
     HalfTmp ht;
-    softmax_half<N, kb, rb, 0, EDGE>(S, sm, k0, pbuf, pb, ht, xrun);
-    softmax_half<N, kb, rb, 1, EDGE>(S, sm, k0, pbuf, pb, ht, xrun);
+    softmax_half<N, kb, rb, 0, EDGE>(S, sm, k0, pbuf, pb, ht);
+    softmax_half<N, kb, rb, 1, EDGE>(S, sm, k0, pbuf, pb, ht);
   });
 }
 template <int N>
@@ -731,13 +723,12 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
     lds_u8* pbuf_n = pbuf0 + ((t + 1) & 1) * kPBuf;
 #pragma unroll
     for (int rb = 0; rb < N; ++rb) sm.ps[rb] = 0.0f;
-    float xrun = -INFINITY;
     HalfTmp ht;
     // half-slice h of the softmax of tile t + 1 over key block KB: row block
     // h / 2, half h % 2
     auto soft_half = [&](auto kbc, auto hc) {
       constexpr int kb = decltype(kbc)::value, h = decltype(hc)::value;
-      softmax_half<N, kb, h / 2, h % 2, EDGE>(S, sm, kq, pbuf_n, pb, ht, xrun);
+      softmax_half<N, kb, h / 2, h % 2, EDGE>(S, sm, kq, pbuf_n, pb, ht);
     };
     // P(t) and the first V fragments are read ahead of the PV MFMAs
     i32x8 P[N];
@@ -786,7 +777,10 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
       });
     });
     if constexpr (MORE) {
-      const unsigned any = __builtin_amdgcn_ballot_w64(xrun > kLazy) != 0 ? 1u : 0u;
+      float psmax = sm.ps[0];
+#pragma unroll
+      for (int rb = 1; rb < N; ++rb) psmax = fmaxf(psmax, sm.ps[rb]);
+      const unsigned any = __builtin_amdgcn_ballot_w64(psmax > 0x1p8f) != 0 ? 1u : 0u;
       if (lane == 0) *(lds_u32*)(lds + kFlagOff + ((t + 1) & 1) * 16 + 4 * wave) = any;
     }
   };
