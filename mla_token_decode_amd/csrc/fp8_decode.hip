@@ -388,9 +388,22 @@ __device__ __forceinline__ void q_from_lds(QRaw& r, const lds_u8* lds, int rh, i
     }
 }
 
-// Quantise one row block to e4m3: the row's scale s = max |q| / 448 over all
-// 576 columns (one shared scale: the rope and latent parts feed one
-// accumulator), bounded below (q8_inv_scale); c = scale_log2 * s.
+// Quantise one row block to e4m3: one scale per row over all 576 columns
+// (the rope and latent parts feed one accumulator), a power of two s = 2^k,
+// the smallest with max |q| / s <= 448 (so max |q| / s lies in (224, 448]
+// exactly), at least 2^-108 (a zero row, or one below 2^-100 in size, then
+// stays far inside e4m3 and gives a near-uniform softmax); c = scale_log2 * s.
+// With a power-of-two scale, gfx950's packed bf16 -> e4m3 conversion (which
+// divides by the power of two of its scale operand, round to nearest even)
+// quantises two columns per instruction.
+typedef short v2i16 __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float q8_pow2_scale(float M) {
+  const float r = M * (1.0f / kQ8Top);
+  float sc = __builtin_bit_cast(float, (__builtin_bit_cast(unsigned, r) + 0x007fffffu) & 0x7f800000u);
+  sc = M > kQ8Top * sc ? 2.0f * sc : sc;  // r rounded below M / 448 onto a power of two
+  return fmaxf(sc, 0x1p-108f);
+}
 template <int N, int RB>
 __device__ __forceinline__ void quantise_q(const UnitSetup& us, QRaw& raw, int g, QFrag<N>& qf,
                                            float& c) {
@@ -411,21 +424,18 @@ __device__ __forceinline__ void quantise_q(const UnitSetup& us, QRaw& raw, int g
         mb = __builtin_elementwise_max(mb, __builtin_bit_cast(u16x2, raw.v[db][i][w] & 0x7fff7fffu));
   const unsigned top = (unsigned)(mb[0] > mb[1] ? mb[0] : mb[1]) << 16;
   const float M = wave_max_across_groups(__builtin_bit_cast(float, top));
-  const float inv = q8_inv_scale(M);
-  c = us.scale_log2 / inv;
+  const float sc = q8_pow2_scale(M);
+  c = us.scale_log2 * sc;
   static_for<5>([&](auto dc) {
     constexpr int db = decltype(dc)::value;
     i32x8 v8;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {  // dword k: columns 4 k .. 4 k + 3 of the lane's 32
       const unsigned x0 = raw.v[db][k >> 1][2 * (k & 1)], x1 = raw.v[db][k >> 1][2 * (k & 1) + 1];
-      int v = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_bit_cast(float, x0 << 16) * inv,
-                                             __builtin_bit_cast(float, x0 & 0xffff0000u) * inv, 0,
-                                             false);
-      v = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_bit_cast(float, x1 << 16) * inv,
-                                         __builtin_bit_cast(float, x1 & 0xffff0000u) * inv, v,
-                                         true);
-      v8[k] = v;
+      v2i16 v = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(v2i16{0, 0}, __builtin_bit_cast(v2bf16, x0),
+                                                          sc, false);
+      v = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(v, __builtin_bit_cast(v2bf16, x1), sc, true);
+      v8[k] = __builtin_bit_cast(int, v);
     }
     if constexpr (q_group<N>(RB, db) >= 0)
       QAcc<q_group<N>(RB, db)>::set(v8);
