@@ -90,11 +90,24 @@ typedef struct mla_plan mla_plan; /* opaque, host-owned */
  *                    (the effective count and chunk length follow the split rule
  *                    documented at mla_plan_query).
  *  num_cus      > 0: compute-unit count the cost model plans for; 0 queries the
- *                    current HIP device. */
+ *                    current HIP device.
+ *  plan_mode:        MLA_PLAN_AUTO (0): each sequence gets its own chunk length
+ *                    from a per-unit time model (KV bytes against MFMA work of
+ *                    its row count, plus fixed and partial-write costs), the
+ *                    candidates scored by list-scheduling the units, longest
+ *                    first, onto the CUs; the work units run longest sequence
+ *                    first.  MLA_PLAN_UNIFORM (1): one chunk length for every
+ *                    sequence, units in the caller's sequence order (the
+ *                    earlier rule, kept for comparison).  The host-only rules
+ *                    follow "bench(cake_mla_varq_dcp_decode): ..." (flashinfer
+ *                    PR #5588), table "What was measured", row "host plan". */
+#define MLA_PLAN_AUTO 0
+#define MLA_PLAN_UNIFORM 1
 typedef struct {
   int32_t force_fold;
   int32_t force_splits;
   int32_t num_cus;
+  int32_t plan_mode;
 } mla_plan_options;
 
 /* Build a plan.
@@ -226,7 +239,7 @@ void mla_plan_destroy(mla_plan* plan);
 /* Message for the last non-OK status on the calling thread ("" if none). */
 const char* mla_last_error(void);
 
-/* Per-sequence plan facts, for tests and tools.
+/* Per-sequence plan facts, for tests and tools; seq is the caller's index.
  *  fold = F_b, tiles = q_len[b] / F_b, splits = S_eff, chunk_len = L_b.
  *  Split rule: with S requested chunks and granule G = MLA_KV_GRANULE,
  *    L = G * ceil(ceil(kv_len / S) / G),  S_eff = ceil(kv_len / L),
@@ -234,6 +247,13 @@ const char* mla_last_error(void);
  *  Any output pointer may be NULL. */
 mla_status mla_plan_query(const mla_plan* plan, int32_t seq, int32_t* fold, int32_t* tiles,
                           int32_t* splits, int32_t* chunk_len);
+
+/* The order in which the plan runs the sequences' work units: order[i] is
+ * the caller's index of the i-th sequence (a permutation of 0 .. batch - 1;
+ * longest unit first under MLA_PLAN_AUTO, the caller's order under
+ * MLA_PLAN_UNIFORM or forced splits).  order: HOST array [batch].
+ * Errors: INVALID_ARGUMENT (null plan or order). */
+mla_status mla_plan_order(const mla_plan* plan, int32_t* order);
 
 /* Whole-plan facts: main-kernel work units (one workgroup each), tiles that
  * are split (rows merged by the reduce), main-kernel launches (one per slice

@@ -21,6 +21,8 @@ MLA_ERR_WORKSPACE_TOO_SMALL = 3
 MLA_ERR_DEVICE = 4
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3 = 1
+MLA_PLAN_AUTO = 0
+MLA_PLAN_UNIFORM = 1
 DQK = 576
 DV = 512
 KV_GRANULE = 64
@@ -29,7 +31,7 @@ MAX_SHARDS = 1024
 
 EXPORTED = ["mla_decode_plan", "mla_decode_plan_shard", "mla_decode_run", "mla_decode_run_paged",
             "mla_decode_reduce", "mla_merge_shards", "mla_plan_destroy", "mla_last_error",
-            "mla_plan_query", "mla_plan_info", "mla_decode_run_static"]
+            "mla_plan_query", "mla_plan_info", "mla_decode_run_static", "mla_plan_order"]
 STATIC_WORKSPACE_BYTES = 32 << 20
 
 _lock = threading.Lock()
@@ -45,7 +47,7 @@ class MlaError(RuntimeError):
 
 class _Options(ctypes.Structure):
     _fields_ = [("force_fold", ctypes.c_int32), ("force_splits", ctypes.c_int32),
-                ("num_cus", ctypes.c_int32)]
+                ("num_cus", ctypes.c_int32), ("plan_mode", ctypes.c_int32)]
 
 
 def lib() -> ctypes.CDLL:
@@ -93,6 +95,8 @@ def lib() -> ctypes.CDLL:
         L.mla_plan_destroy.restype = None
         L.mla_last_error.argtypes = []
         L.mla_last_error.restype = ctypes.c_char_p
+        L.mla_plan_order.argtypes = [ctypes.c_void_p, i32p]
+        L.mla_plan_order.restype = ctypes.c_int
         L.mla_plan_query.argtypes = [ctypes.c_void_p, ctypes.c_int32, i32p, i32p, i32p, i32p]
         L.mla_plan_query.restype = ctypes.c_int
         L.mla_plan_info.argtypes = [ctypes.c_void_p, i32p, i32p, i32p, ctypes.POINTER(ctypes.c_size_t)]
@@ -129,9 +133,10 @@ class Plan:
     """Owns an mla_plan (host memory); free with close() or by garbage collection."""
 
     def __init__(self, num_heads, q_len, kv_len, kv_fp8=False, *, causal_end=None, force_fold=0,
-                 force_splits=0, num_cus=0):
+                 force_splits=0, num_cus=0, plan_mode=0):
         """causal_end: None (mla_decode_plan), or per-sequence causal ends of a
-        key shard (mla_decode_plan_shard)."""
+        key shard (mla_decode_plan_shard).  plan_mode: MLA_PLAN_AUTO (0) or
+        MLA_PLAN_UNIFORM (1)."""
         L = lib()
         q_len = [int(v) for v in q_len]
         kv_len = [int(v) for v in kv_len]
@@ -140,7 +145,7 @@ class Plan:
             raise ValueError("q_len and kv_len must have the same length")
         qa = (ctypes.c_int32 * max(n, 1))(*q_len)
         ka = (ctypes.c_int32 * max(n, 1))(*kv_len)
-        opts = _Options(int(force_fold), int(force_splits), int(num_cus))
+        opts = _Options(int(force_fold), int(force_splits), int(num_cus), int(plan_mode))
         handle = ctypes.c_void_p()
         ws = ctypes.c_size_t(0)
         self._h = None
@@ -172,6 +177,12 @@ class Plan:
         if self._h is None:
             raise ValueError("plan is closed")
         return self._h
+
+    def order(self):
+        """Caller indices of the sequences in the order their units run."""
+        out = (ctypes.c_int32 * len(self.q_len))()
+        _check(lib().mla_plan_order(self.handle, out))
+        return list(out)
 
     def query(self, seq: int):
         """(fold F, tiles T, splits S_eff, chunk length L) of one sequence."""

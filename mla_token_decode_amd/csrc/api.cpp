@@ -125,6 +125,15 @@ void mla_plan_destroy(mla_plan* plan) { delete plan; }
 
 const char* mla_last_error(void) { return mla::last_error(); }
 
+mla_status mla_plan_order(const mla_plan* plan, int32_t* order) {
+  if (!plan || !order) {
+    set_error("plan and order must be non-null");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  for (int32_t i = 0; i < plan->batch; ++i) order[i] = plan->seqs[i].src;
+  return MLA_OK;
+}
+
 mla_status mla_plan_query(const mla_plan* plan, int32_t seq, int32_t* fold, int32_t* tiles,
                           int32_t* splits, int32_t* chunk_len) {
   if (!plan) {
@@ -135,7 +144,7 @@ mla_status mla_plan_query(const mla_plan* plan, int32_t seq, int32_t* fold, int3
     set_error("sequence index %d out of range [0, %d)", seq, plan->batch);
     return MLA_ERR_INVALID_ARGUMENT;
   }
-  const SeqDesc& d = plan->seqs[seq];
+  const SeqDesc& d = plan->seqs[plan->pos[seq]];
   if (fold) *fold = d.F;
   if (tiles) *tiles = d.T;
   if (splits) *splits = d.S;
@@ -222,8 +231,7 @@ mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const
     a.num_seqs = ln.seq_end - ln.seq_begin;
     a.num_units = ln.num_units;
     a.units_per_xcd = (ln.num_units + kNumXcd - 1) / kNumXcd;
-    // page-table rows of this launch's sequences (the kernel indexes them from 0)
-    a.page_table = page_table ? page_table + static_cast<int64_t>(ln.seq_begin) * pt_stride : nullptr;
+    a.page_table = page_table;  // a sequence's row is its SeqDesc::src (the caller's index)
     for (int b = ln.seq_begin; b < ln.seq_end; ++b) a.seqs[b - ln.seq_begin] = plan->seqs[b];
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = fp8 ? (page_table ? launch_fp8_paged(a, ln.nrt, s) : launch_fp8_contiguous(a, ln.nrt, s))

@@ -173,7 +173,7 @@ __device__ __forceinline__ bool unit_setup(const MainArgs& args, UnitSetup& us) 
     us.pt_row = nullptr;
     us.kv_unit = args.kv + ((int64_t)sd.kv_row0 + us.uc.lo) * ROW_BYTES;
   } else {
-    us.pt_row = args.page_table + (int64_t)b * args.pt_stride;
+    us.pt_row = args.page_table + (int64_t)sd.src * args.pt_stride;
     us.kv_unit = args.kv;
     us.page_shift = args.page_shift;
     us.last_page_idx = (sd.n - 1) >> args.page_shift;

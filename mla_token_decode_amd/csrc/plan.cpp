@@ -15,7 +15,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <limits>
+#include <numeric>
+#include <queue>
 
 #include "plan.hpp"
 
@@ -81,6 +84,93 @@ double plan_cost(const std::vector<int32_t>& q_len, const std::vector<int32_t>& 
   return static_cast<double>(waves) * longest;
 }
 
+// Per-sequence chunking (plan_mode MLA_PLAN_AUTO).  A unit of sequence b
+// (one tile, or row block of a tile, against one chunk) is modelled in
+// microseconds of the one CU it occupies: streaming its KV rows or running
+// its MFMAs, whichever is longer, plus a fixed start-up and, when b is split,
+// writing its partial rows.  The rates are the kernels' measured ones on the
+// MI355X (HBM streaming shared by 256 CUs; MFMA throughput as the kernels
+// achieve it, per padded row), so the model ranks plans, it does not predict
+// times to the microsecond.
+constexpr double kCuBytesPerUs = 6.0e12 / 256 / 1e6;     // ~23.4 KB/us per CU
+constexpr double kFlopsPerKeyRow = 2.0 * (kDqk + kDv);     // QK^T and PV
+constexpr double kCuFlopsPerUsBf16 = 4.0e6;                // bf16 KV kernel
+constexpr double kCuFlopsPerUsFp8 = 8.0e6;                 // fp8 KV kernel
+constexpr double kUnitFixedUs = 4.0;                       // Q set-up, first tile, epilogue
+constexpr double kMergeFixedUs = 6.0;                      // launch and ramp of the merge
+constexpr double kMergeBytesPerUs = 5.0e12 / 1e6;          // merge: partial rows read back
+
+struct SeqModel {
+  int64_t n;
+  int64_t units_per_chunk;  // T * NRB
+  double per_key;           // us per key of one unit
+  double part;              // us per unit to write its partial rows (split sequences)
+  double part_bytes;        // partial bytes per unit
+};
+
+double unit_us(const SeqModel& m, int64_t keys, bool split) {
+  return kUnitFixedUs + static_cast<double>(keys) * m.per_key + (split ? m.part : 0.0);
+}
+
+// Chunk length of sequence m for a target unit time tau: the longest granule
+// multiple whose unit fits tau (at least one granule), then balanced over the
+// resulting chunk count by the split rule.
+void chunking_for(const SeqModel& m, double tau, int32_t* L, int32_t* S) {
+  if (unit_us(m, m.n, false) <= tau) {  // the whole sequence fits one unit
+    split_layout(m.n, 1, kGranule, L, S);
+    return;
+  }
+  const double keys = (tau - kUnitFixedUs - m.part) / m.per_key;
+  const int64_t l = keys <= kGranule ? kGranule : static_cast<int64_t>(keys) / kGranule * kGranule;
+  split_layout(m.n, static_cast<int>((m.n + l - 1) / l), kGranule, L, S);
+}
+
+// Predicted main-kernel makespan plus merge time of per-sequence chunkings
+// (L[b], S[b]): units taken in `order` (sequence by sequence, every unit of
+// a chunk together), each started on the CU that frees first.
+double schedule_us(const std::vector<SeqModel>& m, const std::vector<int32_t>& L,
+                   const std::vector<int32_t>& S, const std::vector<int>& order, int num_cus) {
+  double makespan = 0.0, part_bytes = 0.0;
+  int64_t units = 0;
+  for (size_t b = 0; b < m.size(); ++b) units += m[b].units_per_chunk * S[b];
+  if (units <= num_cus) {  // one wave: every unit starts at once
+    for (size_t b = 0; b < m.size(); ++b) {
+      makespan = std::max(makespan, unit_us(m[b], std::min<int64_t>(L[b], m[b].n), S[b] > 1));
+      if (S[b] > 1) part_bytes += m[b].part_bytes * m[b].units_per_chunk * S[b];
+    }
+    return makespan + (part_bytes > 0.0 ? kMergeFixedUs + part_bytes / kMergeBytesPerUs : 0.0);
+  }
+  std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
+  for (int i = 0; i < num_cus; ++i) cu.push(0.0);
+  for (int b : order) {
+    const bool split = S[b] > 1;
+    for (int32_t s = 0; s < S[b]; ++s) {
+      const int64_t keys = std::min<int64_t>(L[b], m[b].n - static_cast<int64_t>(s) * L[b]);
+      const double t = unit_us(m[b], keys, split);
+      for (int64_t u = 0; u < m[b].units_per_chunk; ++u) {
+        const double start = cu.top();
+        cu.pop();
+        cu.push(start + t);
+        makespan = std::max(makespan, start + t);
+      }
+    }
+    if (split) part_bytes += m[b].part_bytes * m[b].units_per_chunk * S[b];
+  }
+  return makespan + (part_bytes > 0.0 ? kMergeFixedUs + part_bytes / kMergeBytesPerUs : 0.0);
+}
+
+// Sequences by decreasing unit time (ties: the caller's order).
+std::vector<int> longest_first(const std::vector<SeqModel>& m, const std::vector<int32_t>& L,
+                               const std::vector<int32_t>& S) {
+  std::vector<int> order(m.size());
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    return unit_us(m[a], std::min<int64_t>(L[a], m[a].n), S[a] > 1) >
+           unit_us(m[b], std::min<int64_t>(L[b], m[b].n), S[b] > 1);
+  });
+  return order;
+}
+
 }  // namespace
 
 mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int32_t* kv_len,
@@ -109,8 +199,13 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
   const int force_fold = opts ? opts->force_fold : 0;
   const int force_splits = opts ? opts->force_splits : 0;
   const int num_cus = opts ? opts->num_cus : 0;
+  const int plan_mode = opts ? opts->plan_mode : MLA_PLAN_AUTO;
   if (force_fold < 0 || force_splits < 0 || num_cus < 0) {
     set_error("plan options must be >= 0");
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (plan_mode != MLA_PLAN_AUTO && plan_mode != MLA_PLAN_UNIFORM) {
+    set_error("unknown plan_mode %d", plan_mode);
     return MLA_ERR_INVALID_ARGUMENT;
   }
   if (num_cus < 1) {
@@ -153,11 +248,14 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
     }
   }
 
-  // Chunk length: forced, or the cost model's choice over granule multiples.
-  std::vector<int32_t> Sreq(batch);
+  // Chunking: forced, one chunk length for all (MLA_PLAN_UNIFORM), or per
+  // sequence (MLA_PLAN_AUTO).
+  std::vector<int32_t> Lb(batch), Sb(batch);
+  std::vector<int> order(batch);
+  std::iota(order.begin(), order.end(), 0);
   if (force_splits > 0) {
-    std::fill(Sreq.begin(), Sreq.end(), force_splits);
-  } else {
+    for (int b = 0; b < batch; ++b) split_layout(kl[b], force_splits, kGranule, &Lb[b], &Sb[b]);
+  } else if (plan_mode == MLA_PLAN_UNIFORM) {
     const int64_t nmax = *std::max_element(kl.begin(), kl.end());
     double best = std::numeric_limits<double>::infinity();
     int32_t bestL = static_cast<int32_t>((nmax + kGranule - 1) / kGranule * kGranule);
@@ -175,16 +273,99 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
       L += step;
     }
     for (int b = 0; b < batch; ++b)
-      Sreq[b] = static_cast<int32_t>((static_cast<int64_t>(kl[b]) + bestL - 1) / bestL);
+      split_layout(kl[b], static_cast<int>((static_cast<int64_t>(kl[b]) + bestL - 1) / bestL),
+                   kGranule, &Lb[b], &Sb[b]);
+  } else {
+    std::vector<SeqModel> m(batch);
+    const double flops = dtype == MLA_KV_BF16 ? kCuFlopsPerUsBf16 : kCuFlopsPerUsFp8;
+    double tau_hi = 0.0;
+    for (int b = 0; b < batch; ++b) {
+      const int32_t T = ql[b] / F[b], R = H * F[b];
+      const int32_t NRB = (R + kMaxUnitRows - 1) / kMaxUnitRows;
+      const int32_t RBS = NRB == 1 ? R : (((R + NRB - 1) / NRB + 15) / 16) * 16;
+      const int32_t rows_pad = (std::min(RBS, R) + 31) / 32 * 32;  // the kernels' row tiles
+      m[b].n = kl[b];
+      m[b].units_per_chunk = static_cast<int64_t>(T) * NRB;
+      m[b].per_key = std::max(static_cast<double>(row_bytes) / kCuBytesPerUs,
+                              rows_pad * kFlopsPerKeyRow / flops);
+      m[b].part_bytes = static_cast<double>(std::min(RBS, R)) * (kDv * 2 + 4);
+      m[b].part = m[b].part_bytes / kCuBytesPerUs;
+      tau_hi = std::max(tau_hi, unit_us(m[b], kl[b], false));
+    }
+    // Candidate unit times come from the chunk counts of the sequence with
+    // the most work: a ~3% geometric sweep of its chunk count, plus the counts
+    // that fill whole waves of CUs (1..16 waves, less a few units for the
+    // other sequences); each candidate's unit time then sets every
+    // sequence's chunking.  Chunkings needing more than 16 waves only add
+    // fixed costs and are skipped; "every sequence whole" always counts.
+    int dom = 0;
+    for (int b = 1; b < batch; ++b)
+      if (m[b].n * m[b].per_key * m[b].units_per_chunk >
+          m[dom].n * m[dom].per_key * m[dom].units_per_chunk)
+        dom = b;
+    const int64_t max_units = 16 * static_cast<int64_t>(num_cus);
+    const int64_t s_max = std::max<int64_t>(
+        1, std::min<int64_t>((m[dom].n + kGranule - 1) / kGranule, max_units / m[dom].units_per_chunk));
+    std::vector<int64_t> counts;
+    for (double x = 1.0; x <= static_cast<double>(s_max); x *= 1.03) counts.push_back(static_cast<int64_t>(x));
+    counts.push_back(s_max);
+    for (int64_t w = 1; w <= 16; ++w)
+      for (int64_t k = 0; k < 4; ++k)
+        counts.push_back((w * num_cus - k) / m[dom].units_per_chunk);
+    std::sort(counts.begin(), counts.end());
+    counts.erase(std::unique(counts.begin(), counts.end()), counts.end());
+    std::vector<double> taus;
+    for (int64_t c : counts) {
+      if (c < 1 || c > s_max) continue;
+      int32_t Ld, Sd;
+      split_layout(m[dom].n, static_cast<int>(c), kGranule, &Ld, &Sd);
+      taus.push_back(unit_us(m[dom], std::min<int64_t>(Ld, m[dom].n), Sd > 1) + 1e-9);
+    }
+    taus.push_back(tau_hi * (1.0 + 1e-9));  // every sequence whole
+    double best = std::numeric_limits<double>::infinity();
+    std::vector<int32_t> L(batch), S(batch), prevS;
+    for (size_t i = 0; i < taus.size(); ++i) {
+      const bool last = i + 1 == taus.size();
+      int64_t units = 0;
+      for (int b = 0; b < batch; ++b) {
+        chunking_for(m[b], taus[i], &L[b], &S[b]);
+        units += m[b].units_per_chunk * S[b];
+      }
+      if ((units > max_units && !last) || S == prevS) continue;
+      prevS = S;
+      const std::vector<int> ord = longest_first(m, L, S);
+      const double c = schedule_us(m, L, S, ord, num_cus);
+      if (c < best * (1.0 - 1e-9)) {
+        best = c;
+        Lb = L;
+        Sb = S;
+        order = ord;
+      }
+    }
   }
 
+  // Rows of each sequence in the caller's layout.
+  std::vector<int64_t> q_row0(batch), kv_row0(batch);
+  {
+    int64_t q_row = 0, kv_row = 0;
+    for (int b = 0; b < batch; ++b) {
+      q_row0[b] = q_row;
+      kv_row0[b] = kv_row;
+      q_row += static_cast<int64_t>(ql[b]) * H;
+      kv_row += kl[b];
+    }
+  }
   plan->seqs.resize(batch);
-  int64_t q_row = 0, kv_row = 0, part_row = 0;
+  plan->pos.resize(batch);
+  int64_t part_row = 0;
   int32_t split_tiles = 0;
-  for (int b = 0; b < batch; ++b) {
-    SeqDesc& d = plan->seqs[b];
-    d.q_row0 = static_cast<int32_t>(q_row);
-    d.kv_row0 = static_cast<int32_t>(kv_row);
+  for (int i = 0; i < batch; ++i) {
+    const int b = order[i];
+    plan->pos[b] = i;
+    SeqDesc& d = plan->seqs[i];
+    d.src = b;
+    d.q_row0 = static_cast<int32_t>(q_row0[b]);
+    d.kv_row0 = static_cast<int32_t>(kv_row0[b]);
     d.n = kl[b];
     d.ce = causal_end ? causal_end[b] : kl[b];
     d.qlen = ql[b];
@@ -193,7 +374,8 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
     d.R = H * F[b];
     d.NRB = (d.R + kMaxUnitRows - 1) / kMaxUnitRows;
     d.RBS = d.NRB == 1 ? d.R : (((d.R + d.NRB - 1) / d.NRB + 15) / 16) * 16;
-    split_layout(d.n, Sreq[b], kGranule, &d.L, &d.S);
+    d.L = Lb[b];
+    d.S = Sb[b];
     if (d.S > 1) {
       d.part_row0 = static_cast<int32_t>(part_row);
       part_row += static_cast<int64_t>(d.T) * d.S * d.R;
@@ -205,8 +387,6 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
     } else {
       d.part_row0 = -1;
     }
-    q_row += static_cast<int64_t>(ql[b]) * H;
-    kv_row += kl[b];
   }
 
   // Launch slices: up to kMaxSeqPerLaunch sequences each.

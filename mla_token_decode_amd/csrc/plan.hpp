@@ -39,6 +39,7 @@ struct SeqDesc {
   int32_t RBS;        // rows per row block (multiple of 16 unless NRB == 1)
   int32_t unit0;      // first work unit of the sequence within its launch
   int32_t ce;         // causal end: token i sees the keys j <= ce - qlen + i (ce = n normally)
+  int32_t src;        // the caller's index of the sequence (its page-table row)
 };
 
 struct MainArgs {
@@ -97,7 +98,8 @@ struct mla_plan {
   int32_t H = 0;
   mla_kv_dtype dtype = MLA_KV_BF16;
   int32_t num_cus = 0;
-  std::vector<mla::SeqDesc> seqs;  // global: unit0 is relative to the sequence's launch
+  std::vector<mla::SeqDesc> seqs;  // plan order; unit0 is relative to the sequence's launch
+  std::vector<int32_t> pos;        // caller's sequence index -> index in seqs
   std::vector<mla::Launch> launches;
   int64_t total_part_rows = 0;
   int32_t num_units = 0;

@@ -1,11 +1,13 @@
 // Host-plan driver for the sanitizer build (AddressSanitizer +
 // UndefinedBehaviorSanitizer, g++ only, no device code): builds plans over a
 // sweep of head counts, verify widths, context lengths, ragged batches and
-// forced options, and checks the plan's own invariants -- the fold rule
-// (largest divisor of q with H * F <= 128), the split rule (chunks of whole
-// 64-key granules covering [0, n)), the unit and partial-row counts, the
-// workspace size -- so that any out-of-bounds access, overflow or
-// uninitialised read in the planner surfaces under the sanitizers.
+// forced options and both plan modes, and checks the plan's own invariants --
+// the sequence order (a permutation of the caller's, with the caller's row
+// offsets), the fold rule (largest divisor of q with H * F <= 128), the split
+// rule (chunks of whole 64-key granules covering [0, n)), the unit and
+// partial-row counts, the workspace size -- so that any out-of-bounds access,
+// overflow or uninitialised read in the planner surfaces under the
+// sanitizers.
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -29,9 +31,23 @@ static int next_int(int lo, int hi) {  // [lo, hi]
 static void check_plan(const mla_plan& p, const std::vector<int32_t>& q, const std::vector<int32_t>& n,
                        int H, const int32_t* ce, int fold_cap) {
   int64_t part_rows = 0, units = 0;
-  CHECK(static_cast<int>(p.seqs.size()) == static_cast<int>(q.size()));
-  for (size_t b = 0; b < q.size(); ++b) {
-    const mla::SeqDesc& d = p.seqs[b];
+  const int batch = static_cast<int>(q.size());
+  CHECK(static_cast<int>(p.seqs.size()) == batch && static_cast<int>(p.pos.size()) == batch);
+  std::vector<int64_t> q_row0(batch), kv_row0(batch);
+  for (int b = 0, qr = 0, kr = 0; b < batch; ++b) {
+    q_row0[b] = qr;
+    kv_row0[b] = kr;
+    qr += q[b] * H;
+    kr += n[b];
+  }
+  std::vector<int> seen(batch, 0);
+  for (int i = 0; i < batch; ++i) {
+    const mla::SeqDesc& d = p.seqs[i];
+    CHECK(d.src >= 0 && d.src < batch && !seen[d.src]);
+    seen[d.src] = 1;
+    const int b = d.src;
+    CHECK(p.pos[b] == i);
+    CHECK(d.q_row0 == q_row0[b] && d.kv_row0 == kv_row0[b]);
     CHECK(d.F >= 1 && q[b] % d.F == 0 && H * d.F <= 128);
     for (int f = d.F + 1; f <= q[b]; ++f)  // the largest such divisor (up to the forced cap)
       CHECK(q[b] % f != 0 || H * f > 128 || (fold_cap > 0 && f > fold_cap));
@@ -77,7 +93,7 @@ int main() {
         if (c < qq) continue;
         for (int fs : {0, 1, 3, 256}) {
           std::vector<int32_t> q{qq}, n{c};
-          mla_plan_options o{0, fs, 256};
+          mla_plan_options o{0, fs, 256, MLA_PLAN_AUTO};
           mla_plan p;
           CHECK(mla::build_plan(1, H, q.data(), n.data(), nullptr, MLA_KV_BF16, &o, &p) == MLA_OK);
           check_plan(p, q, n, H, nullptr, 0);
@@ -96,7 +112,8 @@ int main() {
       n[b] = next_int(q[b], rep % 3 == 0 ? 40000 : 3000);
       ce[b] = next_int(1, n[b] + 5000);
     }
-    mla_plan_options o{next_int(0, 4), next_int(0, 1) ? 0 : next_int(1, 70), next_int(1, 512)};
+    mla_plan_options o{next_int(0, 4), next_int(0, 1) ? 0 : next_int(1, 70), next_int(1, 512),
+                       next_int(0, 1)};
     mla_plan p;
     const bool shard = rep % 4 == 1;
     CHECK(mla::build_plan(batch, H, q.data(), n.data(), shard ? ce.data() : nullptr,
