@@ -103,11 +103,27 @@ typedef struct mla_plan mla_plan; /* opaque, host-owned */
  *                    PR #5588), table "What was measured", row "host plan". */
 #define MLA_PLAN_AUTO 0
 #define MLA_PLAN_UNIFORM 1
+/*  merge_mode:       how split tiles are merged.  MLA_MERGE_REDUCE (1): by
+ *                    the reduce kernel of mla_decode_reduce.
+ *                    MLA_MERGE_LAST_ARRIVER (2): in the main kernel, by the
+ *                    last unit of each split row block to finish (it folds
+ *                    S x rows partial rows alone; the workspace then also
+ *                    holds one 64-bit arrival word per partial row).
+ *                    MLA_MERGE_AUTO (0): the reduce kernel, which measured
+ *                    faster than the last-arriver merge on the MI355X for
+ *                    every tested shape.
+ *                    The in-kernel merge follows "bench(cake_mla_varq_dcp_decode):
+ *                    ..." (flashinfer PR #5588), table "What was measured",
+ *                    row "split rows". */
+#define MLA_MERGE_AUTO 0
+#define MLA_MERGE_REDUCE 1
+#define MLA_MERGE_LAST_ARRIVER 2
 typedef struct {
   int32_t force_fold;
   int32_t force_splits;
   int32_t num_cus;
   int32_t plan_mode;
+  int32_t merge_mode;
 } mla_plan_options;
 
 /* Build a plan.

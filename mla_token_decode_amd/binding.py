@@ -23,6 +23,9 @@ MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3 = 1
 MLA_PLAN_AUTO = 0
 MLA_PLAN_UNIFORM = 1
+MLA_MERGE_AUTO = 0
+MLA_MERGE_REDUCE = 1
+MLA_MERGE_LAST_ARRIVER = 2
 DQK = 576
 DV = 512
 KV_GRANULE = 64
@@ -47,7 +50,8 @@ class MlaError(RuntimeError):
 
 class _Options(ctypes.Structure):
     _fields_ = [("force_fold", ctypes.c_int32), ("force_splits", ctypes.c_int32),
-                ("num_cus", ctypes.c_int32), ("plan_mode", ctypes.c_int32)]
+                ("num_cus", ctypes.c_int32), ("plan_mode", ctypes.c_int32),
+                ("merge_mode", ctypes.c_int32)]
 
 
 def lib() -> ctypes.CDLL:
@@ -133,10 +137,11 @@ class Plan:
     """Owns an mla_plan (host memory); free with close() or by garbage collection."""
 
     def __init__(self, num_heads, q_len, kv_len, kv_fp8=False, *, causal_end=None, force_fold=0,
-                 force_splits=0, num_cus=0, plan_mode=0):
+                 force_splits=0, num_cus=0, plan_mode=0, merge_mode=0):
         """causal_end: None (mla_decode_plan), or per-sequence causal ends of a
         key shard (mla_decode_plan_shard).  plan_mode: MLA_PLAN_AUTO (0) or
-        MLA_PLAN_UNIFORM (1)."""
+        MLA_PLAN_UNIFORM (1).  merge_mode: MLA_MERGE_AUTO (0), MLA_MERGE_REDUCE
+        (1) or MLA_MERGE_LAST_ARRIVER (2)."""
         L = lib()
         q_len = [int(v) for v in q_len]
         kv_len = [int(v) for v in kv_len]
@@ -145,7 +150,8 @@ class Plan:
             raise ValueError("q_len and kv_len must have the same length")
         qa = (ctypes.c_int32 * max(n, 1))(*q_len)
         ka = (ctypes.c_int32 * max(n, 1))(*kv_len)
-        opts = _Options(int(force_fold), int(force_splits), int(num_cus), int(plan_mode))
+        opts = _Options(int(force_fold), int(force_splits), int(num_cus), int(plan_mode),
+                        int(merge_mode))
         handle = ctypes.c_void_p()
         ws = ctypes.c_size_t(0)
         self._h = None

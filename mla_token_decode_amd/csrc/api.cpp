@@ -3,11 +3,13 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <random>
 
 #include "plan.hpp"
 
@@ -24,6 +26,20 @@ hipError_t static_scratch(void** ptr);
 namespace {
 
 constexpr int kMaxDevices = 64;
+
+// Tags of the in-kernel merge's arrival words: one per main-kernel call,
+// never 0 or 0xffffffff, so that a zeroed or 0xff-filled workspace (or the
+// words another call left) holds no arrival of this call.  The sequence
+// starts at a random point in each process.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{static_cast<uint32_t>(std::random_device{}())};
+  uint32_t e;
+  do {
+    e = counter.fetch_add(1, std::memory_order_relaxed) + 1u;
+  } while (e == 0u || e == 0xffffffffu);
+  return e;
+}
+
 std::mutex g_dev_mu;
 int g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 int g_dev_cus[kMaxDevices];
@@ -227,7 +243,13 @@ mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const
   a.page_shift = page_shift;
   a.num_pages = num_pages;
   a.H = plan->H;
+  a.epoch = next_epoch();
+  a.arrivals = plan->arrivals_offset
+                   ? reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) +
+                                                           plan->arrivals_offset)
+                   : nullptr;
   for (const Launch& ln : plan->launches) {
+    a.merge_in_kernel = ln.merge_in_kernel ? 1 : 0;
     a.num_seqs = ln.seq_end - ln.seq_begin;
     a.num_units = ln.num_units;
     a.units_per_xcd = (ln.num_units + kNumXcd - 1) / kNumXcd;
@@ -303,7 +325,7 @@ mla_status reduce_common(const mla_plan* plan, const void* workspace, void* o, f
   a.lse = lse;
   a.H = plan->H;
   for (const Launch& ln : plan->launches) {
-    if (ln.num_split_rows == 0) continue;
+    if (ln.num_split_rows == 0 || ln.merge_in_kernel) continue;  // nothing left to merge
     int ns = 0, rows = 0, smax = 0;
     for (int b = ln.seq_begin; b < ln.seq_end; ++b) {
       const SeqDesc& d = plan->seqs[b];

@@ -182,4 +182,114 @@ __device__ __forceinline__ bool unit_setup(const MainArgs& args, UnitSetup& us) 
   return true;
 }
 
+// In-kernel split-KV merge by the last unit of a split row block to finish
+// ("bench(cake_mla_varq_dcp_decode): ..." (flashinfer PR #5588), table "What
+// was measured", row "split rows").  Every workgroup calls it after its unit,
+// with every wave (all of them reach this point).  A unit of a split tile
+// makes its partial rows visible device-wide and arrives on its row block's
+// counter; the unit that arrives S-th folds the S partial rows of each of its
+// rows into O and LSE: ascending chunk order, each thread 4 (row, 8-column)
+// items at a time against the running maximum of the LSEs it has read (the
+// arithmetic of the reduce kernel).  The counter word holds the call's epoch
+// in its high half (never 0 or ~0) and that call's arrivals in the low half;
+// a word that holds another epoch counts as no arrival, so the workspace's
+// prior contents do not matter.
+__device__ __forceinline__ void merge_if_last(const MainArgs& args, unsigned char* smem) {
+  if (!args.merge_in_kernel) return;
+  UnitSetup us;  // the unit's indices only (the key layout is not used here)
+  if (!unit_setup<2 * kDqk, 64>(args, us) || us.S <= 1) return;
+  // release only (an L2 write-back, no invalidation: the units still running
+  // on this XCD keep their cached KV rows)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();  // every wave's partial rows are written and released
+  volatile unsigned* flag = reinterpret_cast<volatile unsigned*>(smem);
+  if (threadIdx.x == 0) {
+    unsigned long long* w =
+        args.arrivals + ((int64_t)us.part_row0 + (int64_t)us.t * us.S * us.R + us.rowb0);
+    const unsigned long long tag = (unsigned long long)args.epoch << 32;
+    unsigned long long old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long nw;
+    while (true) {  // ends: each failed swap means another unit's arrival went in
+      nw = (old >> 32) == (unsigned long long)args.epoch ? old + 1ull : tag | 1ull;
+      const unsigned long long prev = atomicCAS(w, old, nw);
+      if (prev == old) break;
+      old = prev;
+    }
+    *flag = (unsigned)(nw & 0xffffffffull) == (unsigned)us.S ? 1u : 0u;
+  }
+  __syncthreads();
+  if (*flag == 0u) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the row block's partial rows
+  const int S = us.S, RU = us.RU;
+  const int64_t p0 = (int64_t)us.part_row0 + (int64_t)us.t * S * us.R + us.rowb0;  // chunk 0, row 0
+  constexpr int kItems = 4;   // (row, 8-column) items per thread at a time
+  constexpr int kBatch = 4;   // chunks in flight per item
+  for (int it0 = threadIdx.x * kItems; it0 < RU * 64; it0 += blockDim.x * kItems) {
+    float m[kItems], W[kItems];
+    f32x4 a0[kItems], a1[kItems];
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+      m[j] = -INFINITY;
+      W[j] = 0.0f;
+      a0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      a1[j] = a0[j];
+    }
+    for (int s0 = 0; s0 < S; s0 += kBatch) {
+      float ls[kItems][kBatch];
+      u32x4 v[kItems][kBatch];
+#pragma unroll
+      for (int j = 0; j < kItems; ++j)
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          const int item = it0 + j, s = s0 + i;
+          if (item < RU * 64 && s < S) {
+            const int64_t prow = p0 + (int64_t)s * us.R + (item >> 6);
+            ls[j][i] = us.part_lse[prow];
+            v[j][i] = *(const u32x4*)(us.part_o + prow * kDv + 8 * (item & 63));
+          } else {
+            ls[j][i] = -INFINITY;
+            v[j][i] = u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+#pragma unroll
+      for (int j = 0; j < kItems; ++j) {
+        float mn = m[j];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) mn = fmaxf(mn, ls[j][i]);
+        const float sc = mn == -INFINITY ? 1.0f : __expf(m[j] - mn);
+        a0[j] *= sc;
+        a1[j] *= sc;
+        W[j] *= sc;
+        m[j] = mn;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          const float w = ls[j][i] == -INFINITY ? 0.0f : __expf(ls[j][i] - mn);
+          const u32x4 x = v[j][i];
+          W[j] += w;
+          a0[j] += w * f32x4{__builtin_bit_cast(float, x[0] << 16), __builtin_bit_cast(float, x[0] & 0xffff0000u),
+                             __builtin_bit_cast(float, x[1] << 16), __builtin_bit_cast(float, x[1] & 0xffff0000u)};
+          a1[j] += w * f32x4{__builtin_bit_cast(float, x[2] << 16), __builtin_bit_cast(float, x[2] & 0xffff0000u),
+                             __builtin_bit_cast(float, x[3] << 16), __builtin_bit_cast(float, x[3] & 0xffff0000u)};
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+      const int item = it0 + j;
+      if (item >= RU * 64) break;
+      const int r = item >> 6, c = item & 63;
+      const bool empty = !(W[j] > 0.0f);  // no chunk shows this row a key
+      const float inv = empty ? 0.0f : 1.0f / W[j];
+      u32x4 pk;
+      pk[0] = pack_bf16x2(a0[j][0] * inv, a0[j][1] * inv);
+      pk[1] = pack_bf16x2(a0[j][2] * inv, a0[j][3] * inv);
+      pk[2] = pack_bf16x2(a1[j][0] * inv, a1[j][1] * inv);
+      pk[3] = pack_bf16x2(a1[j][2] * inv, a1[j][3] * inv);
+      const int64_t orow = (int64_t)us.row0 + r;
+      *(u32x4*)(us.o + orow * kDv + 8 * c) = pk;
+      if (c == 0) us.lse[orow] = empty ? -INFINITY : m[j] + __logf(W[j]);
+    }
+  }
+}
+
 }  // namespace mla

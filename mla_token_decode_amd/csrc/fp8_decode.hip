@@ -873,6 +873,7 @@ template <int N, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8(const MainArgs args) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsBytes];
   unit_fp8<N, PAGED>(args, smem);
+  merge_if_last(args, smem);
 }
 
 }  // namespace fp8k

@@ -1701,6 +1701,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_main(const MainArgs ar
     unit_body<FP8, NRT, 1, PAGED>(args, smem);
   else
     unit_body<FP8, NRT, 0, PAGED>(args, smem);
+  merge_if_last(args, smem);
 }
 
 #ifndef MLA_PAGED_KV  // the merges are built once, with the contiguous-KV kernels

@@ -200,12 +200,18 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
   const int force_splits = opts ? opts->force_splits : 0;
   const int num_cus = opts ? opts->num_cus : 0;
   const int plan_mode = opts ? opts->plan_mode : MLA_PLAN_AUTO;
+  const int merge_mode = opts ? opts->merge_mode : MLA_MERGE_AUTO;
   if (force_fold < 0 || force_splits < 0 || num_cus < 0) {
     set_error("plan options must be >= 0");
     return MLA_ERR_INVALID_ARGUMENT;
   }
   if (plan_mode != MLA_PLAN_AUTO && plan_mode != MLA_PLAN_UNIFORM) {
     set_error("unknown plan_mode %d", plan_mode);
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  if (merge_mode != MLA_MERGE_AUTO && merge_mode != MLA_MERGE_REDUCE &&
+      merge_mode != MLA_MERGE_LAST_ARRIVER) {
+    set_error("unknown merge_mode %d", merge_mode);
     return MLA_ERR_INVALID_ARGUMENT;
   }
   if (num_cus < 1) {
@@ -398,13 +404,19 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
     ln.seq_end = std::min(batch, b0 + kMaxSeqPerLaunch);
     int64_t units = 0;
     int maxRU = 0, split_rows = 0;
+    double fold_bytes = 0.0;  // the most partial bytes one split row block folds
     for (int b = ln.seq_begin; b < ln.seq_end; ++b) {
       SeqDesc& d = plan->seqs[b];
       d.unit0 = static_cast<int32_t>(units);
       units += static_cast<int64_t>(d.T) * d.NRB * d.S;
       maxRU = std::max(maxRU, std::min(d.RBS, d.R));
-      if (d.S > 1) split_rows += d.T * d.R;
+      if (d.S > 1) {
+        split_rows += d.T * d.R;
+        fold_bytes = std::max(fold_bytes, static_cast<double>(d.S) * std::min(d.RBS, d.R) * (kDv * 2 + 4));
+      }
     }
+    ln.merge_in_kernel = split_rows > 0 && (merge_mode == MLA_MERGE_LAST_ARRIVER ||
+                                            (merge_mode == MLA_MERGE_AUTO && fold_bytes <= kLastArriverMaxBytes));
     if (units > std::numeric_limits<int32_t>::max() / 2) {
       set_error("too many work units (%lld)", static_cast<long long>(units));
       return MLA_ERR_INVALID_ARGUMENT;
@@ -418,10 +430,17 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
 
   plan->total_part_rows = part_row;
   plan->num_split_tiles = split_tiles;
+  plan->arrivals_offset = 0;
   if (part_row > 0) {
     const size_t lse_bytes = static_cast<size_t>(part_row) * sizeof(float);
     plan->part_o_offset = (lse_bytes + 255) / 256 * 256;
     plan->workspace_bytes = plan->part_o_offset + static_cast<size_t>(part_row) * kDv * sizeof(uint16_t);
+    bool any_in_kernel = false;
+    for (const Launch& ln : plan->launches) any_in_kernel = any_in_kernel || ln.merge_in_kernel;
+    if (any_in_kernel) {  // one 64-bit arrival word per partial row
+      plan->arrivals_offset = (plan->workspace_bytes + 255) / 256 * 256;
+      plan->workspace_bytes = plan->arrivals_offset + static_cast<size_t>(part_row) * 8;
+    }
   } else {
     plan->part_o_offset = 0;
     plan->workspace_bytes = 0;

@@ -59,6 +59,12 @@ struct MainArgs {
   int32_t num_seqs;
   int32_t num_units;
   int32_t units_per_xcd;
+  // in-kernel merge (0 / 1); arrivals: one 64-bit word per partial row (the
+  // counter of a split row block is the word of its chunk 0, row 0); epoch:
+  // this call's tag in the high half of those words (never 0 or ~0)
+  int32_t merge_in_kernel;
+  uint32_t epoch;
+  unsigned long long* arrivals;
   SeqDesc seqs[kMaxSeqPerLaunch];
 };
 
@@ -88,8 +94,16 @@ struct Launch {
   int seq_begin, seq_end;  // [begin, end) global sequence indices
   int num_units;
   int nrt;                 // 16-row MFMA tiles per row group (1..3), from the widest unit
-  int num_split_rows;      // rows the reduce merges for this slice
+  int num_split_rows;      // rows merged for this slice (by the reduce or in the kernel)
+  bool merge_in_kernel;    // the main kernel's last arrivers merge this slice's split tiles
 };
+
+// In-kernel merge under MLA_MERGE_AUTO: used when every split row block of a
+// launch folds at most this many partial bytes.  Zero: on the MI355X the
+// last-arriver merge measured slower than the reduce kernel on every tested
+// shape (the arriving units' L2 write-backs and the one-workgroup fold cost
+// more than the separate launch), so AUTO keeps the reduce kernel.
+constexpr double kLastArriverMaxBytes = 0.0;
 
 }  // namespace mla
 
@@ -106,6 +120,7 @@ struct mla_plan {
   int32_t num_split_tiles = 0;
   size_t workspace_bytes = 0;
   size_t part_o_offset = 0;  // byte offset of partial O inside the workspace
+  size_t arrivals_offset = 0;  // byte offset of the in-kernel merge's arrival words (0: none)
 };
 
 namespace mla {

@@ -69,7 +69,15 @@ static void check_plan(const mla_plan& p, const std::vector<int32_t>& q, const s
   CHECK(p.num_units == units);
   if (part_rows > 0) {
     CHECK(p.part_o_offset % 256 == 0 && p.part_o_offset >= static_cast<size_t>(part_rows) * 4);
-    CHECK(p.workspace_bytes == p.part_o_offset + static_cast<size_t>(part_rows) * 512 * 2);
+    const size_t o_end = p.part_o_offset + static_cast<size_t>(part_rows) * 512 * 2;
+    bool in_kernel = false;
+    for (const mla::Launch& ln : p.launches) in_kernel = in_kernel || ln.merge_in_kernel;
+    if (in_kernel) {
+      CHECK(p.arrivals_offset % 256 == 0 && p.arrivals_offset >= o_end);
+      CHECK(p.workspace_bytes == p.arrivals_offset + static_cast<size_t>(part_rows) * 8);
+    } else {
+      CHECK(p.arrivals_offset == 0 && p.workspace_bytes == o_end);
+    }
   } else {
     CHECK(p.workspace_bytes == 0);
   }
@@ -93,7 +101,7 @@ int main() {
         if (c < qq) continue;
         for (int fs : {0, 1, 3, 256}) {
           std::vector<int32_t> q{qq}, n{c};
-          mla_plan_options o{0, fs, 256, MLA_PLAN_AUTO};
+          mla_plan_options o{0, fs, 256, MLA_PLAN_AUTO, MLA_MERGE_AUTO};
           mla_plan p;
           CHECK(mla::build_plan(1, H, q.data(), n.data(), nullptr, MLA_KV_BF16, &o, &p) == MLA_OK);
           check_plan(p, q, n, H, nullptr, 0);
@@ -113,7 +121,7 @@ int main() {
       ce[b] = next_int(1, n[b] + 5000);
     }
     mla_plan_options o{next_int(0, 4), next_int(0, 1) ? 0 : next_int(1, 70), next_int(1, 512),
-                       next_int(0, 1)};
+                       next_int(0, 1), next_int(0, 2)};
     mla_plan p;
     const bool shard = rep % 4 == 1;
     CHECK(mla::build_plan(batch, H, q.data(), n.data(), shard ? ce.data() : nullptr,

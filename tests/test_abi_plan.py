@@ -81,7 +81,7 @@ def test_auto_plan_shapes_of_the_workloads():
 
 def test_workspace_size_formula():
     H, ql, kl = 12, [8, 3, 1], [5000, 700, 64]
-    p = plan(H, ql, kl, force_splits=4)
+    p = plan(H, ql, kl, force_splits=4, merge_mode=mb.MLA_MERGE_REDUCE)
     rows = 0
     for b in range(3):
         F, T, S, L = p.query(b)
@@ -89,6 +89,21 @@ def test_workspace_size_formula():
             rows += T * S * H * F
     lse_bytes = -(-rows * 4 // 256) * 256
     assert p.workspace_bytes == lse_bytes + rows * 512 * 2  # fp32 LSE, then bf16 O per partial row
+    # the in-kernel merge adds one 64-bit arrival word per partial row (256-byte aligned)
+    q = plan(H, ql, kl, force_splits=4, merge_mode=mb.MLA_MERGE_LAST_ARRIVER)
+    base = -(-(lse_bytes + rows * 512 * 2) // 256) * 256
+    assert q.workspace_bytes == base + rows * 8
+
+
+def test_merge_mode_choice():
+    # AUTO keeps the reduce kernel (no arrival words); LAST_ARRIVER adds them
+    for args in (((96, [1, 2, 3, 4] * 8, [32768] * 32), {}), ((12, [8], [1048576], True), {})):
+        auto = plan(*args[0])
+        red = plan(*args[0], merge_mode=mb.MLA_MERGE_REDUCE)
+        last = plan(*args[0], merge_mode=mb.MLA_MERGE_LAST_ARRIVER)
+        assert auto.workspace_bytes == red.workspace_bytes < last.workspace_bytes
+    with pytest.raises(mb.MlaError):
+        plan(12, [1], [100], merge_mode=3)
 
 
 def test_many_sequences_use_several_launches():

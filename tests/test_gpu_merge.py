@@ -1,0 +1,108 @@
+"""GPU: the two split-KV merges -- in the main kernel by the last unit of a
+split row block to finish, and the reduce kernel -- each checked against the
+oracle on the same inputs ("bench(cake_mla_varq_dcp_decode): ..." (flashinfer
+PR #5588), table "What was measured", row "split rows", where the in-kernel
+last-arriver merge replaced the reduce kernel).  The in-kernel merge counts
+arrivals in workspace words tagged with each call's epoch, so the tests also
+run it on a zeroed, a 0xff-filled and a reused workspace, which must all give
+the same bits."""
+import numpy as np
+import pytest
+
+from mla_token_decode_amd import binding as mb
+from mla_token_decode_amd import inputs as gen
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (H, q_len, kv_len, fp8, force_splits)
+    (96, [1, 2, 3, 4], [3000, 2000, 2500, 1300], False, 0),
+    (96, [1, 2, 3, 4], [3000, 2000, 2500, 1300], True, 3),
+    (12, [8], [5000], True, 3),
+    (12, [8, 1, 3], [2000, 700, 4096], False, 4),
+    (24, [2, 4], [130, 64], True, 2),
+]
+
+
+def _run(inp, dev, ws_fill, merge_mode, force_splits, ws=None, plan=None):
+    import torch
+    if plan is None:
+        plan = mb.Plan(inp.H, inp.q_len, inp.kv_len, inp.kv_fp8, merge_mode=merge_mode,
+                       force_splits=force_splits)
+    q, kv = dev
+    o, lse, ws_new = mb.alloc_outputs(plan, q.device)
+    if ws is None:
+        ws = ws_new
+        if ws_fill is not None:
+            ws.fill_(ws_fill)
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    mb.mla_decode_run(plan, q, kv, inp.sm_scale, inp.kv_scale, o, lse, ws, ws.numel())
+    mb.mla_decode_reduce(plan, ws, o, lse)
+    torch.cuda.synchronize()
+    return o.cpu().clone(), lse.cpu().clone(), ws, plan
+
+
+@pytest.mark.parametrize("H,ql,kl,fp8,fs", CASES)
+def test_last_arriver_merge_vs_reduce_kernel(H, ql, kl, fp8, fs):
+    gu.log(f"merge H={H} q={ql} n={kl} fp8={fp8} splits={fs}")
+    inp = gen.peaked_inputs(gen.random_inputs(H, ql, kl, fp8, seed=60 + H), beta=10.0, seed=3)
+    dev = gu.to_device(inp)
+    ro, rl = gu.oracle_full(inp)
+    o_k, l_k, ws, plan_k = _run(inp, dev, None, mb.MLA_MERGE_LAST_ARRIVER, fs)
+    assert plan_k.num_split_tiles > 0, "the case must have split tiles"
+    o_r, l_r, _, _ = _run(inp, dev, None, mb.MLA_MERGE_REDUCE, fs)
+    gu.compare(o_k.double().numpy(), l_k.double().numpy(), ro, rl, fp8, "last-arriver merge")
+    gu.compare(o_r.double().numpy(), l_r.double().numpy(), ro, rl, fp8, "reduce kernel")
+    # the same partial rows, folded in the same chunk order: within 1 bf16 ulp
+    d = np.abs(o_k.double().numpy() - o_r.double().numpy())
+    assert np.all(d <= 2.0 ** -7 * np.abs(o_r.double().numpy()) + 1e-30), float(d.max())
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_last_arriver_merge_ignores_prior_workspace_contents(fp8):
+    H, ql, kl = 96, [2, 3], [2600, 1900]
+    inp = gen.random_inputs(H, ql, kl, fp8, seed=77)
+    dev = gu.to_device(inp)
+    ref_o, ref_l, ws, plan = _run(inp, dev, 0, mb.MLA_MERGE_LAST_ARRIVER, 3)
+    for fill in (0xFF, 0, 0x5A):
+        o, l, _, _ = _run(inp, dev, fill, mb.MLA_MERGE_LAST_ARRIVER, 3)
+        assert torch_equal(o, ref_o) and torch_equal(l, ref_l), f"workspace filled with {fill:#x}"
+    for rep in range(3):  # the same workspace again: new epochs, the words of the last call
+        o, l, _, _ = _run(inp, dev, None, mb.MLA_MERGE_LAST_ARRIVER, 3, ws=ws, plan=plan)
+        assert torch_equal(o, ref_o) and torch_equal(l, ref_l), f"reuse {rep}"
+
+
+def test_last_arriver_merge_of_rows_that_see_no_key():
+    # a key shard whose last keys are hidden from the first verify tokens
+    import torch
+    H, q, n = 12, 8, 3000
+    inp = gen.random_inputs(H, [q], [n], True, seed=81)
+    a, b = 2100, 3000
+    sh = gen.Inputs(H, inp.q_len.copy(), np.array([b - a], np.int32), inp.q_bits,
+                    np.ascontiguousarray(inp.kv[a:b]), True, inp.kv_scale)
+    qd, kvd = gu.to_device(sh)
+    outs = []
+    for mode in (mb.MLA_MERGE_LAST_ARRIVER, mb.MLA_MERGE_REDUCE):
+        plan = mb.Plan(H, [q], [b - a], True, causal_end=[n - a - 895], force_splits=3,
+                       merge_mode=mode)
+        o, lse, ws = mb.alloc_outputs(plan, qd.device)
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        mb.mla_decode_run(plan, qd, kvd, sh.sm_scale, sh.kv_scale, o, lse, ws, ws.numel())
+        mb.mla_decode_reduce(plan, ws, o, lse)
+        torch.cuda.synchronize()
+        outs.append((o.double().cpu().numpy(), lse.double().cpu().numpy()))
+    (ok, lk), (orr, lr) = outs
+    empty = np.isneginf(lr)
+    assert empty.any() and (~empty).any()
+    assert np.array_equal(np.isneginf(lk), empty)
+    assert np.all(ok[empty] == 0.0)
+    assert np.all(np.abs(ok[~empty] - orr[~empty]) <= 2.0 ** -7 * np.abs(orr[~empty]) + 1e-30)
+
+
+def torch_equal(a, b):
+    import torch
+    return bool(torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)))

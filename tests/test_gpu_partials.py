@@ -8,8 +8,10 @@ bound, a wrong row of a folded tile or a misplaced record fails here even if
 the merge happened to hide it.  The record layout (partial LSE [P] fp32, then
 at the next 256-byte boundary partial O [P, 512] bf16; record of sequence b,
 tile t, chunk s, tile row r at part_row0(b) + (t S + s) R + r, sequences in
-batch order, unsplit ones taking no records) is recomputed here from the
-plan's per-sequence facts."""
+the plan's run order -- the caller's order under forced splits -- unsplit
+ones taking no records) is recomputed here from the plan's per-sequence
+facts.  The plans merge with the reduce kernel, so the workspace holds the
+partial records and nothing else."""
 import numpy as np
 import pytest
 
@@ -47,7 +49,8 @@ def test_split_workspace_matches_oracle_partials(case, peaked):
     inp = gen.random_inputs(H, q_len, kv_len, fp8, seed=61)
     if peaked:
         inp = gen.peaked_inputs(inp, beta=10.0, seed=4)
-    plan = mb.Plan(H, inp.q_len, inp.kv_len, fp8, force_splits=splits)
+    plan = mb.Plan(H, inp.q_len, inp.kv_len, fp8, force_splits=splits,
+                   merge_mode=mb.MLA_MERGE_REDUCE)
     recs, P = _layout(plan, H)
     assert P > 0
     q, kv = gu.to_device(inp)
