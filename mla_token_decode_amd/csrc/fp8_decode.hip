@@ -522,7 +522,7 @@ __device__ __forceinline__ void softmax_tile(f32x4 (&S)[2][N], Soft<N>& sm, int 
 // is rescaled.  Every wave of the workgroup calls it (two barriers).
 template <int N>
 __device__ __forceinline__ void move_references(f32x4 (&S)[2][N], Soft<N>& sm, int k0,
-                                                bool edge, lds_u8* lds, lds_u8* pbuf,
+                                                bool edge, bool o_zero, lds_u8* lds, lds_u8* pbuf,
                                                 const PBase& pb, int kh, int rh, int lane) {
   const int l16 = lane & 15, g = lane >> 4, l32 = lane & 31;
   typedef __attribute__((address_space(3))) float lds_f32;
@@ -561,7 +561,9 @@ __device__ __forceinline__ void move_references(f32x4 (&S)[2][N], Soft<N>& sm, i
   for (int rb = 0; rb < N; ++rb) sm.l[rb] += sm.ps[rb];
   lds_barrier();
   // O rows of row block pbk: every lane scales its row (rare: the AGPRs are
-  // read, scaled and written back in place)
+  // read, scaled and written back in place); nothing to scale while O is
+  // still zero (the first tile, which sets the references)
+  if (o_zero) return;
   static_for<N>([&](auto pc) {
     constexpr int pbk = decltype(pc)::value;
     const float f = factor[32 * pbk + l32];
@@ -722,7 +724,7 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
     const TileLoads<PAGED> tl(src, t + 3, e, lds + ((t + 3) % kSlots) * kTileB);
     if (__builtin_amdgcn_readfirstlane((fl[0] | fl[1]) | (fl[2] | fl[3])) != 0) {
       move_references<N>(S, sm, kKeys * t + 32 * kh + 4 * g, kKeys * t + kKeys - 1 > us.uc.min_lim,
-                         lds, pbuf_t, pb, kh, rh, lane);
+                         t == 0, lds, pbuf_t, pb, kh, rh, lane);
     } else {
 #pragma unroll
       for (int rb = 0; rb < N; ++rb) sm.l[rb] += sm.ps[rb];
