@@ -54,11 +54,19 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# Profiling runs (--profile) read no clocks: rocm-smi is a script started
+# through env, and under a profiler's preloaded library that start would come
+# after the GPU is initialised.
+READ_CLOCKS = True
+
+
 def read_clocks():
     """SCLK / MCLK of GPU 0 as the driver reports them right now (rocm-smi,
     best effort: None with the reason when unavailable)."""
     import re
     import subprocess
+    if not READ_CLOCKS:
+        return {"error": "not read in profiling runs"}
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
                            timeout=20)
@@ -298,6 +306,26 @@ def cpu_baseline(head_inp, other_inps):
     }
 
 
+def profile_inputs(name):
+    """Inputs and device copies of one named workload (profiling runs)."""
+    import torch
+    from mla_token_decode_amd import inputs as gen
+    if name.startswith("flat_"):
+        _, kind, q, _ = name.split("_")
+        q = int(q[1:])
+        if kind == "fp8":
+            base = gen.gen_workload_inputs(gen.workload(HEADLINE))
+            kv, scale = base.kv, base.kv_scale
+        else:
+            kv, scale = gen.gen_kv(6, 1048576, False)
+        qb = gen.gen_q_bits(6, q, 12)
+        inp = gen.Inputs(12, np.array([q], np.int32), np.array([1048576], np.int32), qb, kv,
+                         kind == "fp8", scale)
+    else:
+        inp = gen.gen_workload_inputs(gen.workload(name))
+    return inp, to_device(inp)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,7 +337,14 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--profile", metavar="WORKLOAD",
+                    help="profiling run: the reference kernel, then --steps cold-cache calls "
+                         "of one workload (small, h12_131k, h96_125k, h12_1m_fp8, ragged, or "
+                         "flat_{fp8,bf16}_q{1,2,4,8}_1m); prints one JSON line")
     args = ap.parse_args()
+    if args.profile:
+        global READ_CLOCKS
+        READ_CLOCKS = False
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the decode of one sequence shard is the single-GPU kernel; see the design notes "
@@ -338,6 +373,13 @@ def main():
     log(f"read stream (torch.sum over 1 GiB): {read_stream_gbps:.0f} GB/s")
 
     meas = dict(steps=args.steps, warmup=args.warmup, flush=flush, settle_ms=args.settle_ms)
+    if args.profile:
+        inp, dev = profile_inputs(args.profile)
+        st = measure(inp, dev, **meas)
+        print(json.dumps({"profile": args.profile, "steps": args.steps, "warmup": args.warmup,
+                          **{k: (round(v, 3) if isinstance(v, float) else v) for k, v in st.items()}}),
+              flush=True)
+        return
     log(f"generating {HEADLINE}")
     w = gen.workload(HEADLINE)
     inp = gen.gen_workload_inputs(w)
