@@ -15,8 +15,8 @@
 
 namespace mla {
 const char* last_error();
-hipError_t launch_main_contiguous(const MainArgs& a, bool fp8, int nrt, hipStream_t stream);
-hipError_t launch_main_paged(const MainArgs& a, bool fp8, int nrt, hipStream_t stream);
+hipError_t launch_main_contiguous(const MainArgs& a, int nrt, hipStream_t stream);  // bf16 KV
+hipError_t launch_main_paged(const MainArgs& a, int nrt, hipStream_t stream);       // bf16 KV
 hipError_t launch_fp8_contiguous(const MainArgs& a, int nrt, hipStream_t stream);
 hipError_t launch_fp8_paged(const MainArgs& a, int nrt, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
@@ -257,8 +257,8 @@ mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const
     for (int b = ln.seq_begin; b < ln.seq_end; ++b) a.seqs[b - ln.seq_begin] = plan->seqs[b];
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = fp8 ? (page_table ? launch_fp8_paged(a, ln.nrt, s) : launch_fp8_contiguous(a, ln.nrt, s))
-                       : (page_table ? launch_main_paged(a, false, ln.nrt, s)
-                                     : launch_main_contiguous(a, false, ln.nrt, s));
+                       : (page_table ? launch_main_paged(a, ln.nrt, s)
+                                     : launch_main_contiguous(a, ln.nrt, s));
     if (e != hipSuccess) {
       set_error("main kernel launch failed: %s", hipGetErrorString(e));
       return MLA_ERR_DEVICE;

@@ -1971,20 +1971,19 @@ static void launch_main_t(const MainArgs& a, int nrt, int grid, hipStream_t stre
 // This file is compiled twice: once for contiguous KV (with the merges) and
 // once, with MLA_PAGED_KV defined (kernels_paged.hip), for paged KV, so that
 // the two sets of main kernels build in parallel.
+// bf16 KV only: fp8 KV runs the kernel of fp8_decode.hip (this file's fp8
+// template branches are the earlier fp8 kernels, no longer instantiated).
 #ifdef MLA_PAGED_KV
-hipError_t launch_main_paged(const MainArgs& a, bool fp8, int nrt, hipStream_t stream) {
+hipError_t launch_main_paged(const MainArgs& a, int nrt, hipStream_t stream) {
   constexpr bool kPaged = true;
 #else
-hipError_t launch_main_contiguous(const MainArgs& a, bool fp8, int nrt, hipStream_t stream) {
+hipError_t launch_main_contiguous(const MainArgs& a, int nrt, hipStream_t stream) {
   constexpr bool kPaged = false;
 #endif
   const int grid = ((a.num_units + kNumXcd - 1) / kNumXcd) * kNumXcd;
   if (grid == 0) return hipSuccess;
   if (nrt < 1 || nrt > 3) return hipErrorInvalidValue;
-  if (fp8)
-    launch_main_t<true, kPaged>(a, nrt, grid, stream);
-  else
-    launch_main_t<false, kPaged>(a, nrt, grid, stream);
+  launch_main_t<false, kPaged>(a, nrt, grid, stream);
   return hipGetLastError();
 }
 

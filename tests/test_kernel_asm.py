@@ -39,9 +39,9 @@ def kernels(assembly):
     ks = {}
     for name in ("kernels", "kernels_paged"):  # contiguous and paged KV
         part = asm_scan.kernels(assembly[name])
-        assert len(part) == 6, sorted(part)  # {bf16, fp8} x {16, 32, 48 rows per row group}
+        assert len(part) == 3, sorted(part)  # bf16 KV, 16 / 32 / 48 rows per row group
         ks.update(part)
-    assert len(ks) == 12, sorted(ks)
+    assert len(ks) == 6, sorted(ks)
     return ks
 
 
