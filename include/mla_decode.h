@@ -22,10 +22,12 @@
  * each KV byte of a chunk is streamed from HBM once per tile; it cuts each
  * sequence into split-KV chunks and sizes the caller's workspace.
  * mla_decode_run enqueues the main decode kernel, which writes final O/LSE
- * for unsplit tiles and per-chunk partials for split ones; mla_decode_reduce
- * enqueues the log-sum-exp merge of those partials (a separate kernel, as in
- * "bench(cake_mla_varq_dcp_decode): ..." (flashinfer PR #5588), table "What
- * was measured", row "split rows").
+ * for unsplit tiles and per-chunk partials for split ones; the log-sum-exp
+ * merge of those partials runs as a separate kernel that mla_decode_reduce
+ * enqueues (or, on request, at the end of the main kernel: merge_mode) ("bench(cake_mla_varq_dcp_decode):
+ * ..." (flashinfer PR #5588), table "What was measured", row "split rows").
+ * Call both, in that order: mla_decode_reduce launches only what the main
+ * kernel left to it.
  *
  * Error convention.  Every call returns an mla_status and never throws or
  * aborts.  Unsupported shapes and options are rejected explicitly; there is
@@ -108,16 +110,36 @@ typedef struct mla_plan mla_plan; /* opaque, host-owned */
  *                    MLA_MERGE_LAST_ARRIVER (2): in the main kernel, by the
  *                    last unit of each split row block to finish (it folds
  *                    S x rows partial rows alone; the workspace then also
- *                    holds one 64-bit arrival word per partial row).
- *                    MLA_MERGE_AUTO (0): the reduce kernel, which measured
- *                    faster than the last-arriver merge on the MI355X for
- *                    every tested shape.
- *                    The in-kernel merge follows "bench(cake_mla_varq_dcp_decode):
+ *                    holds one 64-bit arrival word per partial row; launches
+ *                    with a sequence of more than 65535 chunks use the reduce
+ *                    kernel).
+ *                    MLA_MERGE_GRID (3): in the main kernel, by all of its
+ *                    workgroups together once the last unit has finished
+ *                    (they wait on one 64-bit counter per launch, held in the
+ *                    workspace), with the reduce kernel's fold and results.
+ *                    Only for launches whose work units fit the compute units
+ *                    at once (one workgroup per CU: units rounded up to a
+ *                    multiple of 8 <= num_cus); other launches use the reduce
+ *                    kernel, and so does a launch that mla_decode_run finds
+ *                    wider than the current device (it then enqueues that
+ *                    reduce itself).
+ *                    MLA_MERGE_AUTO (0): the reduce kernel.  On the MI355X
+ *                    both in-kernel merges measured slower than the separate
+ *                    reduce on every tested shape: the device-wide release of
+ *                    the partial rows (an L2 write-back per workgroup) and the
+ *                    fold, latency-bound in a workgroup that has to take several
+ *                    items one after another, cost more than the launch saved.
+ *                    The in-kernel merges follow "bench(cake_mla_varq_dcp_decode):
  *                    ..." (flashinfer PR #5588), table "What was measured",
- *                    row "split rows". */
+ *                    row "split rows".
+ *                    Both in-kernel merges count arrivals in workspace words
+ *                    tagged with each call's epoch and a generation, so the
+ *                    workspace's prior contents do not matter and a captured
+ *                    graph may replay the call. */
 #define MLA_MERGE_AUTO 0
 #define MLA_MERGE_REDUCE 1
 #define MLA_MERGE_LAST_ARRIVER 2
+#define MLA_MERGE_GRID 3
 typedef struct {
   int32_t force_fold;
   int32_t force_splits;
@@ -210,8 +232,9 @@ mla_status mla_decode_run_paged(const mla_plan* plan, const void* q, const void*
 /* Enqueue the split-KV merge on `stream`: for every split tile row, in
  * ascending chunk order, M = max_s lse_s, lse = M + ln sum_s exp(lse_s - M),
  * O = sum_s exp(lse_s - lse) * O_s; chunks a row cannot see (lse_s = -inf)
- * get weight 0.  A no-op (returns MLA_OK, launches nothing) when no sequence
- * is split.  Same pointer rules as mla_decode_run. */
+ * get weight 0.  Covers the launches whose split rows the main kernel did
+ * not merge itself (see merge_mode); a no-op (returns MLA_OK, launches
+ * nothing) when there are none.  Same pointer rules as mla_decode_run. */
 mla_status mla_decode_reduce(const mla_plan* plan, const void* workspace, void* o, float* lse,
                              void* stream);
 
@@ -276,6 +299,13 @@ mla_status mla_plan_order(const mla_plan* plan, int32_t* order);
  * of up to 60 sequences), and the workspace bytes. Any pointer may be NULL. */
 mla_status mla_plan_info(const mla_plan* plan, int32_t* num_units, int32_t* num_split_tiles,
                          int32_t* num_launches, size_t* workspace_bytes);
+
+/* One main-kernel launch of the plan (0 <= launch < num_launches): its work
+ * units and who merges its split rows (MLA_MERGE_REDUCE, _LAST_ARRIVER or
+ * _GRID; 0 when it has none).  Any output pointer may be NULL.
+ * Errors: INVALID_ARGUMENT (null plan, launch out of range). */
+mla_status mla_plan_launch_info(const mla_plan* plan, int32_t launch, int32_t* num_units,
+                                int32_t* merge_mode);
 
 #ifdef __cplusplus
 }

@@ -26,6 +26,7 @@ MLA_PLAN_UNIFORM = 1
 MLA_MERGE_AUTO = 0
 MLA_MERGE_REDUCE = 1
 MLA_MERGE_LAST_ARRIVER = 2
+MLA_MERGE_GRID = 3
 DQK = 576
 DV = 512
 KV_GRANULE = 64
@@ -34,7 +35,8 @@ MAX_SHARDS = 1024
 
 EXPORTED = ["mla_decode_plan", "mla_decode_plan_shard", "mla_decode_run", "mla_decode_run_paged",
             "mla_decode_reduce", "mla_merge_shards", "mla_plan_destroy", "mla_last_error",
-            "mla_plan_query", "mla_plan_info", "mla_decode_run_static", "mla_plan_order"]
+            "mla_plan_query", "mla_plan_info", "mla_decode_run_static", "mla_plan_order",
+            "mla_plan_launch_info"]
 STATIC_WORKSPACE_BYTES = 32 << 20
 
 _lock = threading.Lock()
@@ -105,6 +107,8 @@ def lib() -> ctypes.CDLL:
         L.mla_plan_query.restype = ctypes.c_int
         L.mla_plan_info.argtypes = [ctypes.c_void_p, i32p, i32p, i32p, ctypes.POINTER(ctypes.c_size_t)]
         L.mla_plan_info.restype = ctypes.c_int
+        L.mla_plan_launch_info.argtypes = [ctypes.c_void_p, ctypes.c_int32, i32p, i32p]
+        L.mla_plan_launch_info.restype = ctypes.c_int
         _lib = L
         return L
 
@@ -141,7 +145,7 @@ class Plan:
         """causal_end: None (mla_decode_plan), or per-sequence causal ends of a
         key shard (mla_decode_plan_shard).  plan_mode: MLA_PLAN_AUTO (0) or
         MLA_PLAN_UNIFORM (1).  merge_mode: MLA_MERGE_AUTO (0), MLA_MERGE_REDUCE
-        (1) or MLA_MERGE_LAST_ARRIVER (2)."""
+        (1), MLA_MERGE_LAST_ARRIVER (2) or MLA_MERGE_GRID (3)."""
         L = lib()
         q_len = [int(v) for v in q_len]
         kv_len = [int(v) for v in kv_len]
@@ -183,6 +187,13 @@ class Plan:
         if self._h is None:
             raise ValueError("plan is closed")
         return self._h
+
+    def launch(self, i: int):
+        """(work units, merge mode) of main-kernel launch i; the merge mode is
+        MLA_MERGE_REDUCE, _LAST_ARRIVER or _GRID, 0 when it has no split rows."""
+        nu, mm = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().mla_plan_launch_info(self.handle, int(i), ctypes.byref(nu), ctypes.byref(mm)))
+        return nu.value, mm.value
 
     def order(self):
         """Caller indices of the sequences in the order their units run."""

@@ -181,7 +181,27 @@ mla_status mla_plan_info(const mla_plan* plan, int32_t* num_units, int32_t* num_
   return MLA_OK;
 }
 
+mla_status mla_plan_launch_info(const mla_plan* plan, int32_t launch, int32_t* num_units,
+                                int32_t* merge_mode) {
+  if (!plan || launch < 0 || launch >= static_cast<int32_t>(plan->launches.size())) {
+    set_error("need a plan and 0 <= launch < its launch count (got %d)", launch);
+    return MLA_ERR_INVALID_ARGUMENT;
+  }
+  const Launch& ln = plan->launches[launch];
+  if (num_units) *num_units = ln.num_units;
+  if (merge_mode) {
+    *merge_mode = ln.num_split_rows == 0          ? 0
+                  : ln.merge == kMergeGrid        ? MLA_MERGE_GRID
+                  : ln.merge == kMergeLastArriver ? MLA_MERGE_LAST_ARRIVER
+                                                  : MLA_MERGE_REDUCE;
+  }
+  return MLA_OK;
+}
+
 namespace {
+
+mla_status reduce_launch(const mla_plan* plan, const Launch& ln, const void* workspace, void* o,
+                         float* lse, void* stream);
 
 // Shared by the contiguous and the paged entry points: `kv` is the KV array or
 // the page pool; `page_table` is null for contiguous KV.
@@ -223,7 +243,8 @@ mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const
     set_error("this plan needs a 16-byte aligned workspace of %zu bytes", plan->workspace_bytes);
     return MLA_ERR_INVALID_ARGUMENT;
   }
-  mla_status st = current_device(nullptr);
+  int dev_cus = 0;
+  mla_status st = current_device(&dev_cus);
   if (st != MLA_OK) return st;
 
   MainArgs a;
@@ -248,8 +269,20 @@ mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const
                    ? reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) +
                                                            plan->arrivals_offset)
                    : nullptr;
-  for (const Launch& ln : plan->launches) {
-    a.merge_in_kernel = ln.merge_in_kernel ? 1 : 0;
+  unsigned long long* grid_words =
+      plan->grid_words_offset
+          ? reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + plan->grid_words_offset)
+          : nullptr;
+  for (size_t li = 0; li < plan->launches.size(); ++li) {
+    const Launch& ln = plan->launches[li];
+    // The grid merge needs the launch's workgroups resident at once; on a
+    // device with fewer CUs than the plan assumed, the reduce kernel merges
+    // this launch's split rows right after it instead.
+    const int grid = (ln.num_units + kNumXcd - 1) / kNumXcd * kNumXcd;
+    const bool reduce_here = ln.merge == kMergeGrid && grid > dev_cus;
+    a.merge_kind = reduce_here ? kMergeReduce : ln.merge;
+    a.grid_word = ln.merge == kMergeGrid ? grid_words + li : nullptr;
+    a.num_split_rows = ln.num_split_rows;
     a.num_seqs = ln.seq_end - ln.seq_begin;
     a.num_units = ln.num_units;
     a.units_per_xcd = (ln.num_units + kNumXcd - 1) / kNumXcd;
@@ -262,6 +295,10 @@ mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const
     if (e != hipSuccess) {
       set_error("main kernel launch failed: %s", hipGetErrorString(e));
       return MLA_ERR_DEVICE;
+    }
+    if (reduce_here) {
+      st = reduce_launch(plan, ln, workspace, o, lse, stream);
+      if (st != MLA_OK) return st;
     }
   }
   return MLA_OK;
@@ -314,8 +351,9 @@ mla_status mla_decode_run_paged(const mla_plan* plan, const void* q, const void*
 
 namespace {
 
-mla_status reduce_common(const mla_plan* plan, const void* workspace, void* o, float* lse,
-                         void* stream) {
+// The reduce kernel over one launch's split rows.
+mla_status reduce_launch(const mla_plan* plan, const Launch& ln, const void* workspace, void* o,
+                         float* lse, void* stream) {
   ReduceArgs a;
   std::memset(&a, 0, sizeof a);
   a.part_lse = static_cast<const float*>(workspace);
@@ -324,26 +362,35 @@ mla_status reduce_common(const mla_plan* plan, const void* workspace, void* o, f
   a.o = static_cast<uint16_t*>(o);
   a.lse = lse;
   a.H = plan->H;
+  int ns = 0, rows = 0, smax = 0;
+  for (int b = ln.seq_begin; b < ln.seq_end; ++b) {
+    const SeqDesc& d = plan->seqs[b];
+    if (d.S <= 1) continue;
+    a.seqs[ns] = d;
+    a.row0[ns] = rows;
+    rows += d.T * d.R;
+    smax = d.S > smax ? d.S : smax;
+    ++ns;
+  }
+  a.num_seqs = ns;
+  a.num_rows = rows;
+  a.max_splits = smax;
+  hipError_t e = launch_reduce(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_error("reduce kernel launch failed: %s", hipGetErrorString(e));
+    return MLA_ERR_DEVICE;
+  }
+  return MLA_OK;
+}
+
+// The reduce kernel over every launch whose split rows the main kernel left
+// to it.
+mla_status reduce_common(const mla_plan* plan, const void* workspace, void* o, float* lse,
+                         void* stream) {
   for (const Launch& ln : plan->launches) {
-    if (ln.num_split_rows == 0 || ln.merge_in_kernel) continue;  // nothing left to merge
-    int ns = 0, rows = 0, smax = 0;
-    for (int b = ln.seq_begin; b < ln.seq_end; ++b) {
-      const SeqDesc& d = plan->seqs[b];
-      if (d.S <= 1) continue;
-      a.seqs[ns] = d;
-      a.row0[ns] = rows;
-      rows += d.T * d.R;
-      smax = d.S > smax ? d.S : smax;
-      ++ns;
-    }
-    a.num_seqs = ns;
-    a.num_rows = rows;
-    a.max_splits = smax;
-    hipError_t e = launch_reduce(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) {
-      set_error("reduce kernel launch failed: %s", hipGetErrorString(e));
-      return MLA_ERR_DEVICE;
-    }
+    if (ln.num_split_rows == 0 || ln.merge != kMergeReduce) continue;  // nothing left to merge
+    mla_status st = reduce_launch(plan, ln, workspace, o, lse, stream);
+    if (st != MLA_OK) return st;
   }
   return MLA_OK;
 }

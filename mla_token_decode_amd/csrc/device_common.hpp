@@ -182,20 +182,169 @@ __device__ __forceinline__ bool unit_setup(const MainArgs& args, UnitSetup& us) 
   return true;
 }
 
+// Arrival counter of an in-kernel merge: one 64-bit word per counted group,
+// holding the call's epoch (bits 63..32, never 0 or ~0), a generation (31..16)
+// and the arrivals of the current generation (15..0).  A word that holds
+// another epoch belongs to an earlier call (or is the workspace's prior
+// contents): the first arrival of this call claims it (compare-and-swap to
+// generation 0 with one arrival); every other arrival is one fetch-and-add,
+// so arrivals that come together do not retry against each other.  The
+// arrival that brings the count to `expected` (<= 65535) swaps in the next
+// generation with a zero count, so a replay with the same epoch (a captured
+// graph launches with the same arguments) counts again from zero.  Returns
+// the generation this arrival belongs to; *last says whether it completed it.
+// Every update is a read-modify-write, so the chain of them carries each
+// arrival's release to whoever reads the word later.
+__device__ __forceinline__ unsigned arrive(unsigned long long* w, uint32_t epoch, unsigned expected,
+                                           bool* last) {
+  const unsigned long long tag = (unsigned long long)epoch << 32;
+  unsigned long long old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  bool claimed = false;
+  while ((uint32_t)(old >> 32) != epoch) {  // ends: a failed swap means the word changed
+    const unsigned long long prev = atomicCAS(w, old, tag | 1ull);
+    if (prev == old) {
+      claimed = true;
+      break;
+    }
+    old = prev;
+  }
+  if (claimed)
+    old = tag;  // this arrival is the call's first: generation 0, none before it
+  else
+    old = __hip_atomic_fetch_add(w, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned gen = (unsigned)(old >> 16) & 0xffffu;
+  const unsigned cnt = (unsigned)old & 0xffffu;
+  *last = cnt + 1u >= expected;
+  if (*last)
+    __hip_atomic_exchange(w, tag | ((unsigned long long)((gen + 1u) & 0xffffu) << 16), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
+  return gen;
+}
+
+// Split-KV fold of one split output row over its S chunks, for 64 of the 512
+// value columns (block cb), by 256 threads: thread (part p = tid / 8, column
+// group cg = tid % 8) owns columns 8 cg .. 8 cg + 7 of the block (one 16-byte
+// load per chunk) and folds chunks p, p + 32, ... in ascending order, eight at
+// a time with their loads in flight together, against the running maximum of
+// the LSEs it has read (its sums are rescaled when that maximum moves).  The
+// 32 per-part results are combined in part order through LDS, so the result
+// does not depend on timing.  A chunk that shows the row no key has
+// LSE = -inf and weight 0; a row no chunk shows a key gets O = 0, LSE = -inf.
+// Partial row of chunk s: pbase + s * R.  Every thread of the block calls it;
+// it ends with the LDS free again.
+constexpr int kFoldThreads = 256;
+constexpr int kFoldCols = 64;                          // value columns per block
+constexpr int kFoldGroups = kFoldCols / 8;             // 8-column groups
+constexpr int kFoldParts = kFoldThreads / kFoldGroups;  // chunk phases per block
+constexpr int kFoldBatch = 8;                          // chunk loads in flight per thread
+
+struct FoldLds {
+  f32x4 acc[kFoldParts][kFoldGroups][2];
+  float w[kFoldParts], m[kFoldParts];
+};
+
+__device__ __forceinline__ float merge_weight(float ls, float M) {
+  return ls == -INFINITY ? 0.0f : __expf(ls - M);
+}
+
+// 4 bf16 (two dwords, element 0 in the low half of the first) -> fp32, exact.
+__device__ __forceinline__ f32x4 bf16x4_to_f32(uint2 pk) {
+  return f32x4{__builtin_bit_cast(float, pk.x << 16), __builtin_bit_cast(float, pk.x & 0xffff0000u),
+               __builtin_bit_cast(float, pk.y << 16), __builtin_bit_cast(float, pk.y & 0xffff0000u)};
+}
+
+// 8 bf16 (one 16-byte load) -> two fp32 quads, exact.
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4& pk, f32x4& lo, f32x4& hi) {
+  lo = bf16x4_to_f32(uint2{pk[0], pk[1]});
+  hi = bf16x4_to_f32(uint2{pk[2], pk[3]});
+}
+
+__device__ __forceinline__ void fold_split_row(const float* part_lse, const uint16_t* part_o,
+                                               int64_t pbase, int S, int R, int cb,
+                                               uint16_t* o_row, float* lse_out, FoldLds& lds) {
+  const int part = threadIdx.x / kFoldGroups;
+  const int cg = threadIdx.x % kFoldGroups;
+  float m = -INFINITY, W = 0.0f;
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t* po = part_o + kFoldCols * cb + 8 * cg;
+  for (int s0 = part; s0 < S; s0 += kFoldBatch * kFoldParts) {
+    float ls[kFoldBatch];
+    u32x4 v[kFoldBatch];
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) {
+      const int s = s0 + i * kFoldParts;
+      if (s < S) {
+        const int64_t prow = pbase + (int64_t)s * R;
+        ls[i] = part_lse[prow];
+        v[i] = *(const u32x4*)(po + prow * kDv);
+      } else {
+        ls[i] = -INFINITY;
+        v[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    float mn = m;
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) mn = fmaxf(mn, ls[i]);
+    // sums so far are 0 while m = -inf; exp(-inf) = 0 covers a first finite mn
+    const float sc = mn == -INFINITY ? 1.0f : __expf(m - mn);
+    a0 *= sc;
+    a1 *= sc;
+    W *= sc;
+    m = mn;
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) {
+      const float w = merge_weight(ls[i], m);
+      f32x4 lo, hi;
+      bf16x8_to_f32(v[i], lo, hi);
+      W += w;
+      a0 += w * lo;
+      a1 += w * hi;
+    }
+  }
+  lds.acc[part][cg][0] = a0;
+  lds.acc[part][cg][1] = a1;
+  if (cg == 0) {
+    lds.w[part] = W;
+    lds.m[part] = m;
+  }
+  __syncthreads();
+  if (threadIdx.x < kFoldGroups) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < kFoldParts; ++p) M = fmaxf(M, lds.m[p]);
+    f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+    float Wt = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kFoldParts; ++p) {
+      const float f = merge_weight(lds.m[p], M);
+      t0 += f * lds.acc[p][cg][0];
+      t1 += f * lds.acc[p][cg][1];
+      Wt += f * lds.w[p];
+    }
+    const bool empty = !(Wt > 0.0f);  // no chunk shows this row a key
+    const float inv = empty ? 0.0f : 1.0f / Wt;
+    u32x4 pk;
+    pk[0] = pack_bf16x2(t0[0] * inv, t0[1] * inv);
+    pk[1] = pack_bf16x2(t0[2] * inv, t0[3] * inv);
+    pk[2] = pack_bf16x2(t1[0] * inv, t1[1] * inv);
+    pk[3] = pack_bf16x2(t1[2] * inv, t1[3] * inv);
+    *(u32x4*)(o_row + kFoldCols * cb + 8 * cg) = pk;
+    if (lse_out && cg == 0) *lse_out = empty ? -INFINITY : M + __logf(Wt);
+  }
+  __syncthreads();
+}
+
 // In-kernel split-KV merge by the last unit of a split row block to finish
 // ("bench(cake_mla_varq_dcp_decode): ..." (flashinfer PR #5588), table "What
 // was measured", row "split rows").  Every workgroup calls it after its unit,
 // with every wave (all of them reach this point).  A unit of a split tile
 // makes its partial rows visible device-wide and arrives on its row block's
-// counter; the unit that arrives S-th folds the S partial rows of each of its
-// rows into O and LSE: ascending chunk order, each thread 4 (row, 8-column)
-// items at a time against the running maximum of the LSEs it has read (the
-// arithmetic of the reduce kernel).  The counter word holds the call's epoch
-// in its high half (never 0 or ~0) and that call's arrivals in the low half;
-// a word that holds another epoch counts as no arrival, so the workspace's
-// prior contents do not matter.
+// counter (the word of the block's chunk 0, row 0); the unit that arrives
+// S-th folds the S partial rows of each of its rows into O and LSE: ascending
+// chunk order, each thread 4 (row, 8-column) items at a time against the
+// running maximum of the LSEs it has read.
 __device__ __forceinline__ void merge_if_last(const MainArgs& args, unsigned char* smem) {
-  if (!args.merge_in_kernel) return;
+  if (args.merge_kind != kMergeLastArriver) return;
   UnitSetup us;  // the unit's indices only (the key layout is not used here)
   if (!unit_setup<2 * kDqk, 64>(args, us) || us.S <= 1) return;
   // release only (an L2 write-back, no invalidation: the units still running
@@ -206,16 +355,9 @@ __device__ __forceinline__ void merge_if_last(const MainArgs& args, unsigned cha
   if (threadIdx.x == 0) {
     unsigned long long* w =
         args.arrivals + ((int64_t)us.part_row0 + (int64_t)us.t * us.S * us.R + us.rowb0);
-    const unsigned long long tag = (unsigned long long)args.epoch << 32;
-    unsigned long long old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned long long nw;
-    while (true) {  // ends: each failed swap means another unit's arrival went in
-      nw = (old >> 32) == (unsigned long long)args.epoch ? old + 1ull : tag | 1ull;
-      const unsigned long long prev = atomicCAS(w, old, nw);
-      if (prev == old) break;
-      old = prev;
-    }
-    *flag = (unsigned)(nw & 0xffffffffull) == (unsigned)us.S ? 1u : 0u;
+    bool last = false;
+    arrive(w, args.epoch, (unsigned)us.S, &last);
+    *flag = last ? 1u : 0u;
   }
   __syncthreads();
   if (*flag == 0u) return;
@@ -288,6 +430,75 @@ __device__ __forceinline__ void merge_if_last(const MainArgs& args, unsigned cha
       const int64_t orow = (int64_t)us.row0 + r;
       *(u32x4*)(us.o + orow * kDv + 8 * c) = pk;
       if (c == 0) us.lse[orow] = empty ? -INFINITY : m[j] + __logf(W[j]);
+    }
+  }
+}
+
+
+// In-kernel split-KV merge by the whole grid, for launches whose workgroups
+// are all resident at once (at most one per compute unit; the host only asks
+// for it then).  Every workgroup calls it after its unit, with every wave:
+// it makes its partial rows visible device-wide, arrives on the launch's
+// counter and waits for the last arrival; then the workgroups fold the
+// launch's split rows together, workgroup g taking the (split row, 64-column
+// block) items g, g + grid, ... with the fold of the reduce kernel (the same
+// arithmetic in the same order, so the results are the reduce kernel's bit
+// for bit).  The wait is bounded (about a second by the wall clock): a
+// workgroup that gives up writes NaN into the O and LSE of its items instead
+// of folding them, so such a failure shows in the outputs.
+constexpr long long kGridWaitTicks = 100000000;  // wall-clock ticks (100 MHz): 1 s
+
+__device__ __forceinline__ void merge_grid(const MainArgs& args, unsigned char* smem) {
+  if (args.merge_kind != kMergeGrid) return;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();  // every wave's partial rows are written and released
+  volatile unsigned* flag = reinterpret_cast<volatile unsigned*>(smem);
+  if (threadIdx.x == 0) {
+    bool last = false;
+    const unsigned gen = arrive(args.grid_word, args.epoch, gridDim.x, &last);
+    unsigned ok = 1u;
+    if (!last) {
+      const long long t0 = wall_clock64();
+      while (true) {
+        const unsigned long long w =
+            __hip_atomic_load(args.grid_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(w >> 32) != args.epoch || (((unsigned)(w >> 16)) & 0xffffu) != gen) break;
+        if (wall_clock64() - t0 > kGridWaitTicks) {
+          ok = 0u;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);  // ~512 clocks between polls
+      }
+    }
+    *flag = ok;
+  }
+  __syncthreads();
+  const bool ok = *flag != 0u;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every unit's partial rows
+  FoldLds& lds = *reinterpret_cast<FoldLds*>(smem + 256);
+  const int items = args.num_split_rows * (kDv / kFoldCols);
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int gr = item / (kDv / kFoldCols), cb = item % (kDv / kFoldCols);
+    int b = 0, row0 = 0;  // the split sequence that holds split row gr
+    for (; b < args.num_seqs; ++b) {
+      const SeqDesc& d = args.seqs[b];
+      if (d.S <= 1) continue;
+      if (gr < row0 + d.T * d.R) break;
+      row0 += d.T * d.R;
+    }
+    if (b == args.num_seqs) break;  // not reached: items cover the split rows exactly
+    const SeqDesc& sd = args.seqs[b];
+    const int local = gr - row0;
+    const int t = local / sd.R, r = local % sd.R;
+    const int64_t orow = (int64_t)sd.q_row0 + (int64_t)t * sd.R + r;
+    uint16_t* o_row = args.o + orow * kDv;
+    float* lse_out = cb == 0 ? args.lse + orow : nullptr;
+    if (ok) {
+      const int64_t pbase = (int64_t)sd.part_row0 + (int64_t)t * sd.S * sd.R + r;
+      fold_split_row(args.part_lse, args.part_o, pbase, sd.S, sd.R, cb, o_row, lse_out, lds);
+    } else if (threadIdx.x < kFoldGroups) {
+      *(u32x4*)(o_row + kFoldCols * cb + 8 * threadIdx.x) = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+      if (lse_out && threadIdx.x == 0) *lse_out = __builtin_nanf("");
     }
   }
 }

@@ -876,6 +876,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8(const MainArgs arg
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsBytes];
   unit_fp8<N, PAGED>(args, smem);
   merge_if_last(args, smem);
+  merge_grid(args, smem);
 }
 
 }  // namespace fp8k

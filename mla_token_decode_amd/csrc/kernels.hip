@@ -1702,6 +1702,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_main(const MainArgs ar
   else
     unit_body<FP8, NRT, 0, PAGED>(args, smem);
   merge_if_last(args, smem);
+  merge_grid(args, smem);
 }
 
 #ifndef MLA_PAGED_KV  // the merges are built once, with the contiguous-KV kernels
@@ -1721,16 +1722,6 @@ __device__ __forceinline__ float wave_max64(float v) {
 #pragma unroll
   for (int d = 8; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d));
   return v;
-}
-
-// 4 bf16 (two dwords, element 0 in the low half of the first) -> fp32, exact.
-__device__ __forceinline__ f32x4 bf16x4_to_f32(uint2 pk) {
-  return f32x4{__builtin_bit_cast(float, pk.x << 16), __builtin_bit_cast(float, pk.x & 0xffff0000u),
-               __builtin_bit_cast(float, pk.y << 16), __builtin_bit_cast(float, pk.y & 0xffff0000u)};
-}
-
-__device__ __forceinline__ float merge_weight(float ls, float M) {
-  return ls == -INFINITY ? 0.0f : __expf(ls - M);
 }
 
 // Sums of the per-part folds in part order; writes 4 bf16 columns and the LSE.
@@ -1754,29 +1745,13 @@ __device__ __forceinline__ void merge_finish(f32x4 (&red_acc)[kRedParts][kRedGro
 }
 
 // Split-KV merge for many chunks: one 256-thread block per (split output
-// row, 64 of the 512 value columns), as above, but a single pass.  Thread
-// (part p = tid / 8, column group cg = tid % 8) owns columns 8 cg .. 8 cg + 7
-// of the block (one 16-byte load per chunk) and folds chunks p, p + 32, ...
-// in ascending order, eight at a time with their loads in flight together,
-// against the running maximum of the LSEs it has read (its sums are rescaled
-// when that maximum moves).  The 32 per-part results are combined in part
-// order through LDS, so replays are bitwise identical.  A chunk that shows
-// the row no key has LSE = -inf and weight 0.
-constexpr int kRedWideParts = 32;
-constexpr int kRedWideGroups = kRedCols / 8;
-constexpr int kRedWideBatch = 8;
-static_assert(kRedWideParts * kRedWideGroups == kRedThreads, "one thread per (part, group)");
-
-// 8 bf16 (one 16-byte load) -> two fp32 quads, exact.
-__device__ __forceinline__ void bf16x8_to_f32(const u32x4& pk, f32x4& lo, f32x4& hi) {
-  lo = bf16x4_to_f32(uint2{pk[0], pk[1]});
-  hi = bf16x4_to_f32(uint2{pk[2], pk[3]});
-}
+// row, 64 of the 512 value columns), folded by fold_split_row (the fold the
+// grid merge of the main kernels also runs, in the same order).
+static_assert(kFoldThreads == kRedThreads, "the fold runs on the reduce block");
 
 __global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_kernel(const ReduceArgs args) {
-  __shared__ f32x4 red_acc[kRedWideParts][kRedWideGroups][2];
-  __shared__ float red_w[kRedWideParts], red_m[kRedWideParts];
-  constexpr int kBlocksPerRow = kDv / kRedCols;
+  __shared__ FoldLds lds;
+  constexpr int kBlocksPerRow = kDv / kFoldCols;
   const int gr = blockIdx.x / kBlocksPerRow;
   const int cb = blockIdx.x % kBlocksPerRow;
   if (gr >= args.num_rows) return;
@@ -1787,78 +1762,10 @@ __global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_kernel(const Re
   const int R = sd.R;
   const int t = local / R;
   const int r = local % R;
-  const int S = sd.S;
-  const int64_t pbase = (int64_t)sd.part_row0 + (int64_t)t * S * R + r;
-  const int part = threadIdx.x / kRedWideGroups;
-  const int cg = threadIdx.x % kRedWideGroups;
-
-  float m = -INFINITY, W = 0.0f;
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  const uint16_t* po = args.part_o + kRedCols * cb + 8 * cg;
-  for (int s0 = part; s0 < S; s0 += kRedWideBatch * kRedWideParts) {
-    float ls[kRedWideBatch];
-    u32x4 v[kRedWideBatch];
-#pragma unroll
-    for (int i = 0; i < kRedWideBatch; ++i) {
-      const int s = s0 + i * kRedWideParts;
-      if (s < S) {
-        const int64_t prow = pbase + (int64_t)s * R;
-        ls[i] = args.part_lse[prow];
-        v[i] = *(const u32x4*)(po + prow * kDv);
-      } else {
-        ls[i] = -INFINITY;
-        v[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    float mn = m;
-#pragma unroll
-    for (int i = 0; i < kRedWideBatch; ++i) mn = fmaxf(mn, ls[i]);
-    // sums so far are 0 while m = -inf; exp(-inf) = 0 covers a first finite mn
-    const float sc = mn == -INFINITY ? 1.0f : __expf(m - mn);
-    a0 *= sc;
-    a1 *= sc;
-    W *= sc;
-    m = mn;
-#pragma unroll
-    for (int i = 0; i < kRedWideBatch; ++i) {
-      const float w = merge_weight(ls[i], m);
-      f32x4 lo, hi;
-      bf16x8_to_f32(v[i], lo, hi);
-      W += w;
-      a0 += w * lo;
-      a1 += w * hi;
-    }
-  }
-  red_acc[part][cg][0] = a0;
-  red_acc[part][cg][1] = a1;
-  if (cg == 0) {
-    red_w[part] = W;
-    red_m[part] = m;
-  }
-  __syncthreads();
-  if (threadIdx.x >= kRedWideGroups) return;
-  float M = -INFINITY;
-#pragma unroll
-  for (int p = 0; p < kRedWideParts; ++p) M = fmaxf(M, red_m[p]);
-  f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
-  float Wt = 0.0f;
-#pragma unroll
-  for (int p = 0; p < kRedWideParts; ++p) {
-    const float f = merge_weight(red_m[p], M);
-    t0 += f * red_acc[p][cg][0];
-    t1 += f * red_acc[p][cg][1];
-    Wt += f * red_w[p];
-  }
-  const bool empty = !(Wt > 0.0f);  // no chunk shows this row a key
-  const float inv = empty ? 0.0f : 1.0f / Wt;
-  u32x4 pk;
-  pk[0] = pack_bf16x2(t0[0] * inv, t0[1] * inv);
-  pk[1] = pack_bf16x2(t0[2] * inv, t0[3] * inv);
-  pk[2] = pack_bf16x2(t1[0] * inv, t1[1] * inv);
-  pk[3] = pack_bf16x2(t1[2] * inv, t1[3] * inv);
+  const int64_t pbase = (int64_t)sd.part_row0 + (int64_t)t * sd.S * R + r;
   const int64_t orow = (int64_t)sd.q_row0 + (int64_t)t * R + r;
-  *(u32x4*)(args.o + orow * kDv + kRedCols * cb + 8 * cg) = pk;
-  if (cb == 0 && cg == 0) args.lse[orow] = empty ? -INFINITY : M + __logf(Wt);
+  fold_split_row(args.part_lse, args.part_o, pbase, sd.S, R, cb, args.o + orow * kDv,
+                 cb == 0 ? args.lse + orow : nullptr, lds);
 }
 
 // Split-KV merge for launches whose sequences have few chunks (S <= 16, e.g.
@@ -1995,7 +1902,7 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
     const int grid = (a.num_rows + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL(mla_decode_reduce_small_kernel, dim3(grid), dim3(kRedThreads), 0, stream, a);
   } else {
-    const int grid = (kDv / kRedCols) * a.num_rows;
+    const int grid = (kDv / kFoldCols) * a.num_rows;
     hipLaunchKernelGGL(mla_decode_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, stream, a);
   }
   return hipGetLastError();

@@ -210,7 +210,7 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
     return MLA_ERR_INVALID_ARGUMENT;
   }
   if (merge_mode != MLA_MERGE_AUTO && merge_mode != MLA_MERGE_REDUCE &&
-      merge_mode != MLA_MERGE_LAST_ARRIVER) {
+      merge_mode != MLA_MERGE_LAST_ARRIVER && merge_mode != MLA_MERGE_GRID) {
     set_error("unknown merge_mode %d", merge_mode);
     return MLA_ERR_INVALID_ARGUMENT;
   }
@@ -403,8 +403,7 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
     ln.seq_begin = b0;
     ln.seq_end = std::min(batch, b0 + kMaxSeqPerLaunch);
     int64_t units = 0;
-    int maxRU = 0, split_rows = 0;
-    double fold_bytes = 0.0;  // the most partial bytes one split row block folds
+    int maxRU = 0, split_rows = 0, max_s = 0;
     for (int b = ln.seq_begin; b < ln.seq_end; ++b) {
       SeqDesc& d = plan->seqs[b];
       d.unit0 = static_cast<int32_t>(units);
@@ -412,11 +411,22 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
       maxRU = std::max(maxRU, std::min(d.RBS, d.R));
       if (d.S > 1) {
         split_rows += d.T * d.R;
-        fold_bytes = std::max(fold_bytes, static_cast<double>(d.S) * std::min(d.RBS, d.R) * (kDv * 2 + 4));
+        max_s = std::max(max_s, d.S);
       }
     }
-    ln.merge_in_kernel = split_rows > 0 && (merge_mode == MLA_MERGE_LAST_ARRIVER ||
-                                            (merge_mode == MLA_MERGE_AUTO && fold_bytes <= kLastArriverMaxBytes));
+    // The grid merge needs every workgroup of the launch resident at once:
+    // at most one per compute unit (the main kernels hold one workgroup per
+    // CU).  A mode that cannot serve a launch falls back to the reduce kernel.
+    const int64_t grid = (units + kNumXcd - 1) / kNumXcd * kNumXcd;
+    const bool grid_fits = grid <= num_cus && grid <= kMaxArrivals;
+    if (split_rows == 0)
+      ln.merge = kMergeReduce;  // nothing to merge
+    else if (merge_mode == MLA_MERGE_LAST_ARRIVER && max_s <= kMaxArrivals)
+      ln.merge = kMergeLastArriver;
+    else if (merge_mode == MLA_MERGE_GRID && grid_fits)
+      ln.merge = kMergeGrid;
+    else
+      ln.merge = kMergeReduce;  // AUTO: on the MI355X both in-kernel merges measured slower
     if (units > std::numeric_limits<int32_t>::max() / 2) {
       set_error("too many work units (%lld)", static_cast<long long>(units));
       return MLA_ERR_INVALID_ARGUMENT;
@@ -431,15 +441,23 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
   plan->total_part_rows = part_row;
   plan->num_split_tiles = split_tiles;
   plan->arrivals_offset = 0;
+  plan->grid_words_offset = 0;
   if (part_row > 0) {
     const size_t lse_bytes = static_cast<size_t>(part_row) * sizeof(float);
     plan->part_o_offset = (lse_bytes + 255) / 256 * 256;
     plan->workspace_bytes = plan->part_o_offset + static_cast<size_t>(part_row) * kDv * sizeof(uint16_t);
-    bool any_in_kernel = false;
-    for (const Launch& ln : plan->launches) any_in_kernel = any_in_kernel || ln.merge_in_kernel;
-    if (any_in_kernel) {  // one 64-bit arrival word per partial row
+    bool any_last = false, any_grid = false;
+    for (const Launch& ln : plan->launches) {
+      any_last = any_last || ln.merge == kMergeLastArriver;
+      any_grid = any_grid || ln.merge == kMergeGrid;
+    }
+    if (any_last) {  // one 64-bit arrival word per partial row
       plan->arrivals_offset = (plan->workspace_bytes + 255) / 256 * 256;
       plan->workspace_bytes = plan->arrivals_offset + static_cast<size_t>(part_row) * 8;
+    }
+    if (any_grid) {  // one 64-bit counter per launch
+      plan->grid_words_offset = (plan->workspace_bytes + 255) / 256 * 256;
+      plan->workspace_bytes = plan->grid_words_offset + plan->launches.size() * 8;
     }
   } else {
     plan->part_o_offset = 0;

@@ -59,12 +59,16 @@ struct MainArgs {
   int32_t num_seqs;
   int32_t num_units;
   int32_t units_per_xcd;
-  // in-kernel merge (0 / 1); arrivals: one 64-bit word per partial row (the
-  // counter of a split row block is the word of its chunk 0, row 0); epoch:
-  // this call's tag in the high half of those words (never 0 or ~0)
-  int32_t merge_in_kernel;
+  // merge_kind: a MergeKind; arrivals (last-arriver merge): one 64-bit word
+  // per partial row (the counter of a split row block is the word of its
+  // chunk 0, row 0); grid_word (grid merge): the launch's counter; epoch: this
+  // call's tag in the high half of those words (never 0 or ~0);
+  // num_split_rows: the launch's split output rows (grid merge)
+  int32_t merge_kind;
   uint32_t epoch;
   unsigned long long* arrivals;
+  unsigned long long* grid_word;
+  int32_t num_split_rows;
   SeqDesc seqs[kMaxSeqPerLaunch];
 };
 
@@ -95,15 +99,16 @@ struct Launch {
   int num_units;
   int nrt;                 // 16-row MFMA tiles per row group (1..3), from the widest unit
   int num_split_rows;      // rows merged for this slice (by the reduce or in the kernel)
-  bool merge_in_kernel;    // the main kernel's last arrivers merge this slice's split tiles
+  int merge;               // MergeKind of this slice's split rows
 };
 
-// In-kernel merge under MLA_MERGE_AUTO: used when every split row block of a
-// launch folds at most this many partial bytes.  Zero: on the MI355X the
-// last-arriver merge measured slower than the reduce kernel on every tested
-// shape (the arriving units' L2 write-backs and the one-workgroup fold cost
-// more than the separate launch), so AUTO keeps the reduce kernel.
-constexpr double kLastArriverMaxBytes = 0.0;
+// Who merges a launch's split rows: the reduce kernel (mla_decode_reduce),
+// the last unit of each split row block to finish, or the whole grid of the
+// main kernel after its last unit (MLA_MERGE_REDUCE / LAST_ARRIVER / GRID).
+enum MergeKind : int32_t { kMergeReduce = 0, kMergeLastArriver = 1, kMergeGrid = 2 };
+
+// Largest count an arrival word holds (its low 16 bits).
+constexpr int kMaxArrivals = 65535;
 
 }  // namespace mla
 
@@ -120,7 +125,8 @@ struct mla_plan {
   int32_t num_split_tiles = 0;
   size_t workspace_bytes = 0;
   size_t part_o_offset = 0;  // byte offset of partial O inside the workspace
-  size_t arrivals_offset = 0;  // byte offset of the in-kernel merge's arrival words (0: none)
+  size_t arrivals_offset = 0;  // byte offset of the last-arriver merge's arrival words (0: none)
+  size_t grid_words_offset = 0;  // byte offset of the grid merge's counters, one per launch (0: none)
 };
 
 namespace mla {

@@ -1,11 +1,11 @@
 // Host-plan driver for the sanitizer build (AddressSanitizer +
 // UndefinedBehaviorSanitizer, g++ only, no device code): builds plans over a
 // sweep of head counts, verify widths, context lengths, ragged batches and
-// forced options and both plan modes, and checks the plan's own invariants --
+// forced options, both plan modes and every merge mode, and checks the plan's own invariants --
 // the sequence order (a permutation of the caller's, with the caller's row
 // offsets), the fold rule (largest divisor of q with H * F <= 128), the split
 // rule (chunks of whole 64-key granules covering [0, n)), the unit and
-// partial-row counts, the workspace size -- so that any out-of-bounds access,
+// partial-row counts, each launch's merge kind, the workspace size -- so that any out-of-bounds access,
 // overflow or uninitialised read in the planner surfaces under the
 // sanitizers.
 #include <cstdio>
@@ -29,7 +29,7 @@ static int next_int(int lo, int hi) {  // [lo, hi]
 }
 
 static void check_plan(const mla_plan& p, const std::vector<int32_t>& q, const std::vector<int32_t>& n,
-                       int H, const int32_t* ce, int fold_cap) {
+                       int H, const int32_t* ce, int fold_cap, int num_cus, int merge_mode) {
   int64_t part_rows = 0, units = 0;
   const int batch = static_cast<int>(q.size());
   CHECK(static_cast<int>(p.seqs.size()) == batch && static_cast<int>(p.pos.size()) == batch);
@@ -70,19 +70,42 @@ static void check_plan(const mla_plan& p, const std::vector<int32_t>& q, const s
   if (part_rows > 0) {
     CHECK(p.part_o_offset % 256 == 0 && p.part_o_offset >= static_cast<size_t>(part_rows) * 4);
     const size_t o_end = p.part_o_offset + static_cast<size_t>(part_rows) * 512 * 2;
-    bool in_kernel = false;
-    for (const mla::Launch& ln : p.launches) in_kernel = in_kernel || ln.merge_in_kernel;
-    if (in_kernel) {
-      CHECK(p.arrivals_offset % 256 == 0 && p.arrivals_offset >= o_end);
-      CHECK(p.workspace_bytes == p.arrivals_offset + static_cast<size_t>(part_rows) * 8);
-    } else {
-      CHECK(p.arrivals_offset == 0 && p.workspace_bytes == o_end);
+    bool any_last = false, any_grid = false;
+    for (const mla::Launch& ln : p.launches) {
+      any_last = any_last || ln.merge == mla::kMergeLastArriver;
+      any_grid = any_grid || ln.merge == mla::kMergeGrid;
     }
+    size_t end = o_end;
+    if (any_last) {
+      CHECK(p.arrivals_offset % 256 == 0 && p.arrivals_offset >= end);
+      end = p.arrivals_offset + static_cast<size_t>(part_rows) * 8;
+    } else {
+      CHECK(p.arrivals_offset == 0);
+    }
+    if (any_grid) {
+      CHECK(p.grid_words_offset % 256 == 0 && p.grid_words_offset >= end);
+      end = p.grid_words_offset + p.launches.size() * 8;
+    } else {
+      CHECK(p.grid_words_offset == 0);
+    }
+    CHECK(p.workspace_bytes == end);
   } else {
     CHECK(p.workspace_bytes == 0);
   }
   int covered = 0;
   for (const mla::Launch& ln : p.launches) {
+    // merge kind: the requested one where it applies, else the reduce kernel
+    const int64_t grid = (ln.num_units + 7) / 8 * 8;
+    int max_s = 0;
+    for (int i = ln.seq_begin; i < ln.seq_end; ++i) max_s = p.seqs[i].S > max_s ? p.seqs[i].S : max_s;
+    int want = mla::kMergeReduce;
+    if (ln.num_split_rows > 0) {
+      if (merge_mode == MLA_MERGE_LAST_ARRIVER && max_s <= mla::kMaxArrivals)
+        want = mla::kMergeLastArriver;
+      else if (merge_mode == MLA_MERGE_GRID && grid <= num_cus)
+        want = mla::kMergeGrid;
+    }
+    CHECK(ln.merge == want);
     CHECK(ln.seq_begin == covered && ln.seq_end > ln.seq_begin);
     CHECK(ln.seq_end - ln.seq_begin <= mla::kMaxSeqPerLaunch);
     CHECK(ln.nrt >= 1 && ln.nrt <= 3);
@@ -104,7 +127,7 @@ int main() {
           mla_plan_options o{0, fs, 256, MLA_PLAN_AUTO, MLA_MERGE_AUTO};
           mla_plan p;
           CHECK(mla::build_plan(1, H, q.data(), n.data(), nullptr, MLA_KV_BF16, &o, &p) == MLA_OK);
-          check_plan(p, q, n, H, nullptr, 0);
+          check_plan(p, q, n, H, nullptr, 0, 256, MLA_MERGE_AUTO);
           ++plans;
         }
       }
@@ -121,12 +144,12 @@ int main() {
       ce[b] = next_int(1, n[b] + 5000);
     }
     mla_plan_options o{next_int(0, 4), next_int(0, 1) ? 0 : next_int(1, 70), next_int(1, 512),
-                       next_int(0, 1), next_int(0, 2)};
+                       next_int(0, 1), next_int(0, 3)};
     mla_plan p;
     const bool shard = rep % 4 == 1;
     CHECK(mla::build_plan(batch, H, q.data(), n.data(), shard ? ce.data() : nullptr,
                           rep % 2 ? MLA_KV_FP8_E4M3 : MLA_KV_BF16, &o, &p) == MLA_OK);
-    check_plan(p, q, n, H, shard ? ce.data() : nullptr, o.force_fold);
+    check_plan(p, q, n, H, shard ? ce.data() : nullptr, o.force_fold, o.num_cus, o.merge_mode);
     ++plans;
   }
   // rejected shapes leave no trace

@@ -93,17 +93,41 @@ def test_workspace_size_formula():
     q = plan(H, ql, kl, force_splits=4, merge_mode=mb.MLA_MERGE_LAST_ARRIVER)
     base = -(-(lse_bytes + rows * 512 * 2) // 256) * 256
     assert q.workspace_bytes == base + rows * 8
+    # the grid merge adds one 64-bit counter per launch (256-byte aligned)
+    g = plan(H, ql, kl, force_splits=4, merge_mode=mb.MLA_MERGE_GRID)
+    assert g.launch(0)[1] == mb.MLA_MERGE_GRID
+    assert g.workspace_bytes == base + g.num_launches * 8
 
 
 def test_merge_mode_choice():
-    # AUTO keeps the reduce kernel (no arrival words); LAST_ARRIVER adds them
-    for args in (((96, [1, 2, 3, 4] * 8, [32768] * 32), {}), ((12, [8], [1048576], True), {})):
-        auto = plan(*args[0])
-        red = plan(*args[0], merge_mode=mb.MLA_MERGE_REDUCE)
-        last = plan(*args[0], merge_mode=mb.MLA_MERGE_LAST_ARRIVER)
-        assert auto.workspace_bytes == red.workspace_bytes < last.workspace_bytes
+    # AUTO: the reduce kernel; GRID: where a launch's units fit the CUs at once
+    # (units rounded up to a multiple of 8 <= num_cus)
+    head = plan(12, [8], [1048576], True)
+    units, mode = head.launch(0)
+    assert (units + 7) // 8 * 8 <= 256 and mode == mb.MLA_MERGE_REDUCE
+    for mm, want in ((mb.MLA_MERGE_REDUCE, mb.MLA_MERGE_REDUCE),
+                     (mb.MLA_MERGE_LAST_ARRIVER, mb.MLA_MERGE_LAST_ARRIVER),
+                     (mb.MLA_MERGE_GRID, mb.MLA_MERGE_GRID)):
+        assert plan(12, [8], [1048576], True, merge_mode=mm).launch(0)[1] == want
+    # more units than CUs: no grid merge even when asked for
+    for mm in (mb.MLA_MERGE_AUTO, mb.MLA_MERGE_GRID):
+        p = plan(12, [8], [1048576], True, force_splits=300, merge_mode=mm)
+        assert p.launch(0)[0] > 256 and p.launch(0)[1] == mb.MLA_MERGE_REDUCE
+        assert p.workspace_bytes == plan(12, [8], [1048576], True, force_splits=300,
+                                         merge_mode=mb.MLA_MERGE_REDUCE).workspace_bytes
+    # the same plan for a device with fewer CUs
+    p = plan(12, [8], [1048576], True, num_cus=128, merge_mode=mb.MLA_MERGE_GRID)
+    assert p.launch(0)[1] == (mb.MLA_MERGE_GRID if p.launch(0)[0] <= 128 else mb.MLA_MERGE_REDUCE)
+    # an arrival word counts to 65535: a sequence of more chunks is left to the reduce kernel
+    p = plan(1, [1], [64 * 70000], merge_mode=mb.MLA_MERGE_LAST_ARRIVER, force_splits=70000)
+    assert p.query(0)[2] == 70000 and p.launch(0)[1] == mb.MLA_MERGE_REDUCE
+    # a launch with no split rows reports 0
+    assert plan(12, [2], [4096], force_splits=1).launch(0)[1] == 0
+    for bad in (4, -1):
+        with pytest.raises(mb.MlaError):
+            plan(12, [1], [100], merge_mode=bad)
     with pytest.raises(mb.MlaError):
-        plan(12, [1], [100], merge_mode=3)
+        head.launch(1)
 
 
 def test_many_sequences_use_several_launches():
