@@ -221,26 +221,34 @@ __device__ __forceinline__ unsigned arrive(unsigned long long* w, uint32_t epoch
   return gen;
 }
 
-// Split-KV fold of one split output row over its S chunks, for 64 of the 512
-// value columns (block cb), by 256 threads: thread (part p = tid / 8, column
-// group cg = tid % 8) owns columns 8 cg .. 8 cg + 7 of the block (one 16-byte
-// load per chunk) and folds chunks p, p + 32, ... in ascending order, eight at
-// a time with their loads in flight together, against the running maximum of
-// the LSEs it has read (its sums are rescaled when that maximum moves).  The
-// 32 per-part results are combined in part order through LDS, so the result
-// does not depend on timing.  A chunk that shows the row no key has
-// LSE = -inf and weight 0; a row no chunk shows a key gets O = 0, LSE = -inf.
-// Partial row of chunk s: pbase + s * R.  Every thread of the block calls it;
-// it ends with the LDS free again.
+// Split-KV fold of one split output row over its S chunks, for one block of
+// its 512 value columns, by 256 threads in P chunk phases x G = 256 / P column
+// groups (P = 4, 8, 16 or 32; the block holds C = 8 G columns): thread
+// (part p = tid / G, group cg = tid % G) owns columns 8 cg .. 8 cg + 7 of the
+// block (one 16-byte load per chunk) and folds chunks p, p + P, ... in
+// ascending order, eight at a time with their loads in flight together,
+// against the running maximum of the LSEs it has read (its sums are rescaled
+// when that maximum moves).  The P per-part results are combined in part
+// order through LDS, so the result does not depend on timing.  A chunk that
+// shows the row no key has LSE = -inf and weight 0; a row no chunk shows a key
+// gets O = 0, LSE = -inf.  Partial row of chunk s: pbase + s * R.  Every thread
+// of the block calls it; it ends with the LDS free again.
 constexpr int kFoldThreads = 256;
-constexpr int kFoldCols = 64;                          // value columns per block
-constexpr int kFoldGroups = kFoldCols / 8;             // 8-column groups
-constexpr int kFoldParts = kFoldThreads / kFoldGroups;  // chunk phases per block
-constexpr int kFoldBatch = 8;                          // chunk loads in flight per thread
+constexpr int kFoldBatch = 8;  // chunk loads in flight per thread
+
+// Chunk phases for a launch whose sequences have at most smax chunks: the
+// fewest that keep every thread within one batch of loads (up to 256 chunks).
+// P = 1 is its own layout (fold_cols8: four rows per block, no LDS).
+__host__ __device__ constexpr int fold_parts(int smax) {
+  return smax <= kFoldBatch ? 1 : smax <= 32 ? 4 : smax <= 64 ? 8 : smax <= 128 ? 16 : 32;
+}
+template <int P>
+constexpr int fold_cols() { return 8 * (kFoldThreads / P); }  // value columns per block (P >= 4)
+constexpr int kFoldRowsP1 = kFoldThreads / (kDv / 8);         // rows per block with P = 1
 
 struct FoldLds {
-  f32x4 acc[kFoldParts][kFoldGroups][2];
-  float w[kFoldParts], m[kFoldParts];
+  f32x4 acc[kFoldThreads][2];  // [part * G + group]
+  float w[32], m[32];          // per part
 };
 
 __device__ __forceinline__ float merge_weight(float ls, float M) {
@@ -259,20 +267,22 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4& pk, f32x4& lo, f32x4&
   hi = bf16x4_to_f32(uint2{pk[2], pk[3]});
 }
 
+template <int P>
 __device__ __forceinline__ void fold_split_row(const float* part_lse, const uint16_t* part_o,
                                                int64_t pbase, int S, int R, int cb,
                                                uint16_t* o_row, float* lse_out, FoldLds& lds) {
-  const int part = threadIdx.x / kFoldGroups;
-  const int cg = threadIdx.x % kFoldGroups;
+  constexpr int G = kFoldThreads / P, C = fold_cols<P>();
+  const int part = threadIdx.x / G;
+  const int cg = threadIdx.x % G;
   float m = -INFINITY, W = 0.0f;
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  const uint16_t* po = part_o + kFoldCols * cb + 8 * cg;
-  for (int s0 = part; s0 < S; s0 += kFoldBatch * kFoldParts) {
+  const uint16_t* po = part_o + C * cb + 8 * cg;
+  for (int s0 = part; s0 < S; s0 += kFoldBatch * P) {
     float ls[kFoldBatch];
     u32x4 v[kFoldBatch];
 #pragma unroll
     for (int i = 0; i < kFoldBatch; ++i) {
-      const int s = s0 + i * kFoldParts;
+      const int s = s0 + i * P;
       if (s < S) {
         const int64_t prow = pbase + (int64_t)s * R;
         ls[i] = part_lse[prow];
@@ -301,24 +311,24 @@ __device__ __forceinline__ void fold_split_row(const float* part_lse, const uint
       a1 += w * hi;
     }
   }
-  lds.acc[part][cg][0] = a0;
-  lds.acc[part][cg][1] = a1;
+  lds.acc[threadIdx.x][0] = a0;
+  lds.acc[threadIdx.x][1] = a1;
   if (cg == 0) {
     lds.w[part] = W;
     lds.m[part] = m;
   }
   __syncthreads();
-  if (threadIdx.x < kFoldGroups) {
+  if (threadIdx.x < G) {
     float M = -INFINITY;
 #pragma unroll
-    for (int p = 0; p < kFoldParts; ++p) M = fmaxf(M, lds.m[p]);
+    for (int p = 0; p < P; ++p) M = fmaxf(M, lds.m[p]);
     f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
     float Wt = 0.0f;
 #pragma unroll
-    for (int p = 0; p < kFoldParts; ++p) {
+    for (int p = 0; p < P; ++p) {
       const float f = merge_weight(lds.m[p], M);
-      t0 += f * lds.acc[p][cg][0];
-      t1 += f * lds.acc[p][cg][1];
+      t0 += f * lds.acc[p * G + cg][0];
+      t1 += f * lds.acc[p * G + cg][1];
       Wt += f * lds.w[p];
     }
     const bool empty = !(Wt > 0.0f);  // no chunk shows this row a key
@@ -328,10 +338,77 @@ __device__ __forceinline__ void fold_split_row(const float* part_lse, const uint
     pk[1] = pack_bf16x2(t0[2] * inv, t0[3] * inv);
     pk[2] = pack_bf16x2(t1[0] * inv, t1[1] * inv);
     pk[3] = pack_bf16x2(t1[2] * inv, t1[3] * inv);
-    *(u32x4*)(o_row + kFoldCols * cb + 8 * cg) = pk;
+    *(u32x4*)(o_row + C * cb + 8 * cg) = pk;
     if (lse_out && cg == 0) *lse_out = empty ? -INFINITY : M + __logf(Wt);
   }
   __syncthreads();
+}
+
+// P = 1: one thread folds all S chunks of 8 columns (c8) of one split row in
+// ascending order, eight at a time with their loads in flight together, with
+// the same running-maximum arithmetic as one part above, and writes them.
+__device__ __forceinline__ void fold_cols8(const float* part_lse, const uint16_t* part_o,
+                                           int64_t pbase, int S, int R, int c8, uint16_t* o_row,
+                                           float* lse_out) {
+  float m = -INFINITY, W = 0.0f;
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t* po = part_o + 8 * c8;
+  for (int s0 = 0; s0 < S; s0 += kFoldBatch) {
+    float ls[kFoldBatch];
+    u32x4 v[kFoldBatch];
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) {
+      const int s = s0 + i;
+      if (s < S) {
+        const int64_t prow = pbase + (int64_t)s * R;
+        ls[i] = part_lse[prow];
+        v[i] = *(const u32x4*)(po + prow * kDv);
+      } else {
+        ls[i] = -INFINITY;
+        v[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    float mn = m;
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) mn = fmaxf(mn, ls[i]);
+    const float sc = mn == -INFINITY ? 1.0f : __expf(m - mn);
+    a0 *= sc;
+    a1 *= sc;
+    W *= sc;
+    m = mn;
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) {
+      const float w = merge_weight(ls[i], m);
+      f32x4 lo, hi;
+      bf16x8_to_f32(v[i], lo, hi);
+      W += w;
+      a0 += w * lo;
+      a1 += w * hi;
+    }
+  }
+  const bool empty = !(W > 0.0f);  // no chunk shows this row a key
+  const float inv = empty ? 0.0f : 1.0f / W;
+  u32x4 pk;
+  pk[0] = pack_bf16x2(a0[0] * inv, a0[1] * inv);
+  pk[1] = pack_bf16x2(a0[2] * inv, a0[3] * inv);
+  pk[2] = pack_bf16x2(a1[0] * inv, a1[1] * inv);
+  pk[3] = pack_bf16x2(a1[2] * inv, a1[3] * inv);
+  *(u32x4*)(o_row + 8 * c8) = pk;
+  if (lse_out) *lse_out = empty ? -INFINITY : m + __logf(W);
+}
+
+// fold_split_row with the chunk phases chosen at run time (uniform).
+__device__ __forceinline__ void fold_split_row_p(int P, const float* part_lse, const uint16_t* part_o,
+                                                 int64_t pbase, int S, int R, int cb, uint16_t* o_row,
+                                                 float* lse_out, FoldLds& lds) {
+  if (P == 4)
+    fold_split_row<4>(part_lse, part_o, pbase, S, R, cb, o_row, lse_out, lds);
+  else if (P == 8)
+    fold_split_row<8>(part_lse, part_o, pbase, S, R, cb, o_row, lse_out, lds);
+  else if (P == 16)
+    fold_split_row<16>(part_lse, part_o, pbase, S, R, cb, o_row, lse_out, lds);
+  else
+    fold_split_row<32>(part_lse, part_o, pbase, S, R, cb, o_row, lse_out, lds);
 }
 
 // In-kernel split-KV merge by the last unit of a split row block to finish
@@ -440,10 +517,10 @@ __device__ __forceinline__ void merge_if_last(const MainArgs& args, unsigned cha
 // for it then).  Every workgroup calls it after its unit, with every wave:
 // it makes its partial rows visible device-wide, arrives on the launch's
 // counter and waits for the last arrival; then the workgroups fold the
-// launch's split rows together, workgroup g taking the (split row, 64-column
-// block) items g, g + grid, ... with the fold of the reduce kernel (the same
-// arithmetic in the same order, so the results are the reduce kernel's bit
-// for bit).  The wait is bounded (about a second by the wall clock): a
+// launch's split rows together, workgroup g taking the (split row, column
+// block) items g, g + grid, ... with the fold and layout of the reduce kernel
+// (the same arithmetic in the same order, so the results are the reduce
+// kernel's bit for bit).  The wait is bounded (about a second by the wall clock): a
 // workgroup that gives up writes NaN into the O and LSE of its items instead
 // of folding them, so such a failure shows in the outputs.
 constexpr long long kGridWaitTicks = 100000000;  // wall-clock ticks (100 MHz): 1 s
@@ -476,9 +553,18 @@ __device__ __forceinline__ void merge_grid(const MainArgs& args, unsigned char* 
   const bool ok = *flag != 0u;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every unit's partial rows
   FoldLds& lds = *reinterpret_cast<FoldLds*>(smem + 256);
-  const int items = args.num_split_rows * (kDv / kFoldCols);
+  int smax = 0;  // the reduce kernel's layout rule: chunk phases from the launch's largest S
+  for (int b = 0; b < args.num_seqs; ++b) smax = max(smax, args.seqs[b].S > 1 ? args.seqs[b].S : 0);
+  const int P = fold_parts(smax);
+  // items: (split row, column block) for P >= 4; groups of kFoldRowsP1 rows
+  // (64 threads per row) for P = 1
+  const int C = P == 1 ? kDv : 8 * (kFoldThreads / P), nb = kDv / C;
+  const int items = P == 1 ? (args.num_split_rows + kFoldRowsP1 - 1) / kFoldRowsP1
+                           : args.num_split_rows * nb;
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int gr = item / (kDv / kFoldCols), cb = item % (kDv / kFoldCols);
+    const int gr = P == 1 ? kFoldRowsP1 * item + (int)threadIdx.x / (kDv / 8) : item / nb;
+    const int cb = P == 1 ? 0 : item % nb;
+    if (P == 1 && gr >= args.num_split_rows) continue;  // per thread: no barrier below for P = 1
     int b = 0, row0 = 0;  // the split sequence that holds split row gr
     for (; b < args.num_seqs; ++b) {
       const SeqDesc& d = args.seqs[b];
@@ -493,11 +579,20 @@ __device__ __forceinline__ void merge_grid(const MainArgs& args, unsigned char* 
     const int64_t orow = (int64_t)sd.q_row0 + (int64_t)t * sd.R + r;
     uint16_t* o_row = args.o + orow * kDv;
     float* lse_out = cb == 0 ? args.lse + orow : nullptr;
-    if (ok) {
-      const int64_t pbase = (int64_t)sd.part_row0 + (int64_t)t * sd.S * sd.R + r;
-      fold_split_row(args.part_lse, args.part_o, pbase, sd.S, sd.R, cb, o_row, lse_out, lds);
-    } else if (threadIdx.x < kFoldGroups) {
-      *(u32x4*)(o_row + kFoldCols * cb + 8 * threadIdx.x) = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+    const int64_t pbase = (int64_t)sd.part_row0 + (int64_t)t * sd.S * sd.R + r;
+    if (P == 1) {
+      const int c8 = (int)threadIdx.x % (kDv / 8);
+      float* lse1 = c8 == 0 ? args.lse + orow : nullptr;
+      if (ok) {
+        fold_cols8(args.part_lse, args.part_o, pbase, sd.S, sd.R, c8, o_row, lse1);
+      } else {
+        *(u32x4*)(o_row + 8 * c8) = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+        if (lse1) *lse1 = __builtin_nanf("");
+      }
+    } else if (ok) {
+      fold_split_row_p(P, args.part_lse, args.part_o, pbase, sd.S, sd.R, cb, o_row, lse_out, lds);
+    } else if (threadIdx.x < C / 8) {
+      *(u32x4*)(o_row + C * cb + 8 * threadIdx.x) = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
       if (lse_out && threadIdx.x == 0) *lse_out = __builtin_nanf("");
     }
   }

@@ -1707,6 +1707,50 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_main(const MainArgs ar
 
 #ifndef MLA_PAGED_KV  // the merges are built once, with the contiguous-KV kernels
 
+// Split-KV merge: one 256-thread block per (split output row, block of
+// fold_cols<P>() value columns), folded by fold_split_row<P> (the fold the
+// grid merge of the main kernels also runs, with the same layout rule, so
+// that the two give the same bits).  P = fold_parts(largest S of the launch).
+template <int P>
+__global__ __launch_bounds__(kFoldThreads) void mla_decode_reduce_kernel(const ReduceArgs args) {
+  __shared__ FoldLds lds;
+  constexpr int kBlocksPerRow = kDv / fold_cols<P>();
+  const int gr = blockIdx.x / kBlocksPerRow;
+  const int cb = blockIdx.x % kBlocksPerRow;
+  if (gr >= args.num_rows) return;
+  int b = 0;
+  while (b + 1 < args.num_seqs && args.row0[b + 1] <= gr) ++b;
+  const SeqDesc& sd = args.seqs[b];
+  const int local = gr - args.row0[b];
+  const int R = sd.R;
+  const int t = local / R;
+  const int r = local % R;
+  const int64_t pbase = (int64_t)sd.part_row0 + (int64_t)t * sd.S * R + r;
+  const int64_t orow = (int64_t)sd.q_row0 + (int64_t)t * R + r;
+  fold_split_row<P>(args.part_lse, args.part_o, pbase, sd.S, R, cb, args.o + orow * kDv,
+                    cb == 0 ? args.lse + orow : nullptr, lds);
+}
+
+// Split-KV merge of launches whose sequences have at most 8 chunks (P = 1):
+// kFoldRowsP1 split rows per block, 64 threads per row, each thread folding
+// all chunks of 8 columns (fold_cols8).
+__global__ __launch_bounds__(kFoldThreads) void mla_decode_reduce_rows_kernel(const ReduceArgs args) {
+  const int gr = blockIdx.x * kFoldRowsP1 + (int)threadIdx.x / (kDv / 8);
+  const int c8 = (int)threadIdx.x % (kDv / 8);
+  if (gr >= args.num_rows) return;
+  int b = 0;
+  while (b + 1 < args.num_seqs && args.row0[b + 1] <= gr) ++b;
+  const SeqDesc& sd = args.seqs[b];
+  const int local = gr - args.row0[b];
+  const int R = sd.R;
+  const int t = local / R;
+  const int r = local % R;
+  const int64_t pbase = (int64_t)sd.part_row0 + (int64_t)t * sd.S * R + r;
+  const int64_t orow = (int64_t)sd.q_row0 + (int64_t)t * R + r;
+  fold_cols8(args.part_lse, args.part_o, pbase, sd.S, R, c8, args.o + orow * kDv,
+             c8 == 0 ? args.lse + orow : nullptr);
+}
+
 // Merge layout of the shard merge below: one 256-thread block per (output
 // row, 64 of the 512 value columns); thread (part p, column group cg) owns
 // columns 4 cg .. 4 cg + 3 of the block and folds inputs s = 16 i + p in
@@ -1744,87 +1788,6 @@ __device__ __forceinline__ void merge_finish(f32x4 (&red_acc)[kRedParts][kRedGro
   if (lse_writer) *lse_row = empty ? -INFINITY : M + __logf(Wt);
 }
 
-// Split-KV merge for many chunks: one 256-thread block per (split output
-// row, 64 of the 512 value columns), folded by fold_split_row (the fold the
-// grid merge of the main kernels also runs, in the same order).
-static_assert(kFoldThreads == kRedThreads, "the fold runs on the reduce block");
-
-__global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_kernel(const ReduceArgs args) {
-  __shared__ FoldLds lds;
-  constexpr int kBlocksPerRow = kDv / kFoldCols;
-  const int gr = blockIdx.x / kBlocksPerRow;
-  const int cb = blockIdx.x % kBlocksPerRow;
-  if (gr >= args.num_rows) return;
-  int b = 0;
-  while (b + 1 < args.num_seqs && args.row0[b + 1] <= gr) ++b;
-  const SeqDesc& sd = args.seqs[b];
-  const int local = gr - args.row0[b];
-  const int R = sd.R;
-  const int t = local / R;
-  const int r = local % R;
-  const int64_t pbase = (int64_t)sd.part_row0 + (int64_t)t * sd.S * R + r;
-  const int64_t orow = (int64_t)sd.q_row0 + (int64_t)t * R + r;
-  fold_split_row(args.part_lse, args.part_o, pbase, sd.S, R, cb, args.o + orow * kDv,
-                 cb == 0 ? args.lse + orow : nullptr, lds);
-}
-
-// Split-KV merge for launches whose sequences have few chunks (S <= 16, e.g.
-// many tiles of short sequences): the wide layout above would leave most of
-// its 16 parts idle and launch 8 blocks per row.  Here one thread owns 4
-// columns of one row (128 threads per row, 2 rows per block) and folds the
-// row's S chunks itself in ascending order, its loads in flight together.
-constexpr int kRedSmallMaxS = 16;
-
-__global__ __launch_bounds__(kRedThreads) void mla_decode_reduce_small_kernel(const ReduceArgs args) {
-  constexpr int kThreadsPerRow = kDv / 4;
-  const int gr = blockIdx.x * (kRedThreads / kThreadsPerRow) + threadIdx.x / kThreadsPerRow;
-  if (gr >= args.num_rows) return;
-  int b = 0;
-  while (b + 1 < args.num_seqs && args.row0[b + 1] <= gr) ++b;
-  const SeqDesc& sd = args.seqs[b];
-  const int local = gr - args.row0[b];
-  const int R = sd.R;
-  const int t = local / R;
-  const int r = local % R;
-  const int S = sd.S;
-  const int64_t pbase = (int64_t)sd.part_row0 + (int64_t)t * S * R + r;
-  const int cg = threadIdx.x % kThreadsPerRow;
-
-  float ls[kRedSmallMaxS];
-  f32x4 v[kRedSmallMaxS];
-  float M = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < kRedSmallMaxS; ++s) {
-    if (s < S) {
-      const int64_t prow = pbase + (int64_t)s * R;
-      ls[s] = args.part_lse[prow];
-      v[s] = bf16x4_to_f32(*(const uint2*)(args.part_o + prow * kDv + 4 * cg));
-      M = fmaxf(M, ls[s]);
-    }
-  }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float W = 0.0f;
-#pragma unroll
-  for (int s = 0; s < kRedSmallMaxS; ++s) {
-    if (s < S) {
-      const float w = merge_weight(ls[s], M);
-      W += w;
-      acc += w * v[s];
-    }
-  }
-  const bool empty = !(W > 0.0f);  // no chunk shows this row a key
-  const float inv = empty ? 0.0f : 1.0f / W;
-  const int64_t orow = (int64_t)sd.q_row0 + (int64_t)t * R + r;
-  uint2 pk;
-  pk.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  pk.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  *(uint2*)(args.o + orow * kDv + 4 * cg) = pk;
-  if (cg == 0) args.lse[orow] = empty ? -INFINITY : M + __logf(W);
-}
-
-// Combination of per-shard results (bf16 O, fp32 LSE) with the layout and the
-// fixed order of the split-KV merge above (shards in place of chunks); a
-// shard whose LSE is -inf is skipped without reading its O.
 __global__ __launch_bounds__(kRedThreads) void mla_merge_shards_kernel(const MergeArgs args) {
   __shared__ f32x4 red_acc[kRedParts][kRedGroups];
   __shared__ float red_w[kRedParts];
@@ -1897,13 +1860,27 @@ hipError_t launch_main_contiguous(const MainArgs& a, int nrt, hipStream_t stream
 #ifndef MLA_PAGED_KV
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
   if (a.num_rows == 0) return hipSuccess;
-  if (a.max_splits <= kRedSmallMaxS) {
-    constexpr int kRowsPerBlock = kRedThreads / (kDv / 4);
-    const int grid = (a.num_rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL(mla_decode_reduce_small_kernel, dim3(grid), dim3(kRedThreads), 0, stream, a);
-  } else {
-    const int grid = (kDv / kFoldCols) * a.num_rows;
-    hipLaunchKernelGGL(mla_decode_reduce_kernel, dim3(grid), dim3(kRedThreads), 0, stream, a);
+  switch (fold_parts(a.max_splits)) {
+    case 1:
+      hipLaunchKernelGGL(mla_decode_reduce_rows_kernel, dim3((a.num_rows + kFoldRowsP1 - 1) / kFoldRowsP1),
+                         dim3(kFoldThreads), 0, stream, a);
+      break;
+    case 4:
+      hipLaunchKernelGGL(mla_decode_reduce_kernel<4>, dim3((kDv / fold_cols<4>()) * a.num_rows),
+                         dim3(kFoldThreads), 0, stream, a);
+      break;
+    case 8:
+      hipLaunchKernelGGL(mla_decode_reduce_kernel<8>, dim3((kDv / fold_cols<8>()) * a.num_rows),
+                         dim3(kFoldThreads), 0, stream, a);
+      break;
+    case 16:
+      hipLaunchKernelGGL(mla_decode_reduce_kernel<16>, dim3((kDv / fold_cols<16>()) * a.num_rows),
+                         dim3(kFoldThreads), 0, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL(mla_decode_reduce_kernel<32>, dim3((kDv / fold_cols<32>()) * a.num_rows),
+                         dim3(kFoldThreads), 0, stream, a);
+      break;
   }
   return hipGetLastError();
 }

@@ -117,23 +117,24 @@ def test_replay_is_bitwise_deterministic(fp8):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-def test_both_merge_layouts_vs_oracle(fp8):
-    """The split-KV merge has a per-thread layout for launches whose sequences
-    have at most 16 chunks and a 16-part layout beyond that: 1088 keys give 9
-    chunks with force_splits=16 (128-key chunks) and 17 with force_splits=17
-    (64-key chunks); a batch mixes sequences of both kinds in one launch."""
-    inp = gen.random_inputs(12, [8], [1088], fp8, seed=41)
+def test_every_merge_layout_vs_oracle(fp8):
+    """The split-KV merge folds a launch's rows in P = 1, 4, 8, 16 or 32 chunk
+    phases (the fewest that keep each thread within one batch of 8 loads up to
+    256 chunks; past that each thread loops): chunk counts on both sides of
+    each switch and one past 256 (64-key chunks: kv_len = 64 S), then a launch
+    that mixes a short and a long sequence (the longest sets the layout)."""
+    for S in (2, 8, 9, 32, 33, 64, 65, 128, 129, 300):
+        gu.log(f"merge layout S={S} fp8={fp8}")
+        inp = gen.random_inputs(4, [2], [64 * S], fp8, seed=41 + S)
+        ro, rl = gu.oracle_full(inp)
+        o, lse, plan = gu.run_gpu(inp, force_splits=S)
+        assert plan.query(0)[2] == S
+        gu.compare(o, lse, ro, rl, fp8, f"S={S}")
+    inp = gen.random_inputs(24, [1, 4, 2], [320, 70, 12800], fp8, seed=43)
     ro, rl = gu.oracle_full(inp)
-    for splits, want in ((16, 9), (17, 17)):
-        o, lse, plan = gu.run_gpu(inp, force_splits=splits)
-        assert plan.query(0)[2] == want
-        gu.compare(o, lse, ro, rl, fp8, f"splits={splits} S_eff={want}")
-    inp = gen.random_inputs(24, [1, 4, 2], [3000, 70, 1500], fp8, seed=43)
-    ro, rl = gu.oracle_full(inp)
-    for splits in (8, 40):  # every sequence at <= 16 chunks; some beyond 16
-        o, lse, plan = gu.run_gpu(inp, force_splits=splits)
-        gu.compare(o, lse, ro, rl, fp8,
-                   f"mixed chunk counts S_eff={[plan.query(b)[2] for b in range(3)]}")
+    o, lse, plan = gu.run_gpu(inp, force_splits=200)
+    assert [plan.query(b)[2] for b in range(3)] == [5, 2, 200]
+    gu.compare(o, lse, ro, rl, fp8, "mixed chunk counts 5, 2, 200")
 
 
 @pytest.mark.parametrize("beta", [1.0, 2.0, 3.0])
