@@ -3,8 +3,10 @@
     python -m mla_token_decode_amd.build
 
 Compiles the host plan, the C ABI and the HIP kernels into one shared library
-next to this file.  Packed-fp32 instruction selection is disabled on purpose
-(`-target-feature -packed-fp32-ops`): the kernels never rely on it.
+next to this file, and the cold read-stream probe (stream_read.hip) into
+libmla_stream.so, which only the benchmark loads.  Packed-fp32 instruction
+selection is disabled on purpose (`-target-feature -packed-fp32-ops`): the
+kernels never rely on it.
 """
 from __future__ import annotations
 
@@ -17,6 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmla_decode.so")
+STREAM_LIB = os.path.join(HERE, "libmla_stream.so")
+STREAM_SOURCE = "stream_read.hip"
 SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "kernels_paged.hip", "fp8_decode.hip",
            "fp8_decode_paged.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -41,6 +45,11 @@ def build(verbose: bool = False) -> str:
                 print(" ".join(cmd), flush=True)
             objs.append(obj)
             procs.append((cmd, subprocess.Popen(cmd)))
+        stmp = STREAM_LIB + f".tmp{os.getpid()}"
+        cmd = [HIPCC, *compile_flags(), "-shared", "-o", stmp, os.path.join(CSRC, STREAM_SOURCE)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd)))
         for cmd, p in procs:
             if p.wait() != 0:
                 raise subprocess.CalledProcessError(p.returncode, cmd)
@@ -50,6 +59,7 @@ def build(verbose: bool = False) -> str:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    os.replace(stmp, STREAM_LIB)
     return LIB
 
 
