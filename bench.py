@@ -309,42 +309,44 @@ def cpu_baseline(head_inp, other_inps):
 STREAM_LIB = os.path.join(ROOT, "mla_token_decode_amd", "libmla_stream.so")
 
 
-def read_ceiling(flush, nbytes, reps=10):
+def read_ceiling(flush, nbytes, reps=8):
     """Cold read-stream ceiling: the plain streaming read of
-    csrc/stream_read.hip (16-byte words, 8 loads in flight per lane) over
-    nbytes of device memory, the caches flushed before every timed launch,
-    HIP events around the launch (as for the decode kernels); the median of
-    `reps` launches, best over 1024 .. 8192 workgroups."""
+    csrc/stream_read.hip (16-byte non-temporal loads, 8 in flight per lane) over
+    nbytes of device memory, the caches flushed before every timed launch, HIP
+    events around the launch (as for the decode kernels); the median of `reps`
+    launches, best over both layouts and 256 .. 8192 workgroups."""
     import ctypes
     import torch
     lib = ctypes.CDLL(STREAM_LIB)
     lib.mla_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
-                                    ctypes.c_void_p]
+                                    ctypes.c_int, ctypes.c_void_p]
     lib.mla_stream_read.restype = ctypes.c_int
     nbytes -= nbytes % 16
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
     best = None
-    for blocks in (1024, 2048, 4096, 8192):
-        def run():
-            rc = lib.mla_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream.cuda_stream)
-            if rc != 0:
-                raise RuntimeError(f"mla_stream_read failed ({rc})")
-        for _ in range(2):
-            flush()
-            run()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-        for k in range(reps):
-            flush()
-            ev[k][0].record(stream)
-            run()
-            ev[k][1].record(stream)
-        torch.cuda.synchronize()
-        us = float(np.median([ev[k][0].elapsed_time(ev[k][1]) for k in range(reps)]) * 1e3)
-        gbps = nbytes / (us * 1e-6) / 1e9
-        if best is None or gbps > best["gbps"]:
-            best = {"gbps": gbps, "blocks": blocks, "us": us, "bytes": nbytes}
+    for layout in (0, 1):
+        for blocks in (256, 512, 1024, 2048, 4096, 8192):
+            def run():
+                rc = lib.mla_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, layout,
+                                         stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"mla_stream_read failed ({rc})")
+            for _ in range(2):
+                flush()
+                run()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+            for k in range(reps):
+                flush()
+                ev[k][0].record(stream)
+                run()
+                ev[k][1].record(stream)
+            torch.cuda.synchronize()
+            us = float(np.median([ev[k][0].elapsed_time(ev[k][1]) for k in range(reps)]) * 1e3)
+            gbps = nbytes / (us * 1e-6) / 1e9
+            if best is None or gbps > best["gbps"]:
+                best = {"gbps": gbps, "blocks": blocks, "layout": layout, "us": us, "bytes": nbytes}
     del buf
     return best
 
@@ -419,7 +421,7 @@ def main():
     ceiling = read_ceiling(flush, int(inp.kv.nbytes))
     read_stream_gbps = ceiling["gbps"]
     log(f"cold read stream over {ceiling['bytes']} bytes: {read_stream_gbps:.0f} GB/s "
-        f"({ceiling['blocks']} workgroups, {ceiling['us']:.1f} us)")
+        f"({ceiling['blocks']} workgroups, layout {ceiling['layout']}, {ceiling['us']:.1f} us)")
     log("timing headline")
     head = measure(inp, dev, **meas)
     log(f"  {head}")
@@ -512,7 +514,8 @@ def main():
                    "clocks": {"before": head["clocks_before"], "after": head["clocks_after"]},
                    "read_stream_gbps": round(read_stream_gbps, 1),
                    "read_stream": "cold plain streaming read of the headline's KV size "
-                                  "(csrc/stream_read.hip), events, median, best grid",
+                                  "(csrc/stream_read.hip, non-temporal 16-byte loads), events, "
+                                  "median, best of 2 layouts x 6 grid sizes",
                    "frac_of_read_stream": round(head["kv_gbps"] / read_stream_gbps, 4),
                    "context_pages_b300_us": PAGES_FP8_1M_US_B300,
                    "us_per_call_after_dirty_flush": round(dirty, 2) if dirty else None},
