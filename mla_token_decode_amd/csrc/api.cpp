@@ -15,10 +15,11 @@
 
 namespace mla {
 const char* last_error();
-hipError_t launch_main_contiguous(const MainArgs& a, int nrt, hipStream_t stream);  // bf16 KV
-hipError_t launch_main_paged(const MainArgs& a, int nrt, hipStream_t stream);       // bf16 KV
-hipError_t launch_fp8_contiguous(const MainArgs& a, int nrt, hipStream_t stream);
-hipError_t launch_fp8_paged(const MainArgs& a, int nrt, hipStream_t stream);
+// nt: load the KV with the non-temporal hint (Launch::kv_nt)
+hipError_t launch_main_contiguous(const MainArgs& a, int nrt, bool nt, hipStream_t stream);  // bf16 KV
+hipError_t launch_main_paged(const MainArgs& a, int nrt, bool nt, hipStream_t stream);       // bf16 KV
+hipError_t launch_fp8_contiguous(const MainArgs& a, int nrt, bool nt, hipStream_t stream);
+hipError_t launch_fp8_paged(const MainArgs& a, int nrt, bool nt, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t static_scratch(void** ptr);
@@ -289,9 +290,11 @@ mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const
     a.page_table = page_table;  // a sequence's row is its SeqDesc::src (the caller's index)
     for (int b = ln.seq_begin; b < ln.seq_end; ++b) a.seqs[b - ln.seq_begin] = plan->seqs[b];
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = fp8 ? (page_table ? launch_fp8_paged(a, ln.nrt, s) : launch_fp8_contiguous(a, ln.nrt, s))
-                       : (page_table ? launch_main_paged(a, ln.nrt, s)
-                                     : launch_main_contiguous(a, ln.nrt, s));
+    const bool nt = ln.kv_nt;
+    hipError_t e = fp8 ? (page_table ? launch_fp8_paged(a, ln.nrt, nt, s)
+                                     : launch_fp8_contiguous(a, ln.nrt, nt, s))
+                       : (page_table ? launch_main_paged(a, ln.nrt, nt, s)
+                                     : launch_main_contiguous(a, ln.nrt, nt, s));
     if (e != hipSuccess) {
       set_error("main kernel launch failed: %s", hipGetErrorString(e));
       return MLA_ERR_DEVICE;

@@ -133,9 +133,11 @@ __device__ __forceinline__ void fetch_now(const Src<PAGED>& src, int t, int (&e)
 // lanes fill the 1 KB at `dst` (lane i at dst + 16 i) from their own offsets
 // into the descriptor's range (bytes past the range read as zero).  Counted
 // by vmcnt; the compiler does not see it, so every wait for it is explicit.
-// NT: the non-temporal hint, for the KV tiles (each byte is read once; the
-// cold streaming read measured 8-15 % faster with it); Q rows, which every
-// CU reads, keep the default policy.
+// NT: the non-temporal hint, for the KV tiles of launches in which no KV
+// chunk is read by two units (each byte is then read once; a cold streaming
+// read measured 8-15 % faster with it; where several units read one chunk the
+// hint would make each re-read HBM); Q rows, which every CU reads, keep the
+// default policy.
 template <bool NT = false>
 __device__ __forceinline__ void dma16(const lds_u8* dst, int voff, __amdgpu_buffer_rsrc_t r) {
   const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
@@ -170,7 +172,7 @@ __device__ __forceinline__ DmaLanes dma_lanes(int tid) {
 // between its MFMAs.  One descriptor per 32-key half, its range the half's
 // rows in the chunk (the range check on the lane offsets zero-fills the
 // rest).  e: page-table entries of the tile's halves (paged).
-template <bool PAGED>
+template <bool PAGED, bool NT>
 struct TileLoads {
   __amdgpu_buffer_rsrc_t r[2];
   lds_u8* slot;
@@ -186,16 +188,16 @@ struct TileLoads {
   template <int K>
   __device__ __forceinline__ void issue(const DmaLanes& dl, int wave) const {
     if constexpr (K < 8) {  // keys 8 (K % 4) .. + 7 of half K / 4
-      dma16<true>(slot + 4096 * K + 1024 * wave, dl.lat[K & 3], r[K >> 2]);
+      dma16<NT>(slot + 4096 * K + 1024 * wave, dl.lat[K & 3], r[K >> 2]);
     } else {  // rope keys of this wave: 16 wave .. 16 wave + 15
-      dma16<true>(slot + kRopeOff + 1024 * wave, dl.rope, wave >= 2 ? r[1] : r[0]);
+      dma16<NT>(slot + kRopeOff + 1024 * wave, dl.rope, wave >= 2 ? r[1] : r[0]);
     }
   }
 };
-template <bool PAGED>
+template <bool PAGED, bool NT>
 __device__ __forceinline__ void issue_tile(const Src<PAGED>& src, int t, const int (&e)[2],
                                            lds_u8* slot, const DmaLanes& dl, int wave) {
-  const TileLoads<PAGED> tl(src, t, e, slot);
+  const TileLoads<PAGED, NT> tl(src, t, e, slot);
   static_for<9>([&](auto kc) { tl.template issue<decltype(kc)::value>(dl, wave); });
 }
 
@@ -583,7 +585,7 @@ __device__ __forceinline__ void move_references(f32x4 (&S)[2][N], Soft<N>& sm, i
 
 // ------------------------------------------------------------------ unit
 
-template <int N, bool PAGED>
+template <int N, bool PAGED, bool NT>
 __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* smem) {
   UnitSetup us;
   if (!unit_setup<kRowB, kKeys>(args, us)) return;
@@ -633,7 +635,7 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
 #pragma unroll
     for (int k = 0; k < kEarly; ++k) {
       fetch_now(src, k, e);
-      issue_tile(src, k, e, lds + k * kTileB, dl, wave);
+      issue_tile<PAGED, NT>(src, k, e, lds + k * kTileB, dl, wave);
     }
     wait_q<q_dma_loads<N>() + 9 * kEarly>(raw);
     quantise_q<N, 0>(us, raw, g, qf, sm.c[0]);
@@ -649,7 +651,7 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
       });
       lds_barrier();  // the Q rows are read before tile 2 overwrites slot 2
       fetch_now(src, 2, e);
-      issue_tile(src, 2, e, lds + 2 * kTileB, dl, wave);
+      issue_tile<PAGED, NT>(src, 2, e, lds + 2 * kTileB, dl, wave);
     }
   }
   {
@@ -729,7 +731,7 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
     i32x8 k0;
     if constexpr (MORE) k0 = read_k<0, 0>(lds + ((t + 1) % kSlots) * kTileB, kb_);
     // tile t + 3 goes into the slot of tile t - 1 (read by the last PV)
-    const TileLoads<PAGED> tl(src, t + 3, e, lds + ((t + 3) % kSlots) * kTileB);
+    const TileLoads<PAGED, NT> tl(src, t + 3, e, lds + ((t + 3) % kSlots) * kTileB);
     if (__builtin_amdgcn_readfirstlane((fl[0] | fl[1]) | (fl[2] | fl[3])) != 0) {
       move_references<N>(S, sm, kKeys * t + 32 * kh + 4 * g, kKeys * t + kKeys - 1 > us.uc.min_lim,
                          t == 0, lds, pbuf_t, pb, kh, rh, lane);
@@ -879,10 +881,10 @@ __device__ __forceinline__ void unit_fp8(const MainArgs& args, unsigned char* sm
   }
 }
 
-template <int N, bool PAGED>
+template <int N, bool PAGED, bool NT>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8(const MainArgs args) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsBytes];
-  unit_fp8<N, PAGED>(args, smem);
+  unit_fp8<N, PAGED, NT>(args, smem);
   merge_if_last(args, smem);
   merge_grid(args, smem);
 }
@@ -890,25 +892,31 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8(const MainArgs arg
 }  // namespace fp8k
 
 // Launch of the fp8-KV main kernel over a launch's units; nrt = 16-row blocks
-// per row half of the widest unit (1..3).
+// per row half of the widest unit (1..3); nt: the non-temporal KV hint.
+template <bool PAGED, bool NT>
+static hipError_t launch_fp8_t(const MainArgs& a, int nrt, int grid, hipStream_t stream) {
+  if (nrt == 1)
+    hipLaunchKernelGGL((fp8k::mla_decode_fp8<1, PAGED, NT>), dim3(grid), dim3(fp8k::kThreads), 0, stream, a);
+  else if (nrt == 2)
+    hipLaunchKernelGGL((fp8k::mla_decode_fp8<2, PAGED, NT>), dim3(grid), dim3(fp8k::kThreads), 0, stream, a);
+  else if (nrt == 3)
+    hipLaunchKernelGGL((fp8k::mla_decode_fp8<3, PAGED, NT>), dim3(grid), dim3(fp8k::kThreads), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 #ifdef MLA_PAGED_KV
-hipError_t launch_fp8_paged(const MainArgs& a, int nrt, hipStream_t stream) {
+hipError_t launch_fp8_paged(const MainArgs& a, int nrt, bool nt, hipStream_t stream) {
   constexpr bool kPaged = true;
 #else
-hipError_t launch_fp8_contiguous(const MainArgs& a, int nrt, hipStream_t stream) {
+hipError_t launch_fp8_contiguous(const MainArgs& a, int nrt, bool nt, hipStream_t stream) {
   constexpr bool kPaged = false;
 #endif
   const int grid = ((a.num_units + kNumXcd - 1) / kNumXcd) * kNumXcd;
   if (grid == 0) return hipSuccess;
-  if (nrt == 1)
-    hipLaunchKernelGGL((fp8k::mla_decode_fp8<1, kPaged>), dim3(grid), dim3(fp8k::kThreads), 0, stream, a);
-  else if (nrt == 2)
-    hipLaunchKernelGGL((fp8k::mla_decode_fp8<2, kPaged>), dim3(grid), dim3(fp8k::kThreads), 0, stream, a);
-  else if (nrt == 3)
-    hipLaunchKernelGGL((fp8k::mla_decode_fp8<3, kPaged>), dim3(grid), dim3(fp8k::kThreads), 0, stream, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  return nt ? launch_fp8_t<kPaged, true>(a, nrt, grid, stream)
+            : launch_fp8_t<kPaged, false>(a, nrt, grid, stream);
 }
 
 }  // namespace mla

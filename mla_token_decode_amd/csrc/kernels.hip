@@ -127,7 +127,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* kv_un
 // fp8: pieces 0..7 are latent (key tid/64 + 4 M, bytes 8 (tid % 64) ..), piece 8
 // is rope (key tid/8, bytes 512 + 8 (tid % 8) ..).  bf16: piece M is the 16
 // bytes at 16 tid + 4096 M of the tile.
-template <bool FP8, int M>
+// NT: the non-temporal hint (bf16 KV), for launches in which no KV chunk is
+// read by two units: each byte is read once, and a cold streaming read
+// measured faster with it.  Where several units read one chunk (the tiles of
+// one sequence on one XCD) the hint would make each re-read HBM.
+template <bool FP8, int M, bool NT = false>
 __device__ __forceinline__ void stage_load_piece(Stage<FP8>& st, __amdgpu_buffer_rsrc_t r, int tid) {
   constexpr int PB = FP8 ? 8 : 16;  // bytes per piece
   const int off = !FP8 ? tid * PB
@@ -137,14 +141,17 @@ __device__ __forceinline__ void stage_load_piece(Stage<FP8>& st, __amdgpu_buffer
   if constexpr (FP8)
     asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen"
                  : "=&v"(st.p[M]) : "v"(off), "s"(r), "s"(soff) : "memory");
-  else  // non-temporal: each KV byte is read once (the cold streaming read measured faster)
+  else if constexpr (NT)
     asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen nt"
+                 : "=&v"(st.p[M]) : "v"(off), "s"(r), "s"(soff) : "memory");
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen"
                  : "=&v"(st.p[M]) : "v"(off), "s"(r), "s"(soff) : "memory");
 }
 
-template <bool FP8>
+template <bool FP8, bool NT = false>
 __device__ __forceinline__ void stage_load(Stage<FP8>& st, __amdgpu_buffer_rsrc_t r, int tid) {
-  static_for<kPieces>([&](auto mc) { stage_load_piece<FP8, decltype(mc)::value>(st, r, tid); });
+  static_for<kPieces>([&](auto mc) { stage_load_piece<FP8, decltype(mc)::value, NT>(st, r, tid); });
 }
 
 // Where a unit's KV tiles live: one contiguous run of rows, or the pages of a
@@ -828,7 +835,7 @@ __device__ __forceinline__ void prologue_page_rows(const KvSource<FP8, PAGED>& s
   for (int k = 0; k < N; ++k) pr[k] = PAGED ? src.page_row_now(k) : 0;
 }
 
-template <bool FP8, int NRT, bool PAGED>
+template <bool FP8, int NRT, bool PAGED, bool NT>
 __device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* lds, int tid) {
   constexpr int NS = stage_sets<FP8, NRT>();
   constexpr int kAhead = (NS - 1) * kPieces;
@@ -839,12 +846,12 @@ __device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* l
   prologue_page_rows(src, pr);
   Stage<FP8> st[NS];
 #pragma unroll
-  for (int k = 0; k < NS; ++k) stage_load<FP8>(st[k], src.rsrc(k, pr[k]), tid);
+  for (int k = 0; k < NS; ++k) stage_load<FP8, NT>(st[k], src.rsrc(k, pr[k]), tid);
   static_for<2>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     wait_stage<kAhead, FP8>(st[j % NS]);
     stage_store<FP8>(st[j % NS], lds + j * tile_bytes<FP8>(), tid);
-    stage_load<FP8>(st[j % NS], src.rsrc(j + NS, pr[j + NS]), tid);
+    stage_load<FP8, NT>(st[j % NS], src.rsrc(j + NS, pr[j + NS]), tid);
   });
   lds_barrier();
   lds_barrier();  // the exchange of tile 0's scores
@@ -857,7 +864,7 @@ __device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* l
       if (t < u.ntiles) {
         wait_stage<kAhead, FP8>(st[ks]);
         stage_store<FP8>(st[ks], lds + ((t + 2) % ring_slots<FP8, NRT>()) * tile_bytes<FP8>(), tid);
-        stage_load<FP8>(st[ks], src.rsrc(t + 2 + NS, prow_next), tid);
+        stage_load<FP8, NT>(st[ks], src.rsrc(t + 2 + NS, prow_next), tid);
         if constexpr (PAGED)
           prow_next = src.barrier_and_page_row(t + 3 + NS);
         else
@@ -874,7 +881,7 @@ __device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* l
 // past the end load nothing), so the staged registers never need a copy while
 // their loads are in flight (the compiler does not know that an
 // inline-assembly load completes later).
-template <bool FP8, int NRT, int DH, bool PAGED, typename FB, typename QT>
+template <bool FP8, int NRT, int DH, bool PAGED, bool NT, typename FB, typename QT>
 __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, float* xs,
                                               int wave, const FB& fb, const QT& qf,
                                               const float (&c)[NRT], f32x4 (&oacc)[16][NRT],
@@ -894,12 +901,12 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
   prologue_page_rows(src, pr);
   Stage<FP8> st[NS];
 #pragma unroll
-  for (int k = 0; k < NS; ++k) stage_load<FP8>(st[k], src.rsrc(k, pr[k]), tid);
+  for (int k = 0; k < NS; ++k) stage_load<FP8, NT>(st[k], src.rsrc(k, pr[k]), tid);
   static_for<2>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     wait_stage<kAhead, FP8>(st[j % NS]);
     stage_store<FP8>(st[j % NS], lds + j * TB, tid);
-    stage_load<FP8>(st[j % NS], src.rsrc(j + NS, pr[j + NS]), tid);
+    stage_load<FP8, NT>(st[j % NS], src.rsrc(j + NS, pr[j + NS]), tid);
   });
   lds_barrier();
   int64_t prow_next = pr[NS + 2];  // page row of the first tile the loop loads
@@ -972,7 +979,7 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
           } else if constexpr (s < 1 + kPieces) {
             stage_store_piece<FP8, s - 1>(st[ks], slot_s, tid);
           } else {
-            stage_load_piece<FP8, s - 1 - kPieces>(st[ks], rs_next, tid);
+            stage_load_piece<FP8, s - 1 - kPieces, NT>(st[ks], rs_next, tid);
           }
         };
 
@@ -1612,7 +1619,7 @@ __device__ __forceinline__ void total_row_sums(float* xs, int wave, float (&l_ru
   for (int rt = 0; rt < NRT; ++rt) l_run[rt] = own[rt] + peer[rt];
 }
 
-template <bool FP8, int NRT, int DH, bool PAGED>
+template <bool FP8, int NRT, int DH, bool PAGED, bool NT>
 __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* smem) {
   UnitSetup us;
   if (!unit_setup<Stage<FP8>::kGlobalRowBytes, kTK>(args, us)) return;
@@ -1649,7 +1656,7 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
         for (int rt = 0; rt < NRT; ++rt) zero_o(oacc[cc][rt]);
     }
     if (!wave_active) {  // a row group with no row of the unit only stages
-      unit_staging_only<FP8, NRT, PAGED>(us, lds, tid);
+      unit_staging_only<FP8, NRT, PAGED, NT>(us, lds, tid);
       if constexpr (key_split<FP8, NRT>()) lds_barrier();  // the other pair's row-sum exchange
       return;
     }
@@ -1659,8 +1666,8 @@ __device__ __forceinline__ void unit_body(const MainArgs& args, unsigned char* s
       total_row_sums<NRT>(xs, wave, l_run);
       epilogue<NRT, DH, true>(us, grow0, l16, g, oacc, m_run, l_run);
     } else {
-      unit_pipeline<FP8, NRT, DH, PAGED>(us, lds, xs, wave, fb, qf, c, oacc, m_run, l_run, lim, tid,
-                                         g, lane);
+      unit_pipeline<FP8, NRT, DH, PAGED, NT>(us, lds, xs, wave, fb, qf, c, oacc, m_run, l_run, lim,
+                                             tid, g, lane);
       epilogue<NRT, DH>(us, grow0, l16, g, oacc, m_run, l_run);
     }
   };
@@ -1691,16 +1698,16 @@ constexpr int main_lds_bytes() {
   return ring_slots<FP8, NRT>() * tile_bytes<FP8>() + exchange_bytes<FP8, NRT>();
 }
 
-// One kernel per (KV dtype, row tiles per row group, KV layout): a kernel holds
-// a single pipeline, so that the register allocation of one layout never
-// constrains the other.
-template <bool FP8, int NRT, bool PAGED>
+// One kernel per (KV dtype, row tiles per row group, KV layout, KV cache
+// hint): a kernel holds a single pipeline, so that the register allocation of
+// one layout never constrains the other.
+template <bool FP8, int NRT, bool PAGED, bool NT>
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_main(const MainArgs args) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[main_lds_bytes<FP8, NRT>()];
   if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1)
-    unit_body<FP8, NRT, 1, PAGED>(args, smem);
+    unit_body<FP8, NRT, 1, PAGED, NT>(args, smem);
   else
-    unit_body<FP8, NRT, 0, PAGED>(args, smem);
+    unit_body<FP8, NRT, 0, PAGED, NT>(args, smem);
   merge_if_last(args, smem);
   merge_grid(args, smem);
 }
@@ -1828,14 +1835,14 @@ __global__ __launch_bounds__(kRedThreads) void mla_merge_shards_kernel(const Mer
 
 // ------------------------------------------------------------- launchers
 
-template <bool FP8, bool PAGED>
+template <bool FP8, bool PAGED, bool NT>
 static void launch_main_t(const MainArgs& a, int nrt, int grid, hipStream_t stream) {
   if (nrt <= 1)
-    hipLaunchKernelGGL((mla_decode_main<FP8, 1, PAGED>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((mla_decode_main<FP8, 1, PAGED, NT>), dim3(grid), dim3(kThreads), 0, stream, a);
   else if (nrt == 2)
-    hipLaunchKernelGGL((mla_decode_main<FP8, 2, PAGED>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((mla_decode_main<FP8, 2, PAGED, NT>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((mla_decode_main<FP8, 3, PAGED>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((mla_decode_main<FP8, 3, PAGED, NT>), dim3(grid), dim3(kThreads), 0, stream, a);
 }
 
 // This file is compiled twice: once for contiguous KV (with the merges) and
@@ -1844,16 +1851,19 @@ static void launch_main_t(const MainArgs& a, int nrt, int grid, hipStream_t stre
 // bf16 KV only: fp8 KV runs the kernel of fp8_decode.hip (this file's fp8
 // template branches are the earlier fp8 kernels, no longer instantiated).
 #ifdef MLA_PAGED_KV
-hipError_t launch_main_paged(const MainArgs& a, int nrt, hipStream_t stream) {
+hipError_t launch_main_paged(const MainArgs& a, int nrt, bool nt, hipStream_t stream) {
   constexpr bool kPaged = true;
 #else
-hipError_t launch_main_contiguous(const MainArgs& a, int nrt, hipStream_t stream) {
+hipError_t launch_main_contiguous(const MainArgs& a, int nrt, bool nt, hipStream_t stream) {
   constexpr bool kPaged = false;
 #endif
   const int grid = ((a.num_units + kNumXcd - 1) / kNumXcd) * kNumXcd;
   if (grid == 0) return hipSuccess;
   if (nrt < 1 || nrt > 3) return hipErrorInvalidValue;
-  launch_main_t<false, kPaged>(a, nrt, grid, stream);
+  if (nt)
+    launch_main_t<false, kPaged, true>(a, nrt, grid, stream);
+  else
+    launch_main_t<false, kPaged, false>(a, nrt, grid, stream);
   return hipGetLastError();
 }
 

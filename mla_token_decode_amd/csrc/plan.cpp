@@ -404,11 +404,13 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
     ln.seq_end = std::min(batch, b0 + kMaxSeqPerLaunch);
     int64_t units = 0;
     int maxRU = 0, split_rows = 0, max_s = 0;
+    bool shared_chunks = false;  // some chunk is read by more than one unit (tiles or row blocks)
     for (int b = ln.seq_begin; b < ln.seq_end; ++b) {
       SeqDesc& d = plan->seqs[b];
       d.unit0 = static_cast<int32_t>(units);
       units += static_cast<int64_t>(d.T) * d.NRB * d.S;
       maxRU = std::max(maxRU, std::min(d.RBS, d.R));
+      shared_chunks = shared_chunks || d.T * d.NRB > 1;
       if (d.S > 1) {
         split_rows += d.T * d.R;
         max_s = std::max(max_s, d.S);
@@ -431,6 +433,10 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
       set_error("too many work units (%lld)", static_cast<long long>(units));
       return MLA_ERR_INVALID_ARGUMENT;
     }
+    // The non-temporal hint keeps KV lines out of the caches: right when every
+    // chunk is read once; where the tiles of a sequence share chunks (one
+    // XCD's L2 serves the rereads) it would send each reread to HBM.
+    ln.kv_nt = !shared_chunks;
     ln.num_units = static_cast<int>(units);
     ln.nrt = ((maxRU + 1) / 2 + 15) / 16;
     ln.num_split_rows = split_rows;

@@ -100,6 +100,7 @@ struct Launch {
   int nrt;                 // 16-row MFMA tiles per row group (1..3), from the widest unit
   int num_split_rows;      // rows merged for this slice (by the reduce or in the kernel)
   int merge;               // MergeKind of this slice's split rows
+  bool kv_nt;              // no KV chunk is read by two units: load KV with the non-temporal hint
 };
 
 // Who merges a launch's split rows: the reduce kernel (mla_decode_reduce),

@@ -106,6 +106,9 @@ static void check_plan(const mla_plan& p, const std::vector<int32_t>& q, const s
         want = mla::kMergeGrid;
     }
     CHECK(ln.merge == want);
+    bool shared = false;  // a chunk read by two units: no non-temporal KV hint
+    for (int i = ln.seq_begin; i < ln.seq_end; ++i) shared = shared || p.seqs[i].T * p.seqs[i].NRB > 1;
+    CHECK(ln.kv_nt == !shared);
     CHECK(ln.seq_begin == covered && ln.seq_end > ln.seq_begin);
     CHECK(ln.seq_end - ln.seq_begin <= mla::kMaxSeqPerLaunch);
     CHECK(ln.nrt >= 1 && ln.nrt <= 3);

@@ -39,9 +39,10 @@ def kernels(assembly):
     ks = {}
     for name in ("kernels", "kernels_paged"):  # contiguous and paged KV
         part = asm_scan.kernels(assembly[name])
-        assert len(part) == 3, sorted(part)  # bf16 KV, 16 / 32 / 48 rows per row group
+        # bf16 KV, 16 / 32 / 48 rows per row group, with and without the non-temporal KV hint
+        assert len(part) == 6, sorted(part)
         ks.update(part)
-    assert len(ks) == 6, sorted(ks)
+    assert len(ks) == 12, sorted(ks)
     return ks
 
 
@@ -50,9 +51,9 @@ def fp8_kernels(assembly):
     ks = {}
     for name in ("fp8_decode", "fp8_decode_paged"):
         part = asm_scan.kernels(assembly[name], asm_scan.FP8_KERNEL)
-        assert len(part) == 3, sorted(part)  # 32, 64, 96 rows per unit
+        assert len(part) == 6, sorted(part)  # 32, 64, 96 rows per unit; two KV hints
         ks.update(part)
-    assert len(ks) == 6, sorted(ks)
+    assert len(ks) == 12, sorted(ks)
     return ks
 
 
