@@ -216,6 +216,59 @@ __device__ __forceinline__ void wait_stage(Stage<FP8>& st) {
                : "memory");
 }
 
+// Which bf16 kernels move KV tiles by LDS DMA: those of 48-row row groups.
+// With three ring slots a DMA is issued one iteration ahead of its tile, the
+// lead that one register staging set gives, and 48-row groups only have room
+// for one set; DMA frees those registers and the LDS stores (same process:
+// h96_125k main 218 -> 212 us, ragged 557-562 -> 544, bf16 1M q = 8 246 ->
+// 236).  Narrower row groups keep two staging sets, two tiles ahead, which
+// the HBM-bound rows need (bf16 1M q = 1 with DMA: 195-197 -> 202 us).
+template <bool FP8, int NRT>
+constexpr bool tile_dma_path() { return !FP8 && NRT == 3; }
+
+// bf16 KV tiles reach their LDS slot by DMA (buffer_load_dwordx4 ... lds, no
+// staging registers): the 36 KB of a 32-key tile as 36 blocks of 1 KB, wave w
+// issuing blocks J = 4 j + w (j = 0..8).  Lane i of block J fills LDS chunk
+// P = 64 J + i of the slot: key P / 72, physical chunk P % 72, which holds
+// logical chunk (P % 72) ^ swz(key) (the layout stage_store_piece writes; the
+// XOR stays inside each group of 8 chunks), read from the tile's global
+// offset 1152 key + 16 logical.  Keys past the tile's rows read as zero.
+struct TileDma {
+  int off[kPieces];  // per-lane global offsets of blocks 4 j + w, j = 0..8, within a tile
+};
+__device__ __forceinline__ TileDma tile_dma(int wave, int lane) {
+  TileDma d;
+#pragma unroll
+  for (int j = 0; j < kPieces; ++j) {
+    const int P = 64 * (4 * j + wave) + lane;
+    const int key = P / kChunks, ph = P - key * kChunks;
+    d.off[j] = key * kRowBytes + 16 * (ph ^ swz(key));
+  }
+  return d;
+}
+// Block 4 j + w of a tile into `slot`; counted by vmcnt (every wait for it is
+// explicit).  NT: the non-temporal hint (see stage_load_piece).
+template <bool NT>
+__device__ __forceinline__ void tile_dma_piece(lds_u8* slot, int j, int wave, int off,
+                                               __amdgpu_buffer_rsrc_t r) {
+  const unsigned m0v =
+      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(slot + 1024 * (4 * j + wave)));
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :: "s"(m0v), "v"(off), "s"(r) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(m0v), "v"(off), "s"(r) : "memory");
+}
+template <bool NT>
+__device__ __forceinline__ void tile_dma_all(lds_u8* slot, int wave, const TileDma& d,
+                                             __amdgpu_buffer_rsrc_t r) {
+  static_for<kPieces>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    tile_dma_piece<NT>(slot, j, wave, d.off[j], r);
+  });
+}
+
 // Write piece M of a staged tile into an LDS slot.  bf16: swizzled bf16 rows.
 // fp8: latent pieces as they are (key k0 + 4 M with k0 = tid / 64, whose
 // swizzle is k0 ^ f(M): the address is one XOR with a constant away from a
@@ -836,7 +889,7 @@ __device__ __forceinline__ void prologue_page_rows(const KvSource<FP8, PAGED>& s
 }
 
 template <bool FP8, int NRT, bool PAGED, bool NT>
-__device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* lds, int tid) {
+__device__ __forceinline__ void unit_staging_only_regs(const UnitSetup& us, lds_u8* lds, int tid) {
   constexpr int NS = stage_sets<FP8, NRT>();
   constexpr int kAhead = (NS - 1) * kPieces;
   const UnitCtx u = us.uc;
@@ -875,6 +928,35 @@ __device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* l
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads issued past the end
 }
 
+template <bool FP8, int NRT, bool PAGED, bool NT>
+__device__ __forceinline__ void unit_staging_only(const UnitSetup& us, lds_u8* lds, int tid) {
+  if constexpr (tile_dma_path<FP8, NRT>()) {  // LDS DMA: this wave's share of every tile, same waits and barriers
+    const UnitCtx u = us.uc;
+    const KvSource<FP8, PAGED> src = kv_source<FP8, PAGED>(us);
+    if (u.ntiles <= 0) return;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const TileDma dm = tile_dma(wave, tid & 63);
+    int64_t pr[3];
+    prologue_page_rows(src, pr);
+    tile_dma_all<NT>(lds, wave, dm, src.rsrc(0, pr[0]));
+    tile_dma_all<NT>(lds + kTileBytes, wave, dm, src.rsrc(1, pr[1]));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    lds_barrier();  // the exchange of tile 0's scores
+    int64_t prow_next = pr[2];  // page row of tile 2, the first the loop loads
+    for (int t = 0; t < u.ntiles; ++t) {
+      tile_dma_all<NT>(lds + ((t + 2) % 3) * kTileBytes, wave, dm, src.rsrc(t + 2, prow_next));
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if constexpr (PAGED)
+        prow_next = src.barrier_and_page_row(t + 3);
+      else
+        lds_barrier();
+    }
+  } else {
+    unit_staging_only_regs<FP8, NRT, PAGED, NT>(us, lds, tid);
+  }
+}
+
 // The whole KV chunk of a unit, software-pipelined as described above.  The
 // tile loop is unrolled by the number of staging sets so that set k always
 // holds tiles = k mod NS; every global load and wait is unconditional (tiles
@@ -887,7 +969,8 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
                                               const float (&c)[NRT], f32x4 (&oacc)[16][NRT],
                                               float (&m_run)[NRT], float (&l_run)[NRT],
                                               const int (&lim)[NRT], int tid, int g, int lane) {
-  constexpr int NS = stage_sets<FP8, NRT>();
+  constexpr bool kDma = tile_dma_path<FP8, NRT>();
+  constexpr int NS = kDma ? 1 : stage_sets<FP8, NRT>();
   constexpr int kAhead = (NS - 1) * kPieces;  // loads issued after a set's own
   constexpr int kXsWave = NRT * 2 * 256;      // floats of one wave's partial scores
   constexpr int DK = k_ahead<NRT, FP8>(), DV = v_ahead<NRT, FP8>();
@@ -896,20 +979,32 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
   const KvSource<FP8, PAGED> src = kv_source<FP8, PAGED>(us);
   if (u.ntiles <= 0) return;
 
-  // prologue: tiles 0 and 1 into their slots; tile k always travels in set k % NS
+  // prologue: tiles 0 and 1 into their slots (register staging: tile k always
+  // travels in set k % NS)
   int64_t pr[NS + 3];
   prologue_page_rows(src, pr);
   Stage<FP8> st[NS];
+  TileDma dm;
+  int64_t prow_next;  // page row of the first tile the loop loads
+  if constexpr (kDma) {
+    dm = tile_dma(wave, lane);
+    tile_dma_all<NT>(lds, wave, dm, src.rsrc(0, pr[0]));
+    tile_dma_all<NT>(lds + TB, wave, dm, src.rsrc(1, pr[1]));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    prow_next = pr[2];
+  } else {
 #pragma unroll
-  for (int k = 0; k < NS; ++k) stage_load<FP8, NT>(st[k], src.rsrc(k, pr[k]), tid);
-  static_for<2>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    wait_stage<kAhead, FP8>(st[j % NS]);
-    stage_store<FP8>(st[j % NS], lds + j * TB, tid);
-    stage_load<FP8, NT>(st[j % NS], src.rsrc(j + NS, pr[j + NS]), tid);
-  });
-  lds_barrier();
-  int64_t prow_next = pr[NS + 2];  // page row of the first tile the loop loads
+    for (int k = 0; k < NS; ++k) stage_load<FP8, NT>(st[k], src.rsrc(k, pr[k]), tid);
+    static_for<2>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      wait_stage<kAhead, FP8>(st[j % NS]);
+      stage_store<FP8>(st[j % NS], lds + j * TB, tid);
+      stage_load<FP8, NT>(st[j % NS], src.rsrc(j + NS, pr[j + NS]), tid);
+    });
+    lds_barrier();
+    prow_next = pr[NS + 2];
+  }
 
   f32x4 sacc[2][NRT], sfull[2][NRT];
   auto scores = [&](lds_u8* tile, auto&& pre, auto&& slice) {
@@ -961,7 +1056,8 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         lds_u8* slot_s = lds + ((t + 2) % RING) * TB;
         const int k0 = t * kTK;
         const bool edge = k0 + kTK - 1 > u.min_lim;
-        const __amdgpu_buffer_rsrc_t rs_next = src.rsrc(t + 2 + NS, prow_next);
+        // DMA: tile t + 2 into the slot of tile t - 1; staging: loads of tile t + 2 + NS
+        const __amdgpu_buffer_rsrc_t rs_next = src.rsrc(kDma ? t + 2 : t + 2 + NS, prow_next);
         lds_u8* vbase = nullptr;  // fp8: V reads of tile t (column tile ct adds ^ 16 ct)
         if constexpr (FP8) {
           vbase = slot_t + fb.v;
@@ -970,11 +1066,14 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
           issue_v_head<DH, DV>(vr, slot_t, fb);
         }
 
-        // staging of tile t + 2: wait for its loads, LDS store, next loads
-        constexpr int kStageSlices = 1 + 2 * kPieces;
+        // tile t + 2 into its slot: the 9 DMA loads of this wave, or (register
+        // staging) wait for its loads, LDS store, next loads
+        constexpr int kStageSlices = kDma ? kPieces : 1 + 2 * kPieces;
         auto stage_slice = [&](auto sc) {
           constexpr int s = decltype(sc)::value;
-          if constexpr (s == 0) {
+          if constexpr (kDma) {
+            tile_dma_piece<NT>(slot_s, s, wave, dm.off[s], rs_next);
+          } else if constexpr (s == 0) {
             wait_stage<kAhead, FP8>(st[ks]);
           } else if constexpr (s < 1 + kPieces) {
             stage_store_piece<FP8, s - 1>(st[ks], slot_s, tid);
@@ -1019,8 +1118,9 @@ __device__ __forceinline__ void unit_pipeline(const UnitSetup& us, lds_u8* lds, 
         else
           pv_phase<NRT, DH, DV>(slot_t, fb, pf, oacc, vr, pv_slice);
 
+        if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile t + 2 landed
         if constexpr (PAGED)
-          prow_next = src.barrier_and_page_row(t + 3 + NS);
+          prow_next = src.barrier_and_page_row(kDma ? t + 3 : t + 3 + NS);
         else
           lds_barrier();
 #pragma unroll

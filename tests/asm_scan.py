@@ -201,6 +201,14 @@ def staged_copies_in_prologues(lines) -> list:
     return found
 
 
+DMA_LOAD = re.compile(r"buffer_load_dword\S* .*\blds\s*$")
+
+
+def dma_loads_in_loops(lines) -> int:
+    """LDS DMA loads (buffer_load ... lds) inside the KV tile loops."""
+    return sum(1 for idx in tile_loops(lines).values() for k in idx if DMA_LOAD.search(lines[k]))
+
+
 def staged_loads_in_loops(lines) -> int:
     return sum(1 for idx in staging_loops(lines).values() for k in idx
                if STAGED_LOAD.search(lines[k]))

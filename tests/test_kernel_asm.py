@@ -1,8 +1,9 @@
 """CPU checks of the decode kernels' gfx950 assembly (hipcc cross-compiles
 them here with the library's own flags): hazards around the inline-assembly
-MFMAs and transcendental results, no copies of registers that staged loads
-are filling, no register-file moves inside the bf16 KV tile loop, and no
-compiler use of the AGPRs that the fp8 kernel allocates by hand."""
+MFMAs and transcendental results, KV tiles moved by LDS DMA in the tile loops
+where the kernels use it and no copies of registers that staged loads are
+filling elsewhere, no register-file moves inside the bf16 KV tile loop, and
+no compiler use of the AGPRs that the fp8 kernel allocates by hand."""
 import os
 import shutil
 import subprocess
@@ -86,11 +87,32 @@ def test_fp8_kernels_pad_mfma_hazards(fp8_kernels):
         assert asm_scan.mfma_hazards(lines) == [], name
 
 
-def test_tile_loop_has_staged_loads_and_never_copies_them(kernels):
+def test_tile_loops_move_kv_by_dma_or_uncopied_staging(kernels, fp8_kernels):
+    """The fp8 kernels and the bf16 kernels of 48-row row groups move KV tiles
+    with LDS DMA inside their tile loops; the narrower bf16 kernels stage
+    them in registers, and no compiler copy reads a staged register while its
+    load is in flight."""
+    for name, lines in fp8_kernels.items():
+        assert asm_scan.dma_loads_in_loops(lines) > 0, name
+    assert sum("Li3E" in n for n in kernels) == 4, sorted(kernels)
     for name, lines in kernels.items():
-        assert asm_scan.staged_loads_in_loops(lines) > 0, name  # the scan sees the loads
+        if "Li3E" in name:  # 3 row tiles per row group: DMA
+            assert asm_scan.dma_loads_in_loops(lines) > 0, name
+            assert asm_scan.staged_loads_in_loops(lines) == 0, name
+        else:
+            assert asm_scan.staged_loads_in_loops(lines) > 0, name  # the scan sees the loads
         assert asm_scan.staged_copies_in_loops(lines) == [], name
         assert asm_scan.staged_copies_in_prologues(lines) == [], name
+
+
+def test_scan_sees_dma_loads():
+    loop = [".LBB0_1:                                ; =>This Inner Loop Header: Depth=1",
+            "\tbuffer_load_dwordx4 v3, s[4:7], 0 offen nt lds",
+            "\tv_mfma_f32_16x16x32_bf16 v[0:3], v[4:7], v[4:7], v[0:3]",
+            "\tbuffer_load_dwordx4 v5, s[4:7], 0 offen lds",
+            "\ts_cbranch_scc1 .LBB0_1"]
+    assert asm_scan.dma_loads_in_loops(loop) == 2
+    assert asm_scan.staged_loads_in_loops(loop) == 0
 
 
 def test_tile_loop_keeps_register_files(kernels):
