@@ -43,7 +43,11 @@
  * array that is part of the library's loaded device code).  A plan is host memory owned by the
  * library until mla_plan_destroy; it must outlive work enqueued with it only
  * until mla_decode_run / mla_decode_reduce return (kernel arguments are
- * copied at launch).
+ * copied at launch), except that a plan of more than 60 sequences uploads
+ * its sequence descriptors into the workspace with an asynchronous copy from
+ * a pinned host buffer it owns (made by its first mla_decode_run): that copy
+ * must have run before the plan is destroyed, and a captured graph that
+ * holds it needs the plan for as long as the graph is replayed.
  *
  * Threading.  Plans are immutable after creation and may be used from
  * several threads.  Calls that share one workspace on overlapping streams
@@ -152,8 +156,10 @@ typedef struct {
  *  batch >= 1; num_heads = H in [1, 128]; q_len, kv_len: HOST arrays [batch]
  *  with 1 <= q_len[b] <= kv_len[b].  opts may be NULL.
  *  On MLA_OK, *plan_out owns a new plan and *workspace_bytes_out (may be
- *  NULL) is the device workspace mla_decode_run needs (0 when no sequence is
- *  split).  Pure host computation; touches the GPU only when num_cus == 0.
+ *  NULL) is the device workspace mla_decode_run needs: the split partials,
+ *  and for a batch of more than 60 sequences the sequence descriptor tables
+ *  of its single main launch (0 when neither applies).  Pure host
+ *  computation; touches the GPU only when num_cus == 0.
  *  Errors: INVALID_ARGUMENT (shapes, null pointers), UNSUPPORTED (H > 128,
  *  unknown dtype), DEVICE (CU query failed). */
 mla_status mla_decode_plan(int32_t batch, int32_t num_heads, const int32_t* q_len,
@@ -234,7 +240,8 @@ mla_status mla_decode_run_paged(const mla_plan* plan, const void* q, const void*
  * O = sum_s exp(lse_s - lse) * O_s; chunks a row cannot see (lse_s = -inf)
  * get weight 0.  Covers the launches whose split rows the main kernel did
  * not merge itself (see merge_mode); a no-op (returns MLA_OK, launches
- * nothing) when there are none.  Same pointer rules as mla_decode_run. */
+ * nothing) when there are none.  Same pointer rules as mla_decode_run, with
+ * the workspace of the mla_decode_run it follows. */
 mla_status mla_decode_reduce(const mla_plan* plan, const void* workspace, void* o, float* lse,
                              void* stream);
 
@@ -295,8 +302,9 @@ mla_status mla_plan_query(const mla_plan* plan, int32_t seq, int32_t* fold, int3
 mla_status mla_plan_order(const mla_plan* plan, int32_t* order);
 
 /* Whole-plan facts: main-kernel work units (one workgroup each), tiles that
- * are split (rows merged by the reduce), main-kernel launches (one per slice
- * of up to 60 sequences), and the workspace bytes. Any pointer may be NULL. */
+ * are split (rows merged by the reduce), main-kernel launches (one: up to 60
+ * sequence descriptors travel in its arguments, larger batches keep theirs
+ * in the workspace), and the workspace bytes. Any pointer may be NULL. */
 mla_status mla_plan_info(const mla_plan* plan, int32_t* num_units, int32_t* num_split_tiles,
                          int32_t* num_launches, size_t* workspace_bytes);
 

@@ -159,6 +159,7 @@ class Plan:
         handle = ctypes.c_void_p()
         ws = ctypes.c_size_t(0)
         self._h = None
+        self._lib = L  # the library that owns the handle also frees it
         dtype = MLA_KV_FP8_E4M3 if kv_fp8 else MLA_KV_BF16
         if causal_end is None:
             _check(L.mla_decode_plan(n, int(num_heads), qa, ka, dtype, ctypes.byref(opts),
@@ -210,7 +211,7 @@ class Plan:
 
     def close(self):
         if self._h is not None:
-            lib().mla_plan_destroy(self._h)
+            self._lib.mla_plan_destroy(self._h)
             self._h = None
 
     def __del__(self):

@@ -138,7 +138,10 @@ mla_status mla_decode_plan_shard(int32_t batch, int32_t num_heads, const int32_t
                      workspace_bytes_out);
 }
 
-void mla_plan_destroy(mla_plan* plan) { delete plan; }
+void mla_plan_destroy(mla_plan* plan) {
+  if (plan && plan->pinned_blob) (void)hipHostFree(plan->pinned_blob);
+  delete plan;
+}
 
 const char* mla_last_error(void) { return mla::last_error(); }
 
@@ -254,8 +257,8 @@ mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const
   a.kv = static_cast<const uint8_t*>(kv);
   a.o = static_cast<uint16_t*>(o);
   a.lse = lse;
-  a.part_lse = plan->workspace_bytes ? static_cast<float*>(workspace) : nullptr;
-  a.part_o = plan->workspace_bytes
+  a.part_lse = plan->total_part_rows ? static_cast<float*>(workspace) : nullptr;
+  a.part_o = plan->total_part_rows
                  ? reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + plan->part_o_offset)
                  : nullptr;
   const double log2e = 1.4426950408889634;
@@ -274,6 +277,31 @@ mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const
       plan->grid_words_offset
           ? reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + plan->grid_words_offset)
           : nullptr;
+  if (plan->seq_table) {  // the descriptor tables of a large plan, into the workspace
+    void* src = nullptr;
+    {
+      std::lock_guard<std::mutex> lk(plan->pinned_mu);
+      if (!plan->pinned_blob) {
+        void* p = nullptr;
+        hipError_t e = hipHostMalloc(&p, plan->table_blob.size(), hipHostMallocDefault);
+        if (e != hipSuccess) {
+          set_error("pinned host buffer for the descriptor tables failed: %s", hipGetErrorString(e));
+          return MLA_ERR_DEVICE;
+        }
+        std::memcpy(p, plan->table_blob.data(), plan->table_blob.size());
+        plan->pinned_blob = p;
+      }
+      src = plan->pinned_blob;
+    }
+    char* tab = static_cast<char*>(workspace) + plan->table_offset;
+    hipError_t e = hipMemcpyAsync(tab, src, plan->table_blob.size(), hipMemcpyHostToDevice,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+      set_error("descriptor table upload failed: %s", hipGetErrorString(e));
+      return MLA_ERR_DEVICE;
+    }
+    a.seq_table = reinterpret_cast<const SeqDesc*>(tab);
+  }
   for (size_t li = 0; li < plan->launches.size(); ++li) {
     const Launch& ln = plan->launches[li];
     // The grid merge needs the launch's workgroups resident at once; on a
@@ -288,7 +316,8 @@ mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const
     a.num_units = ln.num_units;
     a.units_per_xcd = (ln.num_units + kNumXcd - 1) / kNumXcd;
     a.page_table = page_table;  // a sequence's row is its SeqDesc::src (the caller's index)
-    for (int b = ln.seq_begin; b < ln.seq_end; ++b) a.seqs[b - ln.seq_begin] = plan->seqs[b];
+    if (!plan->seq_table)
+      for (int b = ln.seq_begin; b < ln.seq_end; ++b) a.seqs[b - ln.seq_begin] = plan->seqs[b];
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool nt = ln.kv_nt;
     hipError_t e = fp8 ? (page_table ? launch_fp8_paged(a, ln.nrt, nt, s)
@@ -369,11 +398,18 @@ mla_status reduce_launch(const mla_plan* plan, const Launch& ln, const void* wor
   for (int b = ln.seq_begin; b < ln.seq_end; ++b) {
     const SeqDesc& d = plan->seqs[b];
     if (d.S <= 1) continue;
-    a.seqs[ns] = d;
-    a.row0[ns] = rows;
+    if (!plan->seq_table) {
+      a.seqs[ns] = d;
+      a.row0[ns] = rows;
+    }
     rows += d.T * d.R;
     smax = d.S > smax ? d.S : smax;
     ++ns;
+  }
+  if (plan->seq_table) {  // uploaded by mla_decode_run into the same workspace
+    const char* tab = static_cast<const char*>(workspace) + plan->table_offset;
+    a.seq_table = reinterpret_cast<const SeqDesc*>(tab + plan->reduce_table_offset);
+    a.row0_table = reinterpret_cast<const int32_t*>(tab + plan->row0_table_offset);
   }
   a.num_seqs = ns;
   a.num_rows = rows;

@@ -131,6 +131,40 @@ struct UnitSetup {
   uint16_t* part_o;
 };
 
+// Descriptor of sequence b (wave-uniform) of the launch: from the kernel
+// arguments, or from the device table of a large plan, moved to scalar
+// registers (its fields feed buffer descriptors and scalar loops).
+__device__ __forceinline__ SeqDesc seq_desc(const MainArgs& args, int b) {
+  if (!args.seq_table) return args.seqs[b];
+  SeqDesc d = args.seq_table[b];
+  static_assert(sizeof(SeqDesc) % 4 == 0, "SeqDesc is made of 32-bit fields");
+  int* w = reinterpret_cast<int*>(&d);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(SeqDesc) / 4); ++i) w[i] = __builtin_amdgcn_readfirstlane(w[i]);
+  return d;
+}
+
+// The sequence that holds work unit u (wave-uniform): the last one whose
+// first unit is <= u (first units ascend in plan order; every sequence has at
+// least one unit).
+// A binary search over a large plan's table, a scan over the kernel arguments.
+__device__ __forceinline__ int seq_of_unit(const MainArgs& args, int u) {
+  if (args.seq_table) {
+    int lo = 0, hi = args.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (__builtin_amdgcn_readfirstlane(args.seq_table[mid].unit0) <= u)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    return lo;
+  }
+  int b = 0;
+  while (b + 1 < args.num_seqs && args.seqs[b + 1].unit0 <= u) ++b;
+  return b;
+}
+
 // ROW_BYTES: bytes of one KV row in memory (1152 bf16, 576 fp8); TILE_KEYS:
 // keys per compute tile of the kernel (uc.ntiles counts those).
 template <int ROW_BYTES, int TILE_KEYS>
@@ -138,9 +172,7 @@ __device__ __forceinline__ bool unit_setup(const MainArgs& args, UnitSetup& us) 
   const int p = blockIdx.x;
   const int u = (p % kNumXcd) * args.units_per_xcd + p / kNumXcd;  // XCD-aware order
   if (u >= args.num_units) return false;
-  int b = 0;
-  while (b + 1 < args.num_seqs && args.seqs[b + 1].unit0 <= u) ++b;
-  const SeqDesc& sd = args.seqs[b];
+  const SeqDesc sd = seq_desc(args, seq_of_unit(args, u));
   const int v = u - sd.unit0;
   const int per_chunk = sd.T * sd.NRB;  // units sharing one KV chunk are consecutive
   us.s = v / per_chunk;
@@ -554,7 +586,10 @@ __device__ __forceinline__ void merge_grid(const MainArgs& args, unsigned char* 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every unit's partial rows
   FoldLds& lds = *reinterpret_cast<FoldLds*>(smem + 256);
   int smax = 0;  // the reduce kernel's layout rule: chunk phases from the launch's largest S
-  for (int b = 0; b < args.num_seqs; ++b) smax = max(smax, args.seqs[b].S > 1 ? args.seqs[b].S : 0);
+  for (int b = 0; b < args.num_seqs; ++b) {
+    const int sb = seq_desc(args, b).S;
+    smax = max(smax, sb > 1 ? sb : 0);
+  }
   const int P = fold_parts(smax);
   // items: (split row, column block) for P >= 4; groups of kFoldRowsP1 rows
   // (64 threads per row) for P = 1
@@ -567,13 +602,13 @@ __device__ __forceinline__ void merge_grid(const MainArgs& args, unsigned char* 
     if (P == 1 && gr >= args.num_split_rows) continue;  // per thread: no barrier below for P = 1
     int b = 0, row0 = 0;  // the split sequence that holds split row gr
     for (; b < args.num_seqs; ++b) {
-      const SeqDesc& d = args.seqs[b];
+      const SeqDesc d = seq_desc(args, b);
       if (d.S <= 1) continue;
       if (gr < row0 + d.T * d.R) break;
       row0 += d.T * d.R;
     }
     if (b == args.num_seqs) break;  // not reached: items cover the split rows exactly
-    const SeqDesc& sd = args.seqs[b];
+    const SeqDesc sd = seq_desc(args, b);
     const int local = gr - row0;
     const int t = local / sd.R, r = local % sd.R;
     const int64_t orow = (int64_t)sd.q_row0 + (int64_t)t * sd.R + r;

@@ -1814,21 +1814,53 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_main(const MainArgs ar
 
 #ifndef MLA_PAGED_KV  // the merges are built once, with the contiguous-KV kernels
 
+// The split sequence that holds reduce row gr (first rows ascend; every split
+// sequence has at least one row) and the row's index inside it: a binary
+// search over a large plan's tables (TABLE), a scan over the kernel
+// arguments.  Each kernel reads one of the two sources only: a kernel that
+// could read a descriptor from either would have its arguments copied to
+// scratch memory.
+struct RedRow {
+  SeqDesc sd;
+  int local;
+};
+template <bool TABLE>
+__device__ __forceinline__ RedRow red_row(const ReduceArgs& args, int gr) {
+  RedRow rr;
+  if constexpr (TABLE) {
+    int lo = 0, hi = args.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (args.row0_table[mid] <= gr)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    rr.sd = args.seq_table[lo];
+    rr.local = gr - args.row0_table[lo];
+  } else {
+    int b = 0;
+    while (b + 1 < args.num_seqs && args.row0[b + 1] <= gr) ++b;
+    rr.sd = args.seqs[b];
+    rr.local = gr - args.row0[b];
+  }
+  return rr;
+}
+
 // Split-KV merge: one 256-thread block per (split output row, block of
 // fold_cols<P>() value columns), folded by fold_split_row<P> (the fold the
 // grid merge of the main kernels also runs, with the same layout rule, so
 // that the two give the same bits).  P = fold_parts(largest S of the launch).
-template <int P>
+template <int P, bool TABLE>
 __global__ __launch_bounds__(kFoldThreads) void mla_decode_reduce_kernel(const ReduceArgs args) {
   __shared__ FoldLds lds;
   constexpr int kBlocksPerRow = kDv / fold_cols<P>();
   const int gr = blockIdx.x / kBlocksPerRow;
   const int cb = blockIdx.x % kBlocksPerRow;
   if (gr >= args.num_rows) return;
-  int b = 0;
-  while (b + 1 < args.num_seqs && args.row0[b + 1] <= gr) ++b;
-  const SeqDesc& sd = args.seqs[b];
-  const int local = gr - args.row0[b];
+  const RedRow rr = red_row<TABLE>(args, gr);
+  const SeqDesc& sd = rr.sd;
+  const int local = rr.local;
   const int R = sd.R;
   const int t = local / R;
   const int r = local % R;
@@ -1841,14 +1873,14 @@ __global__ __launch_bounds__(kFoldThreads) void mla_decode_reduce_kernel(const R
 // Split-KV merge of launches whose sequences have at most 8 chunks (P = 1):
 // kFoldRowsP1 split rows per block, 64 threads per row, each thread folding
 // all chunks of 8 columns (fold_cols8).
+template <bool TABLE>
 __global__ __launch_bounds__(kFoldThreads) void mla_decode_reduce_rows_kernel(const ReduceArgs args) {
   const int gr = blockIdx.x * kFoldRowsP1 + (int)threadIdx.x / (kDv / 8);
   const int c8 = (int)threadIdx.x % (kDv / 8);
   if (gr >= args.num_rows) return;
-  int b = 0;
-  while (b + 1 < args.num_seqs && args.row0[b + 1] <= gr) ++b;
-  const SeqDesc& sd = args.seqs[b];
-  const int local = gr - args.row0[b];
+  const RedRow rr = red_row<TABLE>(args, gr);
+  const SeqDesc& sd = rr.sd;
+  const int local = rr.local;
   const int R = sd.R;
   const int t = local / R;
   const int r = local % R;
@@ -1968,30 +2000,39 @@ hipError_t launch_main_contiguous(const MainArgs& a, int nrt, bool nt, hipStream
 }
 
 #ifndef MLA_PAGED_KV
-hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
-  if (a.num_rows == 0) return hipSuccess;
+template <bool TABLE>
+static void launch_reduce_t(const ReduceArgs& a, hipStream_t stream) {
   switch (fold_parts(a.max_splits)) {
     case 1:
-      hipLaunchKernelGGL(mla_decode_reduce_rows_kernel, dim3((a.num_rows + kFoldRowsP1 - 1) / kFoldRowsP1),
-                         dim3(kFoldThreads), 0, stream, a);
+      hipLaunchKernelGGL(mla_decode_reduce_rows_kernel<TABLE>,
+                         dim3((a.num_rows + kFoldRowsP1 - 1) / kFoldRowsP1), dim3(kFoldThreads), 0,
+                         stream, a);
       break;
     case 4:
-      hipLaunchKernelGGL(mla_decode_reduce_kernel<4>, dim3((kDv / fold_cols<4>()) * a.num_rows),
+      hipLaunchKernelGGL((mla_decode_reduce_kernel<4, TABLE>), dim3((kDv / fold_cols<4>()) * a.num_rows),
                          dim3(kFoldThreads), 0, stream, a);
       break;
     case 8:
-      hipLaunchKernelGGL(mla_decode_reduce_kernel<8>, dim3((kDv / fold_cols<8>()) * a.num_rows),
+      hipLaunchKernelGGL((mla_decode_reduce_kernel<8, TABLE>), dim3((kDv / fold_cols<8>()) * a.num_rows),
                          dim3(kFoldThreads), 0, stream, a);
       break;
     case 16:
-      hipLaunchKernelGGL(mla_decode_reduce_kernel<16>, dim3((kDv / fold_cols<16>()) * a.num_rows),
-                         dim3(kFoldThreads), 0, stream, a);
+      hipLaunchKernelGGL((mla_decode_reduce_kernel<16, TABLE>),
+                         dim3((kDv / fold_cols<16>()) * a.num_rows), dim3(kFoldThreads), 0, stream, a);
       break;
     default:
-      hipLaunchKernelGGL(mla_decode_reduce_kernel<32>, dim3((kDv / fold_cols<32>()) * a.num_rows),
-                         dim3(kFoldThreads), 0, stream, a);
+      hipLaunchKernelGGL((mla_decode_reduce_kernel<32, TABLE>),
+                         dim3((kDv / fold_cols<32>()) * a.num_rows), dim3(kFoldThreads), 0, stream, a);
       break;
   }
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
+  if (a.num_rows == 0) return hipSuccess;
+  if (a.seq_table)
+    launch_reduce_t<true>(a, stream);
+  else
+    launch_reduce_t<false>(a, stream);
   return hipGetLastError();
 }
 

@@ -395,13 +395,15 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
     }
   }
 
-  // Launch slices: up to kMaxSeqPerLaunch sequences each.
+  // One launch: its sequence descriptors travel in the kernel arguments (up
+  // to kMaxSeqPerLaunch) or, for larger batches, in a table in the workspace.
   plan->launches.clear();
   plan->num_units = 0;
-  for (int b0 = 0; b0 < batch; b0 += kMaxSeqPerLaunch) {
+  plan->seq_table = batch > kMaxSeqPerLaunch;
+  {
     Launch ln{};
-    ln.seq_begin = b0;
-    ln.seq_end = std::min(batch, b0 + kMaxSeqPerLaunch);
+    ln.seq_begin = 0;
+    ln.seq_end = batch;
     int64_t units = 0;
     int maxRU = 0, split_rows = 0, max_s = 0;
     bool shared_chunks = false;  // some chunk is read by more than one unit (tiles or row blocks)
@@ -468,6 +470,35 @@ mla_status build_plan(int32_t batch, int32_t H, const int32_t* q_len, const int3
   } else {
     plan->part_o_offset = 0;
     plan->workspace_bytes = 0;
+  }
+  plan->table_offset = plan->reduce_table_offset = plan->row0_table_offset = 0;
+  plan->reduce_seqs = 0;
+  plan->table_blob.clear();
+  if (plan->seq_table) {
+    std::vector<SeqDesc> red;
+    std::vector<int32_t> row0;
+    int64_t rows = 0;
+    for (const SeqDesc& d : plan->seqs) {
+      if (d.S <= 1) continue;
+      red.push_back(d);
+      row0.push_back(static_cast<int32_t>(rows));
+      rows += static_cast<int64_t>(d.T) * d.R;
+    }
+    plan->reduce_seqs = static_cast<int32_t>(red.size());
+    const size_t main_bytes = plan->seqs.size() * sizeof(SeqDesc);
+    plan->reduce_table_offset = (main_bytes + 255) / 256 * 256;
+    plan->row0_table_offset =
+        (plan->reduce_table_offset + red.size() * sizeof(SeqDesc) + 255) / 256 * 256;
+    plan->table_blob.assign(plan->row0_table_offset + row0.size() * sizeof(int32_t), 0);
+    std::memcpy(plan->table_blob.data(), plan->seqs.data(), main_bytes);
+    if (!red.empty()) {
+      std::memcpy(plan->table_blob.data() + plan->reduce_table_offset, red.data(),
+                  red.size() * sizeof(SeqDesc));
+      std::memcpy(plan->table_blob.data() + plan->row0_table_offset, row0.data(),
+                  row0.size() * sizeof(int32_t));
+    }
+    plan->table_offset = (plan->workspace_bytes + 255) / 256 * 256;
+    plan->workspace_bytes = plan->table_offset + plan->table_blob.size();
   }
   return MLA_OK;
 }

@@ -4,6 +4,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "mla_decode.h"
@@ -14,7 +15,7 @@ constexpr int kDqk = MLA_DQK;            // 576 = 512 latent + 64 rope
 constexpr int kDv = MLA_DV;              // 512
 constexpr int kMaxRows = MLA_MAX_TILE_ROWS;  // 128
 constexpr int kGranule = MLA_KV_GRANULE;     // 64 keys
-constexpr int kMaxSeqPerLaunch = 60;     // sequence descriptors travel in kernel arguments
+constexpr int kMaxSeqPerLaunch = 60;     // sequence descriptors that travel in kernel arguments
 constexpr int kMaxUnitRows = 96;         // rows one workgroup processes (2 groups x 3 MFMA tiles)
 constexpr int kNumXcd = 8;               // MI355X: 8 XCDs, workgroups dealt round-robin
 // Largest workspace mla_decode_run_static serves from its per-device array.
@@ -69,6 +70,9 @@ struct MainArgs {
   unsigned long long* arrivals;
   unsigned long long* grid_word;
   int32_t num_split_rows;
+  // plans of more than kMaxSeqPerLaunch sequences: the descriptors of all
+  // num_seqs sequences in device memory (seqs[] unused); null otherwise
+  const SeqDesc* seq_table;
   SeqDesc seqs[kMaxSeqPerLaunch];
 };
 
@@ -83,6 +87,10 @@ struct ReduceArgs {
   int32_t max_splits;  // largest S among the launch's sequences (picks the merge layout)
   SeqDesc seqs[kMaxSeqPerLaunch];
   int32_t row0[kMaxSeqPerLaunch];  // first reduce row of each sequence in this launch
+  // more than kMaxSeqPerLaunch split sequences: seqs and row0 in device memory
+  // (the arrays above unused); null otherwise
+  const SeqDesc* seq_table;
+  const int32_t* row0_table;
 };
 
 struct MergeArgs {
@@ -128,6 +136,21 @@ struct mla_plan {
   size_t part_o_offset = 0;  // byte offset of partial O inside the workspace
   size_t arrivals_offset = 0;  // byte offset of the last-arriver merge's arrival words (0: none)
   size_t grid_words_offset = 0;  // byte offset of the grid merge's counters, one per launch (0: none)
+  // More than kMaxSeqPerLaunch sequences: one launch, its descriptor tables in
+  // the workspace at table_offset (mla_decode_run uploads table_blob there):
+  // all sequences (plan order), then the split ones at reduce_table_offset,
+  // then their first reduce rows at row0_table_offset (offsets in the blob).
+  bool seq_table = false;
+  size_t table_offset = 0;
+  size_t reduce_table_offset = 0;
+  size_t row0_table_offset = 0;
+  int32_t reduce_seqs = 0;
+  std::vector<uint8_t> table_blob;
+  // a pinned host copy of table_blob, made by the first mla_decode_run that
+  // needs it (so that the upload is an asynchronous copy) and freed with the
+  // plan
+  mutable std::mutex pinned_mu;
+  mutable void* pinned_blob = nullptr;
 };
 
 namespace mla {

@@ -24,6 +24,7 @@ from __future__ import annotations
 import re
 
 MAIN_KERNEL = re.compile(r"^(_Z\S*mla_decode_main\S*):", re.M)
+MERGE_KERNEL = re.compile(r"^(_Z\S*mla_(?:decode_reduce|merge_shards)\S*):", re.M)
 FP8_KERNEL = re.compile(r"^(_Z\S*mla_decode_fp8\S*):", re.M)
 TRANS_OP = re.compile(r"^v_(exp|log|rcp|rcp_iflag|rsq|sqrt|sin|cos)(_legacy)?_f(16|32)")
 STAGED_LOAD = re.compile(r"buffer_load_dwordx[24] (v\S+?),? v\d+, s\[\d+:\d+\], s\d+ offen")

@@ -10,6 +10,7 @@
 // sanitizers.
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <vector>
 
 #include "plan.hpp"
@@ -88,9 +89,32 @@ static void check_plan(const mla_plan& p, const std::vector<int32_t>& q, const s
     } else {
       CHECK(p.grid_words_offset == 0);
     }
-    CHECK(p.workspace_bytes == end);
-  } else {
+    if (!p.seq_table) CHECK(p.workspace_bytes == end);
+  } else if (!p.seq_table) {
     CHECK(p.workspace_bytes == 0);
+  }
+  // more than kMaxSeqPerLaunch sequences: one launch, descriptor tables last
+  // in the workspace (all sequences, the split ones, their first reduce rows)
+  CHECK(p.seq_table == (batch > mla::kMaxSeqPerLaunch));
+  CHECK(static_cast<int>(p.launches.size()) == 1);
+  if (p.seq_table) {
+    CHECK(p.table_offset % 256 == 0 && p.workspace_bytes == p.table_offset + p.table_blob.size());
+    const mla::SeqDesc* all = reinterpret_cast<const mla::SeqDesc*>(p.table_blob.data());
+    for (int i = 0; i < batch; ++i) CHECK(std::memcmp(&all[i], &p.seqs[i], sizeof(mla::SeqDesc)) == 0);
+    const mla::SeqDesc* red =
+        reinterpret_cast<const mla::SeqDesc*>(p.table_blob.data() + p.reduce_table_offset);
+    const int32_t* row0 = reinterpret_cast<const int32_t*>(p.table_blob.data() + p.row0_table_offset);
+    int k = 0;
+    int64_t rows = 0;
+    for (int i = 0; i < batch; ++i) {
+      if (p.seqs[i].S <= 1) continue;
+      CHECK(std::memcmp(&red[k], &p.seqs[i], sizeof(mla::SeqDesc)) == 0);
+      CHECK(row0[k] == rows);
+      rows += static_cast<int64_t>(p.seqs[i].T) * p.seqs[i].R;
+      ++k;
+    }
+    CHECK(k == p.reduce_seqs);
+    CHECK(p.row0_table_offset + sizeof(int32_t) * k == p.table_blob.size());
   }
   int covered = 0;
   for (const mla::Launch& ln : p.launches) {
@@ -110,7 +134,7 @@ static void check_plan(const mla_plan& p, const std::vector<int32_t>& q, const s
     for (int i = ln.seq_begin; i < ln.seq_end; ++i) shared = shared || p.seqs[i].T * p.seqs[i].NRB > 1;
     CHECK(ln.kv_nt == !shared);
     CHECK(ln.seq_begin == covered && ln.seq_end > ln.seq_begin);
-    CHECK(ln.seq_end - ln.seq_begin <= mla::kMaxSeqPerLaunch);
+    CHECK(p.seq_table || ln.seq_end - ln.seq_begin <= mla::kMaxSeqPerLaunch);
     CHECK(ln.nrt >= 1 && ln.nrt <= 3);
     covered = ln.seq_end;
   }

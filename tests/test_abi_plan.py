@@ -130,9 +130,17 @@ def test_merge_mode_choice():
         head.launch(1)
 
 
-def test_many_sequences_use_several_launches():
-    p = plan(8, [1] * 150, [300] * 150)
-    assert p.num_launches == 3
+def test_many_sequences_run_as_one_launch_with_a_descriptor_table():
+    # up to 60 sequence descriptors travel in the kernel arguments; a larger
+    # batch is still one launch, its descriptors in the workspace
+    small = plan(8, [1] * 60, [300] * 60, force_splits=1)
+    assert small.num_launches == 1 and small.workspace_bytes == 0
+    big = plan(8, [1] * 150, [300] * 150, force_splits=1)
+    assert big.num_launches == 1 and big.launch(0)[0] == big.num_units
+    desc = 60  # bytes of one sequence descriptor
+    assert 150 * desc <= big.workspace_bytes < 150 * desc + 1024  # no split: the table alone
+    split = plan(8, [1] * 150, [3000] * 150, force_splits=3)
+    assert split.num_launches == 1 and split.num_split_tiles == 150
 
 
 @pytest.mark.parametrize("args,status", [

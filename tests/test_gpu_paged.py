@@ -21,6 +21,8 @@ CASES = [
     (96, [2], [700], 64, 0),
     (12, [1, 3, 2, 4], [100, 2048, 513, 1200], 256, 0),
     (16, [4, 1], [4097, 64], 4096, 2),
+    # more than 60 sequences: one launch, its descriptor tables in the workspace
+    (8, ([1, 2, 3, 4] * 18)[:70], [65 + (97 * i) % 640 for i in range(70)], 64, 3),
 ]
 
 

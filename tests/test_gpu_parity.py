@@ -8,6 +8,7 @@ determinism, NaN-poisoned workspace."""
 import numpy as np
 import pytest
 
+from mla_token_decode_amd import binding as mb
 from mla_token_decode_amd import inputs as gen
 from tests import gpu_util as gu
 
@@ -135,6 +136,25 @@ def test_every_merge_layout_vs_oracle(fp8):
     o, lse, plan = gu.run_gpu(inp, force_splits=200)
     assert [plan.query(b)[2] for b in range(3)] == [5, 2, 200]
     gu.compare(o, lse, ro, rl, fp8, "mixed chunk counts 5, 2, 200")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("batch,mode", [(130, mb.MLA_MERGE_REDUCE), (70, mb.MLA_MERGE_LAST_ARRIVER),
+                                        (70, mb.MLA_MERGE_GRID)])
+def test_large_batch_is_one_launch(fp8, batch, mode):
+    """More than 60 sequences run as one launch whose descriptor tables sit in
+    the workspace (uploaded by mla_decode_run, searched by the kernels): mixed
+    q_len and lengths, split into up to 3 chunks, every merge, vs the oracle."""
+    gu.log(f"large batch B={batch} merge={mode} fp8={fp8}")
+    rng = np.random.default_rng(batch + 7 * mode)
+    ql = rng.integers(1, 5, batch).tolist()
+    kl = rng.integers(64, 700, batch).tolist()
+    inp = gen.random_inputs(8, ql, kl, fp8, seed=batch + mode)
+    ro, rl = gu.oracle_full(inp)
+    o, lse, plan = gu.run_gpu(inp, force_splits=3, merge_mode=mode, poison_workspace=True)
+    assert plan.num_launches == 1 and plan.num_split_tiles > 0
+    assert plan.launch(0)[1] == mode, "the case must take the merge it names"
+    gu.compare(o, lse, ro, rl, fp8, f"B={batch} merge={mode}")
 
 
 @pytest.mark.parametrize("beta", [1.0, 2.0, 3.0])

@@ -64,6 +64,18 @@ def test_main_kernels_use_no_scratch(kernels):
         assert asm_scan.scratch_bytes(lines) == 0, name
 
 
+def test_merge_kernels_use_no_scratch(assembly):
+    """The reduce and shard-merge kernels, in both the forms that read
+    sequence descriptors from the kernel arguments and from a large plan's
+    workspace tables, hold nothing in private memory (an argument array
+    indexed per lane would copy the whole argument block there)."""
+    ks = asm_scan.kernels(assembly["kernels"], asm_scan.MERGE_KERNEL)
+    # reduce: 1 row layout + 4 chunk-phase layouts, two descriptor sources; shard merge
+    assert len(ks) == 11, sorted(ks)
+    for name, lines in ks.items():
+        assert asm_scan.scratch_bytes(lines) == 0, name
+
+
 def test_no_unpadded_mfma_hazards(kernels):
     for name, lines in kernels.items():
         assert asm_scan.mfma_hazards(lines) == [], name
