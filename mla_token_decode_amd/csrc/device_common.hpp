@@ -131,12 +131,10 @@ struct UnitSetup {
   uint16_t* part_o;
 };
 
-// Descriptor of sequence b (wave-uniform) of the launch: from the kernel
-// arguments, or from the device table of a large plan, moved to scalar
-// registers (its fields feed buffer descriptors and scalar loops).
-__device__ __forceinline__ SeqDesc seq_desc(const MainArgs& args, int b) {
-  if (!args.seq_table) return args.seqs[b];
-  SeqDesc d = args.seq_table[b];
+// Entry b (wave-uniform) of a descriptor table in device memory, moved to
+// scalar registers (its fields feed buffer descriptors and scalar loops).
+__device__ __forceinline__ SeqDesc uniform_desc(const SeqDesc* table, int b) {
+  SeqDesc d = table[b];
   static_assert(sizeof(SeqDesc) % 4 == 0, "SeqDesc is made of 32-bit fields");
   int* w = reinterpret_cast<int*>(&d);
 #pragma unroll
@@ -144,25 +142,38 @@ __device__ __forceinline__ SeqDesc seq_desc(const MainArgs& args, int b) {
   return d;
 }
 
+// The last index i in [0, n) with key(i) <= x, for keys that ascend with
+// key(0) <= x: a binary search (x wave-uniform, so every probe is one scalar
+// load).
+template <class Key>
+__device__ __forceinline__ int last_at_or_below(int n, int x, Key key) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (key(mid) <= x)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// Descriptor of sequence b (wave-uniform) of the launch: from the kernel
+// arguments, or from the device table of a large plan.
+__device__ __forceinline__ SeqDesc seq_desc(const MainArgs& args, int b) {
+  if (!args.seq_table) return args.seqs[b];
+  return uniform_desc(args.seq_table, b);
+}
+
 // The sequence that holds work unit u (wave-uniform): the last one whose
 // first unit is <= u (first units ascend in plan order; every sequence has at
 // least one unit).
-// A binary search over a large plan's table, a scan over the kernel arguments.
 __device__ __forceinline__ int seq_of_unit(const MainArgs& args, int u) {
-  if (args.seq_table) {
-    int lo = 0, hi = args.num_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (__builtin_amdgcn_readfirstlane(args.seq_table[mid].unit0) <= u)
-        lo = mid;
-      else
-        hi = mid - 1;
-    }
-    return lo;
-  }
-  int b = 0;
-  while (b + 1 < args.num_seqs && args.seqs[b + 1].unit0 <= u) ++b;
-  return b;
+  if (args.seq_table)
+    return last_at_or_below(args.num_seqs, u, [&](int i) {
+      return __builtin_amdgcn_readfirstlane(args.seq_table[i].unit0);
+    });
+  return last_at_or_below(args.num_seqs, u, [&](int i) { return args.seqs[i].unit0; });
 }
 
 // ROW_BYTES: bytes of one KV row in memory (1152 bf16, 576 fp8); TILE_KEYS:
@@ -260,8 +271,9 @@ __device__ __forceinline__ unsigned arrive(unsigned long long* w, uint32_t epoch
 // block (one 16-byte load per chunk) and folds chunks p, p + P, ... in
 // ascending order, eight at a time with their loads in flight together,
 // against the running maximum of the LSEs it has read (its sums are rescaled
-// when that maximum moves).  The P per-part results are combined in part
-// order through LDS, so the result does not depend on timing.  A chunk that
+// when that maximum moves).  The P per-part results are combined in a fixed
+// order (a butterfly over the parts that one wave holds, then the four waves
+// in wave order through LDS), so the result does not depend on timing.  A chunk that
 // shows the row no key has LSE = -inf and weight 0; a row no chunk shows a key
 // gets O = 0, LSE = -inf.  Partial row of chunk s: pbase + s * R.  Every thread
 // of the block calls it; it ends with the LDS free again.
@@ -278,13 +290,27 @@ template <int P>
 constexpr int fold_cols() { return 8 * (kFoldThreads / P); }  // value columns per block (P >= 4)
 constexpr int kFoldRowsP1 = kFoldThreads / (kDv / 8);         // rows per block with P = 1
 
+constexpr int kFoldWaves = kFoldThreads / 64;
 struct FoldLds {
-  f32x4 acc[kFoldThreads][2];  // [part * G + group]
-  float w[32], m[32];          // per part
+  f32x4 acc[kFoldWaves][64][2];  // per wave: the sums of each column group
+  float w[kFoldWaves], m[kFoldWaves];
 };
 
 __device__ __forceinline__ float merge_weight(float ls, float M) {
   return ls == -INFINITY ? 0.0f : __expf(ls - M);
+}
+
+// Folds (mo, Wo, b0, b1) into (m, W, a0, a1): two folds of the same columns,
+// each a running maximum, its weight sum and its weighted sums, rescaled to
+// their common maximum.
+__device__ __forceinline__ void fold_pair(float& m, float& W, f32x4& a0, f32x4& a1, float mo,
+                                          float Wo, const f32x4& b0, const f32x4& b1) {
+  const float M = fmaxf(m, mo);
+  const float f = merge_weight(m, M), g = merge_weight(mo, M);
+  a0 = f * a0 + g * b0;
+  a1 = f * a1 + g * b1;
+  W = f * W + g * Wo;
+  m = M;
 }
 
 // 4 bf16 (two dwords, element 0 in the low half of the first) -> fp32, exact.
@@ -343,25 +369,44 @@ __device__ __forceinline__ void fold_split_row(const float* part_lse, const uint
       a1 += w * hi;
     }
   }
-  lds.acc[threadIdx.x][0] = a0;
-  lds.acc[threadIdx.x][1] = a1;
-  if (cg == 0) {
-    lds.w[part] = W;
-    lds.m[part] = m;
+  // The P folds of each column group are combined in two fixed stages: the
+  // P / 4 parts within a wave by a butterfly over the lanes (lane l and lane
+  // l ^ d hold the same columns for d >= G), then the 4 waves in wave order
+  // through LDS.
+  static_assert(G <= 64 && 64 % G == 0, "a wave holds whole parts");
+#pragma unroll
+  for (int d = G; d < 64; d <<= 1) {
+    f32x4 b0, b1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      b0[k] = __shfl_xor(a0[k], d);
+      b1[k] = __shfl_xor(a1[k], d);
+    }
+    const float mo = __shfl_xor(m, d), Wo = __shfl_xor(W, d);
+    fold_pair(m, W, a0, a1, mo, Wo, b0, b1);
+  }
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  if (lane < G) {  // part 0 of the wave: cg == lane
+    lds.acc[wave][lane][0] = a0;
+    lds.acc[wave][lane][1] = a1;
+    if (lane == 0) {
+      lds.w[wave] = W;
+      lds.m[wave] = m;
+    }
   }
   __syncthreads();
   if (threadIdx.x < G) {
     float M = -INFINITY;
 #pragma unroll
-    for (int p = 0; p < P; ++p) M = fmaxf(M, lds.m[p]);
+    for (int k = 0; k < kFoldWaves; ++k) M = fmaxf(M, lds.m[k]);
     f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
     float Wt = 0.0f;
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const float f = merge_weight(lds.m[p], M);
-      t0 += f * lds.acc[p * G + cg][0];
-      t1 += f * lds.acc[p * G + cg][1];
-      Wt += f * lds.w[p];
+    for (int k = 0; k < kFoldWaves; ++k) {
+      const float f = merge_weight(lds.m[k], M);
+      t0 += f * lds.acc[k][cg][0];
+      t1 += f * lds.acc[k][cg][1];
+      Wt += f * lds.w[k];
     }
     const bool empty = !(Wt > 0.0f);  // no chunk shows this row a key
     const float inv = empty ? 0.0f : 1.0f / Wt;

@@ -1814,12 +1814,12 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_main(const MainArgs ar
 
 #ifndef MLA_PAGED_KV  // the merges are built once, with the contiguous-KV kernels
 
-// The split sequence that holds reduce row gr (first rows ascend; every split
-// sequence has at least one row) and the row's index inside it: a binary
-// search over a large plan's tables (TABLE), a scan over the kernel
-// arguments.  Each kernel reads one of the two sources only: a kernel that
-// could read a descriptor from either would have its arguments copied to
-// scratch memory.
+// The split sequence that holds reduce row gr (wave-uniform; first rows
+// ascend and every split sequence has at least one row) and the row's index
+// inside it, found by binary search over a large plan's tables in the
+// workspace (TABLE) or over the kernel arguments.  Each kernel reads one of
+// the two sources only: a kernel that could read a descriptor from either
+// would have its arguments copied to scratch memory.
 struct RedRow {
   SeqDesc sd;
   int local;
@@ -1828,19 +1828,13 @@ template <bool TABLE>
 __device__ __forceinline__ RedRow red_row(const ReduceArgs& args, int gr) {
   RedRow rr;
   if constexpr (TABLE) {
-    int lo = 0, hi = args.num_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (args.row0_table[mid] <= gr)
-        lo = mid;
-      else
-        hi = mid - 1;
-    }
-    rr.sd = args.seq_table[lo];
-    rr.local = gr - args.row0_table[lo];
+    const int b = last_at_or_below(args.num_seqs, gr, [&](int i) {
+      return __builtin_amdgcn_readfirstlane(args.row0_table[i]);
+    });
+    rr.sd = uniform_desc(args.seq_table, b);
+    rr.local = gr - __builtin_amdgcn_readfirstlane(args.row0_table[b]);
   } else {
-    int b = 0;
-    while (b + 1 < args.num_seqs && args.row0[b + 1] <= gr) ++b;
+    const int b = last_at_or_below(args.num_seqs, gr, [&](int i) { return args.row0[i]; });
     rr.sd = args.seqs[b];
     rr.local = gr - args.row0[b];
   }
@@ -1875,8 +1869,10 @@ __global__ __launch_bounds__(kFoldThreads) void mla_decode_reduce_kernel(const R
 // all chunks of 8 columns (fold_cols8).
 template <bool TABLE>
 __global__ __launch_bounds__(kFoldThreads) void mla_decode_reduce_rows_kernel(const ReduceArgs args) {
-  const int gr = blockIdx.x * kFoldRowsP1 + (int)threadIdx.x / (kDv / 8);
-  const int c8 = (int)threadIdx.x % (kDv / 8);
+  // one row per wave: the row index is wave-uniform
+  static_assert(kDv / 8 == 64, "a row's 8-column groups fill one wave");
+  const int gr = blockIdx.x * kFoldRowsP1 + __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64);
+  const int c8 = (int)threadIdx.x % 64;
   if (gr >= args.num_rows) return;
   const RedRow rr = red_row<TABLE>(args, gr);
   const SeqDesc& sd = rr.sd;
