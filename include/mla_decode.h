@@ -68,7 +68,8 @@ typedef enum {
   MLA_ERR_INVALID_ARGUMENT = 1, /* bad shape, null/misaligned pointer, bad scale */
   MLA_ERR_UNSUPPORTED = 2,      /* no valid fold (H > 128), unknown dtype, not gfx950 */
   MLA_ERR_WORKSPACE_TOO_SMALL = 3,
-  MLA_ERR_DEVICE = 4            /* a HIP call failed; mla_last_error() has its message */
+  MLA_ERR_DEVICE = 4,           /* a HIP call failed; mla_last_error() has its message */
+  MLA_ERR_OUT_OF_MEMORY = 5     /* host memory for a plan could not be allocated */
 } mla_status;
 
 typedef enum {

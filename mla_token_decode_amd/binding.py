@@ -19,6 +19,7 @@ MLA_ERR_INVALID_ARGUMENT = 1
 MLA_ERR_UNSUPPORTED = 2
 MLA_ERR_WORKSPACE_TOO_SMALL = 3
 MLA_ERR_DEVICE = 4
+MLA_ERR_OUT_OF_MEMORY = 5
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3 = 1
 MLA_PLAN_AUTO = 0

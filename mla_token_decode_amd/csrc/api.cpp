@@ -105,9 +105,15 @@ static mla_status plan_common(int32_t batch, int32_t num_heads, const int32_t* q
   mla_plan* p = new (std::nothrow) mla_plan();
   if (!p) {
     set_error("out of host memory");
-    return MLA_ERR_INVALID_ARGUMENT;
+    return MLA_ERR_OUT_OF_MEMORY;
   }
-  mla_status st = build_plan(batch, num_heads, q_len, kv_len, causal_end, kv_dtype, &o, p);
+  mla_status st;
+  try {  // the plan's tables are host vectors: no exception may leave the C ABI
+    st = build_plan(batch, num_heads, q_len, kv_len, causal_end, kv_dtype, &o, p);
+  } catch (const std::bad_alloc&) {
+    set_error("out of host memory building the plan");
+    st = MLA_ERR_OUT_OF_MEMORY;
+  }
   if (st != MLA_OK) {
     delete p;
     return st;

@@ -30,6 +30,14 @@ def test_library_exports_every_declared_symbol():
         assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
 
 
+def test_status_codes_match_the_header():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    enum = {k: int(v) for k, v in re.findall(r"\b(MLA_(?:OK|ERR_[A-Z_]+))\s*=\s*(\d+)", text)}
+    assert "MLA_ERR_OUT_OF_MEMORY" in enum
+    binding = {n: getattr(mb, n) for n in dir(mb) if n == "MLA_OK" or n.startswith("MLA_ERR_")}
+    assert enum == binding
+
+
 def plan(H, q_len, kv_len, fp8=False, **kw):
     kw.setdefault("num_cus", 256)
     return mb.Plan(H, q_len, kv_len, fp8, **kw)
