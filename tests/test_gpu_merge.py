@@ -166,6 +166,63 @@ def test_graph_replays_match_the_eager_call(mode):
         assert torch_equal(o2.cpu(), ref_o2.cpu()) and torch_equal(lse2.cpu(), ref_l2.cpu()), f"eager {rep}"
 
 
+def test_graph_replays_of_a_large_plan():
+    """A plan of more than 60 sequences copies its descriptor tables into the
+    workspace on every run (an asynchronous copy from the plan's pinned host
+    buffer, which a captured graph holds as a copy node).  Eager runs of
+    another large plan overwrite those tables between the replays; every
+    replay must still give the bits of the eager call."""
+    import torch
+    gu.log("graph replay of a 70-sequence plan, 90-sequence plan between replays")
+    rng = np.random.default_rng(5)
+
+    def make(batch, seed):
+        return gen.random_inputs(8, rng.integers(1, 5, batch).tolist(),
+                                 rng.integers(64, 700, batch).tolist(), False, seed=seed)
+
+    inp, other = make(70, 11), make(90, 12)
+    q, kv = gu.to_device(inp)
+    q2, kv2 = gu.to_device(other)
+    plan = mb.Plan(inp.H, inp.q_len, inp.kv_len, False, force_splits=3)
+    plan2 = mb.Plan(other.H, other.q_len, other.kv_len, False, force_splits=3)
+    assert plan.num_launches == 1 and plan2.num_launches == 1
+    assert plan.num_split_tiles > 0 and plan2.num_split_tiles > 0
+    o, lse, ws = mb.alloc_outputs(plan, q.device)
+    o2, lse2, ws2 = mb.alloc_outputs(plan2, q.device)
+    ws = ws if ws.numel() >= ws2.numel() else ws2  # one workspace for both plans
+
+    def call(pl, qq, kk, oo, ll, src):
+        mb.mla_decode_run(pl, qq, kk, src.sm_scale, src.kv_scale, oo, ll, ws, ws.numel())
+        mb.mla_decode_reduce(pl, ws, oo, ll)
+
+    call(plan, q, kv, o, lse, inp)
+    torch.cuda.synchronize()
+    ref_o, ref_l = o.clone(), lse.clone()
+    call(plan2, q2, kv2, o2, lse2, other)
+    torch.cuda.synchronize()
+    ref_o2, ref_l2 = o2.clone(), lse2.clone()
+    ro, rl = gu.oracle_full(inp)
+    gu.compare(o.cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl, False, "eager, 70 sequences")
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call(plan, q, kv, o, lse, inp)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch_equal(o.cpu(), ref_o.cpu()) and torch_equal(lse.cpu(), ref_l.cpu()), f"replay {rep}"
+        call(plan2, q2, kv2, o2, lse2, other)  # the other plan's tables into the same workspace
+        torch.cuda.synchronize()
+        assert torch_equal(o2.cpu(), ref_o2.cpu()) and torch_equal(lse2.cpu(), ref_l2.cpu()), f"eager {rep}"
+
+
 def torch_equal(a, b):
     import torch
     return bool(torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
