@@ -45,9 +45,10 @@
  * until mla_decode_run / mla_decode_reduce return (kernel arguments are
  * copied at launch), except that a plan of more than 60 sequences uploads
  * its sequence descriptors into the workspace with an asynchronous copy from
- * a pinned host buffer it owns (made by its first mla_decode_run): that copy
- * must have run before the plan is destroyed, and a captured graph that
- * holds it needs the plan for as long as the graph is replayed.
+ * a pinned host buffer it owns (made when the plan is created, or, if that
+ * fails, by its first mla_decode_run): that copy must have run before the
+ * plan is destroyed, and a captured graph that holds it needs the plan for
+ * as long as the graph is replayed.
  *
  * Threading.  Plans are immutable after creation and may be used from
  * several threads.  Calls that share one workspace on overlapping streams
@@ -160,7 +161,10 @@ typedef struct {
  *  NULL) is the device workspace mla_decode_run needs: the split partials,
  *  and for a batch of more than 60 sequences the sequence descriptor tables
  *  of its single main launch (0 when neither applies).  Pure host
- *  computation; touches the GPU only when num_cus == 0.
+ *  computation, except that it queries the device when num_cus == 0 and
+ *  that a batch of more than 60 sequences gets the pinned host buffer its
+ *  descriptor tables are uploaded from (hipHostMalloc; if that fails the
+ *  plan is still made and its first mla_decode_run allocates the buffer).
  *  Errors: INVALID_ARGUMENT (shapes, null pointers), UNSUPPORTED (H > 128,
  *  unknown dtype), DEVICE (CU query failed). */
 mla_status mla_decode_plan(int32_t batch, int32_t num_heads, const int32_t* q_len,
@@ -273,9 +277,14 @@ mla_status mla_merge_shards(int32_t num_rows, int32_t num_shards, const void* o_
  *  contents (no call depends on what it held before: every partial the merge
  *  reads is written by the same call).  Calls that overlap on one device --
  *  on two streams, or from two threads -- race on it; serialise them.
- *  Errors: those of mla_decode_run, and WORKSPACE_TOO_SMALL for a plan whose
+ *  A plan of more than 60 sequences uploads its descriptor tables from the
+ *  pinned host buffer made when the plan was created; this call never makes
+ *  one.
+ *  Errors: those of mla_decode_run; WORKSPACE_TOO_SMALL for a plan whose
  *  workspace exceeds MLA_STATIC_WORKSPACE_BYTES (the plan's workspace_bytes
- *  tells which plans fit; the graded shapes need at most 26 MB). */
+ *  tells which plans fit; the graded shapes need at most 26 MB); DEVICE for a
+ *  plan of more than 60 sequences whose creation could not make its pinned
+ *  buffer and that has not run through mla_decode_run since. */
 mla_status mla_decode_run_static(const mla_plan* plan, const void* q, const void* kv,
                                  float sm_scale, float kv_scale, void* o, float* lse,
                                  void* stream);

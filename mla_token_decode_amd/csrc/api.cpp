@@ -78,6 +78,27 @@ mla_status current_device(int* cus) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The pinned host copy of a large plan's descriptor tables, the source of the
+// upload that every run enqueues.  Made once under the plan's lock: by plan
+// creation, or, when that could not make it, by the first run allowed to
+// allocate.  A failed allocation leaves HIP's error state clear, so that it
+// is not reported by a later launch check.
+hipError_t pinned_tables(const mla_plan* p, bool may_allocate, const void** out) {
+  std::lock_guard<std::mutex> lk(p->pinned_mu);
+  if (!p->pinned_blob && may_allocate) {
+    void* ptr = nullptr;
+    const hipError_t e = hipHostMalloc(&ptr, p->table_blob.size(), hipHostMallocDefault);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return e;
+    }
+    std::memcpy(ptr, p->table_blob.data(), p->table_blob.size());
+    p->pinned_blob = ptr;
+  }
+  *out = p->pinned_blob;
+  return hipSuccess;
+}
+
 }  // namespace
 }  // namespace mla
 
@@ -117,6 +138,10 @@ static mla_status plan_common(int32_t batch, int32_t num_heads, const int32_t* q
   if (st != MLA_OK) {
     delete p;
     return st;
+  }
+  if (p->seq_table) {  // made here when possible, so that no run needs to allocate
+    const void* unused = nullptr;
+    (void)pinned_tables(p, true, &unused);
   }
   *plan_out = p;
   if (workspace_bytes_out) *workspace_bytes_out = p->workspace_bytes;
@@ -215,10 +240,12 @@ mla_status reduce_launch(const mla_plan* plan, const Launch& ln, const void* wor
 
 // Shared by the contiguous and the paged entry points: `kv` is the KV array or
 // the page pool; `page_table` is null for contiguous KV.
+// may_allocate: whether a large plan without its pinned tables may make them
+// here (not for mla_decode_run_static).
 mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const int32_t* page_table,
                       int32_t pt_stride, int32_t page_shift, int32_t num_pages, float sm_scale,
                       float kv_scale, void* o, float* lse, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      void* stream, bool may_allocate) {
   if (!plan) {
     set_error("plan must be non-null");
     return MLA_ERR_INVALID_ARGUMENT;
@@ -284,20 +311,17 @@ mla_status run_common(const mla_plan* plan, const void* q, const void* kv, const
           ? reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + plan->grid_words_offset)
           : nullptr;
   if (plan->seq_table) {  // the descriptor tables of a large plan, into the workspace
-    void* src = nullptr;
-    {
-      std::lock_guard<std::mutex> lk(plan->pinned_mu);
-      if (!plan->pinned_blob) {
-        void* p = nullptr;
-        hipError_t e = hipHostMalloc(&p, plan->table_blob.size(), hipHostMallocDefault);
-        if (e != hipSuccess) {
-          set_error("pinned host buffer for the descriptor tables failed: %s", hipGetErrorString(e));
-          return MLA_ERR_DEVICE;
-        }
-        std::memcpy(p, plan->table_blob.data(), plan->table_blob.size());
-        plan->pinned_blob = p;
-      }
-      src = plan->pinned_blob;
+    const void* src = nullptr;
+    const hipError_t pe = pinned_tables(plan, may_allocate, &src);
+    if (pe != hipSuccess) {
+      set_error("pinned host buffer for the descriptor tables failed: %s", hipGetErrorString(pe));
+      return MLA_ERR_DEVICE;
+    }
+    if (!src) {
+      set_error("the plan has no pinned host buffer for its descriptor tables (its creation could "
+                "not make one) and mla_decode_run_static allocates nothing; run the plan once with "
+                "mla_decode_run first");
+      return MLA_ERR_DEVICE;
     }
     char* tab = static_cast<char*>(workspace) + plan->table_offset;
     hipError_t e = hipMemcpyAsync(tab, src, plan->table_blob.size(), hipMemcpyHostToDevice,
@@ -348,7 +372,7 @@ mla_status mla_decode_run(const mla_plan* plan, const void* q, const void* kv, f
                           float kv_scale, void* o, float* lse, void* workspace,
                           size_t workspace_bytes, void* stream) {
   return run_common(plan, q, kv, nullptr, 0, 0, 0, sm_scale, kv_scale, o, lse, workspace,
-                    workspace_bytes, stream);
+                    workspace_bytes, stream, true);
 }
 
 mla_status mla_decode_run_paged(const mla_plan* plan, const void* q, const void* kv_pages,
@@ -384,7 +408,7 @@ mla_status mla_decode_run_paged(const mla_plan* plan, const void* q, const void*
   int shift = 0;
   while ((1 << shift) < page_size) ++shift;
   return run_common(plan, q, kv_pages, page_table, page_table_stride, shift, num_pages, sm_scale,
-                    kv_scale, o, lse, workspace, workspace_bytes, stream);
+                    kv_scale, o, lse, workspace, workspace_bytes, stream, true);
 }
 
 namespace {
@@ -486,7 +510,7 @@ mla_status mla_decode_run_static(const mla_plan* plan, const void* q, const void
     }
   }
   st = run_common(plan, q, kv, nullptr, 0, 0, 0, sm_scale, kv_scale, o, lse, ws,
-                  plan->workspace_bytes, stream);
+                  plan->workspace_bytes, stream, false);
   if (st != MLA_OK || plan->total_part_rows == 0) return st;
   return reduce_common(plan, ws, o, lse, stream);
 }

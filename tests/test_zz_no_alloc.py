@@ -76,6 +76,24 @@ def test_static_workspace_full_size_headline_and_limit():
     assert torch.count_nonzero(o).item() == 0  # nothing was launched
 
 
+def test_static_entry_point_first_run_of_a_large_plan():
+    """A plan of more than 60 sequences uploads its descriptor tables from the
+    pinned host buffer made when the plan was created: the static entry
+    point, as the plan's first run, allocates nothing and matches the
+    caller-workspace run bitwise."""
+    rng = np.random.default_rng(9)
+    batch = 70
+    gu.log(f"static entry point, first run of a {batch}-sequence plan")
+    inp = gen.random_inputs(8, rng.integers(1, 5, batch).tolist(), rng.integers(64, 700, batch).tolist(),
+                            False, seed=9)
+    dev = gu.to_device(inp)
+    o2, l2, p2 = _static(inp, dev, force_splits=3)
+    assert p2.num_launches == 1 and p2.num_split_tiles > 0
+    assert 0 < p2.workspace_bytes <= mb.STATIC_WORKSPACE_BYTES
+    o1, l1, _ = gu.run_gpu(inp, dev, poison_workspace=True, force_splits=3)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 def test_static_entry_point_without_split_work():
     inp = gen.random_inputs(12, [4], [200], False, seed=5)
     dev = gu.to_device(inp)
