@@ -210,6 +210,8 @@ def measure(inp, dev, steps, warmup, flush, paged=None, settle_ms=0, **plan_opts
         "wall_s": wall,
         "clocks_before": clocks_before,
         "clocks_after": read_clocks(),
+        "_calls_us": tot.tolist(),  # per-call samples (kept out of the JSON line)
+        "_main_us": main.tolist(),
     }
 
 
@@ -371,6 +373,39 @@ def profile_inputs(name):
     return inp, to_device(inp)
 
 
+SCLK_PEAK_MHZ = 2400.0  # MI355X peak engine clock
+CLOCK_GATE = 0.70       # a workload counts only if its shader clock stayed above this share of the peak
+REPEAT_GATE = 0.02      # largest relative difference between the two headline measurements
+
+
+def validity_checks(per, head_us, head_repeat_us):
+    """The lowest shader clock read around any timed workload against the
+    peak, and the headline's second pass (after every other workload)
+    against its first: a clock below CLOCK_GATE x peak, or passes more than
+    REPEAT_GATE apart, is flagged.  Nothing is dropped: the reported headline
+    is the median over the calls of both passes."""
+    fracs = {}
+    for name, st in per.items():
+        if not isinstance(st, dict):
+            continue
+        mhz = [c.get("sclk_mhz") for c in (st.get("clocks_before"), st.get("clocks_after"))
+               if isinstance(c, dict) and isinstance(c.get("sclk_mhz"), (int, float))]
+        if mhz:
+            fracs[name] = round(min(mhz) / SCLK_PEAK_MHZ, 4)
+    out = {"sclk_peak_mhz": SCLK_PEAK_MHZ, "clock_gate": CLOCK_GATE,
+           "sclk_min_frac": min(fracs.values()) if fracs else None,
+           "clock_gate_passed": (min(fracs.values()) >= CLOCK_GATE) if fracs else None,
+           "clock_gate_failed": sorted(k for k, f in fracs.items() if f < CLOCK_GATE),
+           "repeat_gate": REPEAT_GATE, "headline_first_pass_us": round(head_us, 2),
+           "headline_repeat_us": None, "repeat_disagreement": None,
+           "repeat_gate_passed": None}
+    if head_repeat_us is not None:
+        d = abs(head_repeat_us - head_us) / head_us
+        out.update(headline_repeat_us=round(head_repeat_us, 2), repeat_disagreement=round(d, 4),
+                   repeat_gate_passed=d <= REPEAT_GATE)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -480,6 +515,27 @@ def main():
             del wdev
             torch.cuda.empty_cache()
 
+    # measurement-validity checks: the headline again after every other
+    # workload (repeatability), and the shader clock of every workload
+    head_repeat = None
+    first_pass_us = head["us_per_call"]
+    if not args.quick:
+        rep_st = measure(inp, dev, **meas)
+        head_repeat = rep_st["us_per_call"]
+        log(f"  headline again: {head_repeat:.1f} us")
+        # the headline figures are those of both passes' calls together
+        calls = np.array(head["_calls_us"] + rep_st["_calls_us"])
+        mains = np.array(head["_main_us"] + rep_st["_main_us"])
+        med = float(np.median(calls))
+        head.update(us_per_call=med, p10=float(np.percentile(calls, 10)),
+                    p90=float(np.percentile(calls, 90)), main_us_mean=float(mains.mean()),
+                    main_us_median=float(np.median(mains)),
+                    kv_gbps=head["kv_bytes"] / (med * 1e-6) / 1e9,
+                    frac_hbm_peak=head["kv_bytes"] / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                    calls_timed=len(calls))
+    validity = validity_checks(per, first_pass_us, head_repeat)
+    log(f"  validity: {validity}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline")
@@ -531,9 +587,11 @@ def main():
                      "read_ceiling_gbps": round(read_stream_gbps, 1),
                      "frac_of_read_ceiling": round(achieved / read_stream_gbps, 4),
                      "kernel_source_sha256": kernel_source_sha256()},
+        "validity": validity,
         "cpu_baseline": cpu,
         "per_workload": {k: ({kk: (round(vv, 4) if isinstance(vv, float) else vv)
-                              for kk, vv in v.items()} if isinstance(v, dict) else v)
+                              for kk, vv in v.items() if not kk.startswith("_")}
+                             if isinstance(v, dict) else v)
                          for k, v in per.items()},
     }
     print(json.dumps(line), flush=True)
