@@ -79,6 +79,53 @@ def test_key_shards(H, q, n, cuts, fp8):
                f"merged {len(bounds)} shards")
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_key_shards_of_a_large_batch(fp8):
+    """70 sequences, each decoded over its own key shard [a_b, n_b) with its
+    causal end (the plan's descriptors then live in the workspace tables):
+    every row against the oracle's partial over the same keys."""
+    import torch
+    batch, H = 70, 8
+    rng = np.random.default_rng(83)
+    ql = rng.integers(1, 5, batch)
+    kl = rng.integers(200, 900, batch)
+    cut = np.array([rng.integers(0, n - 1) for n in kl])  # shard [cut, n): at least 2 keys
+    gu.log(f"shards of a {batch}-sequence batch fp8={fp8}")
+    inp = gen.peaked_inputs(gen.random_inputs(H, ql.tolist(), kl.tolist(), fp8, seed=84), beta=10.0,
+                            seed=6)
+    off = np.concatenate([[0], np.cumsum(kl)])
+    kv_sh = np.concatenate([inp.kv[off[b] + cut[b]:off[b + 1]] for b in range(batch)])
+    sh = gen.Inputs(H, inp.q_len.copy(), (kl - cut).astype(np.int32), inp.q_bits,
+                    np.ascontiguousarray(kv_sh), fp8, inp.kv_scale)
+    q_dev, kv_dev = gu.to_device(sh)
+    plan = mb.Plan(H, ql.tolist(), (kl - cut).tolist(), fp8, causal_end=(kl - cut).tolist(),
+                   force_splits=3)
+    assert plan.num_launches == 1 and plan.num_split_tiles > 0
+    o, lse, ws = mb.alloc_outputs(plan, q_dev.device)
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    ws.fill_(0xFF)
+    mb.mla_decode_run(plan, q_dev, kv_dev, sh.sm_scale, sh.kv_scale, o, lse, ws, ws.numel())
+    mb.mla_decode_reduce(plan, ws, o, lse)
+    torch.cuda.synchronize()
+    go, gl = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    rows = int(ql.sum())
+    ro = np.empty((rows, H, mb.DV))
+    rl = np.empty((rows, H))
+    r = 0
+    for b in range(batch):
+        for i in range(int(ql[b])):
+            for h in range(H):
+                ro[r, h], rl[r, h] = oracle.mla_partial(
+                    inp.q_bits, inp.kv, inp.q_len, inp.kv_len, H, b, i, h, int(cut[b]), int(kl[b]),
+                    kv_is_fp8=fp8, kv_scale=inp.kv_scale, sm_scale=inp.sm_scale)
+            r += 1
+    empty = np.isneginf(rl)
+    assert np.all(np.isneginf(gl[empty])) and np.all(go[empty] == 0.0)
+    gu.compare(go[~empty], gl[~empty], ro[~empty], rl[~empty], fp8,
+               f"{batch} shards, empty rows {int(empty.sum())}")
+
+
 def test_merge_of_one_shard_is_the_identity_up_to_rounding():
     import torch
     rows = 37
