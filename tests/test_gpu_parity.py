@@ -157,6 +157,31 @@ def test_large_batch_is_one_launch(fp8, batch, mode):
     gu.compare(o, lse, ro, rl, fp8, f"B={batch} merge={mode}")
 
 
+@pytest.mark.parametrize("splits,fp8,mode", [
+    (20, False, mb.MLA_MERGE_REDUCE),        # 4 chunk phases
+    (40, False, mb.MLA_MERGE_REDUCE),        # 8
+    (40, True, mb.MLA_MERGE_LAST_ARRIVER),
+    (100, True, mb.MLA_MERGE_REDUCE),        # 16
+    (150, True, mb.MLA_MERGE_REDUCE),        # 32
+])
+def test_large_batch_every_fold_layout(splits, fp8, mode):
+    """More than 60 sequences with enough chunks that the merge reads the
+    workspace tables in every fold layout (4 to 32 chunk phases): sequence b
+    holds 64 splits - r_b keys (r_b < 64), so every sequence has exactly
+    `splits` chunks and a ragged last one."""
+    batch = 70
+    gu.log(f"large batch B={batch} splits={splits} fp8={fp8} merge={mode}")
+    rng = np.random.default_rng(splits + 3 * mode)
+    kl = (64 * splits - rng.integers(0, 64, batch)).tolist()
+    inp = gen.random_inputs(2, [1] * batch, kl, fp8, seed=splits)
+    ro, rl = gu.oracle_full(inp)
+    o, lse, plan = gu.run_gpu(inp, force_splits=splits, merge_mode=mode, poison_workspace=True)
+    assert plan.num_launches == 1
+    assert all(plan.query(b)[2] == splits for b in range(batch))
+    assert plan.launch(0)[1] == mode
+    gu.compare(o, lse, ro, rl, fp8, f"B={batch} splits={splits} merge={mode}")
+
+
 @pytest.mark.parametrize("beta", [1.0, 2.0, 3.0])
 def test_moderate_peaks_fp8(beta):
     """Dominant keys a few octaves above the rest, below the reference-move
