@@ -182,6 +182,26 @@ def test_large_batch_every_fold_layout(splits, fp8, mode):
     gu.compare(o, lse, ro, rl, fp8, f"B={batch} splits={splits} merge={mode}")
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_large_mixed_batch_auto_plan(fp8):
+    """80 sequences, about a third of them long: the automatic plan splits
+    only those (and reorders the batch, longest first), so the merge's table
+    of split sequences is a reordered subset of the descriptor table."""
+    batch = 80
+    rng = np.random.default_rng(1)
+    kl = np.where(rng.random(batch) < 0.3, rng.integers(3000, 12000, batch),
+                  rng.integers(16, 400, batch)).tolist()
+    ql = rng.integers(1, 5, batch).tolist()
+    gu.log(f"large mixed batch B={batch} fp8={fp8}")
+    inp = gen.random_inputs(4, ql, kl, fp8, seed=88)
+    ro, rl = gu.oracle_full(inp)
+    o, lse, plan = gu.run_gpu(inp, poison_workspace=True)
+    splits = [plan.query(b)[2] for b in range(batch)]
+    assert plan.num_launches == 1
+    assert 0 < sum(s > 1 for s in splits) < batch and max(splits) > 8
+    gu.compare(o, lse, ro, rl, fp8, f"B={batch} auto plan, {sum(s > 1 for s in splits)} split")
+
+
 @pytest.mark.parametrize("beta", [1.0, 2.0, 3.0])
 def test_moderate_peaks_fp8(beta):
     """Dominant keys a few octaves above the rest, below the reference-move
