@@ -110,6 +110,13 @@ def workload(name: str) -> Workload:
         ql = ragged_q_lens(5, 32)
         return Workload(name, 96, ql, [32768] * 32, False, 5,
                         "bf16, 32 sequences, H=96, q_b uniform {1..4}, ctx=32768 each")
+    if name in ("batch150", "batch150_fp8"):  # more sequences than the kernel arguments hold
+        rng = np.random.default_rng([6, 3])
+        kl = [int(v) for v in rng.integers(2048, 4097, size=150)]
+        fp8 = name.endswith("fp8")
+        return Workload(name, 12, [2] * 150, kl, fp8, 6,
+                        f"{'fp8-e4m3' if fp8 else 'bf16'} KV, 150 sequences, H=12, q=2, "
+                        "ctx uniform in [2048, 4096]")
     raise KeyError(name)
 
 
