@@ -166,7 +166,8 @@ typedef struct {
  *  descriptor tables are uploaded from (hipHostMalloc; if that fails the
  *  plan is still made and its first mla_decode_run allocates the buffer).
  *  Errors: INVALID_ARGUMENT (shapes, null pointers), UNSUPPORTED (H > 128,
- *  unknown dtype), DEVICE (CU query failed). */
+ *  unknown dtype), DEVICE (CU query failed), OUT_OF_MEMORY (host memory for
+ *  the plan). */
 mla_status mla_decode_plan(int32_t batch, int32_t num_heads, const int32_t* q_len,
                            const int32_t* kv_len, mla_kv_dtype kv_dtype,
                            const mla_plan_options* opts, mla_plan** plan_out,
